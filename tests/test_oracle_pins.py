@@ -1,0 +1,453 @@
+"""Pins for the float64 oracle: checks against what the pages and the
+mathematics fix, never against the oracle's own formulas retyped.
+
+Each test names the page passage it rests on.  Together they are chosen so
+that a plausible slip anywhere in the oracle (dropped scale, wrong sign,
+transposed operand, wrong head or block index, missing sum weight, sink on the
+wrong side) fails at least one of them; ``test_planted_mistakes_are_caught``
+plants such slips in copies of the oracle and checks exactly that.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attn_ref
+from synth import make_workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RTOL = 1e-12
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def _bruteforce_row(q, K, V, scale, sink=None):
+    """Literal formula of the aclnnIncreFlashAttentionV3 "Function" section
+    (and the sink denominator of aclnnFlashAttentionScoreV4): no max
+    subtraction, pure-Python loops, math.fsum.  Tiny inputs only."""
+    L, D = len(K), len(q)
+    e = [math.exp(scale * math.fsum(q[d] * K[j][d] for d in range(D))) for j in range(L)]
+    den = math.fsum(e) + (math.exp(sink) if sink is not None else 0.0)
+    out = [math.fsum(e[j] * V[j][c] for j in range(L)) / den for c in range(len(V[0]))] if L else [0.0] * len(V[0])
+    return out, math.log(den)
+
+
+# ---------------------------------------------------------------- P1
+def test_softmax_rows_sum_to_one():
+    """aclnnIncreFlashAttentionV3 Function: each row is normalised by softmax;
+    aclnnFlashAttentionScoreV4 formula: the sink weight is part of the sum."""
+    rng = np.random.default_rng(1)
+    for L in (1, 2, 17, 300):
+        s = _rand(rng, L) * 5
+        p, ps, m, den = oracle.softmax_weights(s)
+        assert ps == 0.0 and abs(p.sum() - 1.0) < RTOL
+        for sink in (-3.0, 0.0, 9.0):
+            p, ps, m, den = oracle.softmax_weights(s, sink)
+            assert abs(p.sum() + ps - 1.0) < RTOL
+            assert m == max(s.max(), sink)
+            assert np.all(p >= 0) and ps > 0
+
+
+# ---------------------------------------------------------------- P2
+@pytest.mark.parametrize("seed", range(6))
+def test_split_invariance_merge_equals_full(seed):
+    """aclnnRingAttentionUpdate formula (weighted reading R1): merging the
+    partial results of any split of the KV axis, in any order, reproduces the
+    attention over the whole axis."""
+    rng = np.random.default_rng(100 + seed)
+    L, D, Dv = int(rng.integers(1, 200)), 16, 12
+    q, K, V = _rand(rng, D), _rand(rng, L, D), _rand(rng, L, Dv)
+    scale = 1 / math.sqrt(D)
+    full, lse = oracle.attention_row(q, K, V, scale)
+    nparts = int(rng.integers(2, 17))
+    cuts = np.sort(rng.integers(0, L + 1, size=nparts - 1))
+    bounds = [0, *cuts.tolist(), L]
+    parts = [oracle.partial_triple(q, K[a:b], V[a:b], scale) for a, b in zip(bounds[:-1], bounds[1:])]
+    order = rng.permutation(len(parts))
+    o, m, l = oracle.merge_many([parts[i] for i in order])
+    np.testing.assert_allclose(o, full, rtol=0, atol=1e-12)
+    assert abs((m + math.log(l)) - lse) < 1e-12
+
+
+def test_split_invariance_two_halves_of_64():
+    """The tiny fp32 workload is checked as the merge of its two 64-token halves."""
+    rng = np.random.default_rng(7)
+    D = 64
+    q, K, V = _rand(rng, D), _rand(rng, 128, D), _rand(rng, 128, D)
+    full, lse = oracle.attention_row(q, K, V, 1 / 8)
+    a = oracle.partial_triple(q, K[:64], V[:64], 1 / 8)
+    b = oracle.partial_triple(q, K[64:], V[64:], 1 / 8)
+    o, m, l = oracle.merge(*a, *b)
+    np.testing.assert_allclose(o, full, atol=1e-13)
+    assert abs(m + math.log(l) - lse) < 1e-12
+
+
+def test_merge_empty_partial_is_neutral():
+    """An empty partial (max -inf, sum 0) leaves the other one unchanged, on
+    either side; two empty partials stay empty (no NaN from -inf - -inf)."""
+    rng = np.random.default_rng(3)
+    o = _rand(rng, 8)
+    for args in [(o, 1.5, 2.0, np.zeros(8), -np.inf, 0.0), (np.zeros(8), -np.inf, 0.0, o, 1.5, 2.0)]:
+        r, m, l = oracle.merge(*args)
+        np.testing.assert_array_equal(r, o)
+        assert m == 1.5 and l == 2.0
+    r, m, l = oracle.merge(np.zeros(8), -np.inf, 0.0, np.zeros(8), -np.inf, 0.0)
+    assert np.all(r == 0) and m == -np.inf and l == 0.0
+
+
+# ---------------------------------------------------------------- P3
+def test_printed_update_formula_in_lse_form():
+    """aclnnRingAttentionUpdate prints sum = ps e^(pm-M) + e^(cm-M) and
+    out = po e^(pm-M)/sum + co e^(cm-M)/sum.  With the partials in
+    log-sum-exp form (max = lse, sum = 1) the printed formula and the weighted
+    reading agree exactly; with sums != 1 only the weighted reading matches
+    full attention."""
+    rng = np.random.default_rng(11)
+    D = 8
+    q, K, V = _rand(rng, D), _rand(rng, 40, D), _rand(rng, 40, D)
+    full, lse = oracle.attention_row(q, K, V, 0.3)
+    po, pm, ps = oracle.partial_triple(q, K[:15], V[:15], 0.3)
+    co, cm, cs = oracle.partial_triple(q, K[15:], V[15:], 0.3)
+    plse, clse = pm + math.log(ps), cm + math.log(cs)
+
+    def printed(po, pm, ps, co, cm):
+        M = max(pm, cm)
+        s = ps * math.exp(pm - M) + math.exp(cm - M)
+        return po * math.exp(pm - M) / s + co * math.exp(cm - M) / s, M, s
+
+    o1, M1, s1 = printed(po, plse, 1.0, co, clse)
+    o2, M2, s2 = oracle.merge(po, plse, 1.0, co, clse, 1.0)
+    np.testing.assert_allclose(o1, o2, atol=1e-15)
+    np.testing.assert_allclose(o1, full, atol=1e-12)
+    # (m, l) form gives the same merged output and the same lse
+    o3, M3, s3 = oracle.merge(po, pm, ps, co, cm, cs)
+    np.testing.assert_allclose(o3, full, atol=1e-12)
+    assert abs(M3 + math.log(s3) - lse) < 1e-12
+    # the printed formula applied literally to (m, l) triples is not attention
+    o4, _, _ = printed(po, pm, ps, co, cm)
+    assert np.max(np.abs(o4 - full)) > 1e-3
+
+
+# ---------------------------------------------------------------- P4 / P13
+@pytest.mark.parametrize("bs,lengths", [(16, [1, 15, 16, 17, 40]), (32, [0, 31, 32, 33, 100]), (128, [5, 127, 128, 129, 300])])
+def test_paged_equals_contiguous(bs, lengths):
+    """aclnnIncreFlashAttentionV3 Constraints, page attention scenario: the
+    paged layout (blocknum, KV_N, blocksize, D) addressed through blockTable
+    gives the same attention as the contiguous layout holding the same tokens;
+    the block permutation is seeded and random; lengths straddle block
+    boundaries (bs-1, bs, bs+1) and include 0."""
+    B, Nq, Nkv, D = len(lengths), 4, 2, 8
+    w = make_workload(batch=B, n_q=Nq, n_kv=Nkv, qk_dim=D, kv_dtype="f32", layout="paged",
+                      block_size=bs, lengths=lengths, seed=5, sink=False, extra_blocks=3)
+    smax = max(lengths) + 3
+    kc = torch.full((B, Nkv, smax, D), float("nan"))
+    vc = torch.full((B, Nkv, smax, D), float("nan"))
+    bt = w.block_table.long()
+    for b, L in enumerate(lengths):
+        for j in range(L):
+            kc[b, :, j] = w.k_cache[bt[b, j // bs], :, j % bs]
+            vc[b, :, j] = w.v_cache[bt[b, j // bs], :, j % bs]
+    o_p, l_p = oracle.decode_workload(w)
+    o_c, l_c = oracle.decode(w.q, kc, vc, "bnsd", w.seq_lens, Nkv, w.scale)
+    np.testing.assert_array_equal(o_p, o_c)
+    np.testing.assert_array_equal(l_p, l_c)
+    assert not np.isnan(o_p).any()
+    # identity block table over a pool laid out in batch order
+    nb = [(L + bs - 1) // bs for L in lengths]
+    pool = sum(nb)
+    kp = torch.zeros((pool, Nkv, bs, D))
+    vp = torch.zeros((pool, Nkv, bs, D))
+    tab = torch.full((B, max(nb) or 1), -1, dtype=torch.int32)
+    off = 0
+    for b, L in enumerate(lengths):
+        for i in range(nb[b]):
+            tab[b, i] = off + i
+            n = min(bs, L - i * bs)
+            kp[off + i, :, :n] = kc[b, :, i * bs:i * bs + n]
+            vp[off + i, :, :n] = vc[b, :, i * bs:i * bs + n]
+        off += nb[b]
+    o_i, l_i = oracle.decode(w.q, kp, vp, "paged", w.seq_lens, Nkv, w.scale, block_table=tab, block_size=bs)
+    np.testing.assert_array_equal(o_i, o_c)
+    np.testing.assert_array_equal(l_i, l_c)
+
+
+# ---------------------------------------------------------------- P5
+def test_token_permutation_invariance():
+    """Attention is a sum over KV tokens: permuting (K_j, V_j) jointly changes nothing."""
+    rng = np.random.default_rng(21)
+    q, K, V = _rand(rng, 16), _rand(rng, 77, 16), _rand(rng, 77, 10)
+    o, l = oracle.attention_row(q, K, V, 0.25, sink=0.7)
+    p = rng.permutation(77)
+    o2, l2 = oracle.attention_row(q, K[p], V[p], 0.25, sink=0.7)
+    np.testing.assert_allclose(o2, o, atol=1e-13)
+    assert abs(l2 - l) < 1e-12
+
+
+# ---------------------------------------------------------------- P6
+@pytest.mark.parametrize("sink", [-5.0, 0.0, 8.0, 30.0])
+def test_sink_closed_form(sink):
+    """aclnnFlashAttentionScoreV4 formula: the sink adds e^(sink-m) to the
+    denominator only.  Hence out_sink = out / (1 + e^(sink - lse)),
+    lse_sink = logaddexp(lse, sink), and it equals merging in a pseudo
+    partial with out 0, max sink, sum 1."""
+    rng = np.random.default_rng(31)
+    q, K, V = _rand(rng, 16), _rand(rng, 50, 16), _rand(rng, 50, 16)
+    o0, l0 = oracle.attention_row(q, K, V, 0.25)
+    o1, l1 = oracle.attention_row(q, K, V, 0.25, sink=sink)
+    np.testing.assert_allclose(o1, o0 / (1 + math.exp(sink - l0)), atol=1e-13, rtol=1e-12)
+    assert abs(l1 - np.logaddexp(l0, sink)) < 1e-12
+    part = oracle.partial_triple(q, K, V, 0.25)
+    om, mm, lm = oracle.merge(*part, np.zeros(16), sink, 1.0)
+    np.testing.assert_allclose(om, o1, atol=1e-13)
+    assert abs(mm + math.log(lm) - l1) < 1e-12
+
+
+def test_sink_to_minus_infinity_recovers_plain_attention():
+    rng = np.random.default_rng(32)
+    q, K, V = _rand(rng, 8), _rand(rng, 20, 8), _rand(rng, 20, 8)
+    o0, l0 = oracle.attention_row(q, K, V, 0.5)
+    for s in (-np.inf, -1e4):
+        o1, l1 = oracle.attention_row(q, K, V, 0.5, sink=s)
+        np.testing.assert_allclose(o1, o0, atol=1e-15)
+        assert abs(l1 - l0) < 1e-12
+
+
+# ---------------------------------------------------------------- P7
+def test_ifa_v3_example_all_ones():
+    """Golden: the aclnnIncreFlashAttentionV3 sample (all-ones inputs) gives 1.0."""
+    g = json.load(open(os.path.join(GOLDEN, "ifa_v3_example_all_ones.json")))
+    B, N, D, S = g["batch"], g["num_heads"], g["head_dim"], g["kv_len"]
+    assert g["scale_value"] == 1 / math.sqrt(D)
+    q = np.ones((B, N, D))
+    k = np.ones((B, g["num_key_value_heads"], S, D))
+    out, lse = oracle.decode(q, k, k.copy(), "bnsd", [S] * B, g["num_key_value_heads"], g["scale_value"])
+    np.testing.assert_array_equal(out, np.full((B, N, D), g["expected_out"]))
+    # every score equals scale * D, so lse = scale*D + ln S
+    np.testing.assert_allclose(lse, g["scale_value"] * D + math.log(S), atol=1e-12)
+
+
+def test_special_cases():
+    """V constant -> output constant; K = 0 -> uniform weights (mean of V,
+    lse = ln L); one token -> its own value row and lse = its score."""
+    rng = np.random.default_rng(41)
+    q = _rand(rng, 12)
+    K = _rand(rng, 33, 12)
+    o, _ = oracle.attention_row(q, K, np.full((33, 5), -2.5), 0.3)
+    np.testing.assert_allclose(o, -2.5, atol=1e-14)
+    V = _rand(rng, 33, 5)
+    o, l = oracle.attention_row(q, np.zeros((33, 12)), V, 0.3)
+    np.testing.assert_allclose(o, V.mean(0), atol=1e-14)
+    assert abs(l - math.log(33)) < 1e-14
+    o, l = oracle.attention_row(q, K[:1], V[:1], 0.3)
+    np.testing.assert_allclose(o, V[0], atol=1e-15)
+    assert abs(l - 0.3 * float(K[0] @ q)) < 1e-13
+
+
+def test_empty_sequence():
+    """FusedInferAttentionScore blog, empty-tensor semantics: empty KV gives
+    an all-zero output; the lse of an empty row is -inf (reading R6), and
+    with a sink the row is the sink alone (out 0, lse = sink)."""
+    o, l = oracle.attention_row(np.ones(4), np.zeros((0, 4)), np.zeros((0, 3)), 0.5)
+    assert np.all(o == 0) and l == -np.inf
+    o, l = oracle.attention_row(np.ones(4), np.zeros((0, 4)), np.zeros((0, 3)), 0.5, sink=1.25)
+    assert np.all(o == 0) and l == 1.25
+    o, m, s = oracle.partial_triple(np.ones(4), np.zeros((0, 4)), np.zeros((0, 3)), 0.5)
+    assert np.all(o == 0) and m == -np.inf and s == 0.0
+
+
+# ---------------------------------------------------------------- P8
+@pytest.mark.parametrize("seed", range(5))
+def test_bruteforce_tiny(seed):
+    """Whole decode vs a separate pure-Python evaluation of the literal
+    formula (no max subtraction) on tiny shapes, with GQA, paging, sink."""
+    rng = np.random.default_rng(500 + seed)
+    B = int(rng.integers(1, 3))
+    Nkv = int(rng.choice([1, 2]))
+    Nq = Nkv * int(rng.choice([1, 2]))
+    D = int(rng.choice([4, 8]))
+    lengths = [int(x) for x in rng.integers(0, 17, size=B)]
+    use_sink = bool(seed % 2)
+    w = make_workload(batch=B, n_q=Nq, n_kv=Nkv, qk_dim=D, kv_dtype="f32", layout="paged",
+                      block_size=16, lengths=lengths, seed=seed, sink=use_sink)
+    out, lse = oracle.decode_workload(w)
+    qf = w.q.double().numpy()
+    bt = w.block_table.long().numpy()
+    G = Nq // Nkv
+    for b in range(B):
+        L = lengths[b]
+        for h in range(Nq):
+            g = h // G
+            K = [[float(w.k_cache[bt[b, j // 16], g, j % 16, d]) for d in range(D)] for j in range(L)]
+            V = [[float(w.v_cache[bt[b, j // 16], g, j % 16, d]) for d in range(D)] for j in range(L)]
+            sk = float(w.sink[h]) if use_sink else None
+            if L == 0 and sk is None:
+                assert np.all(out[b, h] == 0) and lse[b, h] == -np.inf
+                continue
+            ob, lb = _bruteforce_row(qf[b, h].tolist(), K, V if L else [[0.0] * D], w.scale, sk)
+            np.testing.assert_allclose(out[b, h], ob, rtol=1e-12, atol=1e-14)
+            assert abs(lse[b, h] - lb) < 1e-12
+
+
+# ---------------------------------------------------------------- P9
+def test_gqa_equals_mha_with_repeated_kv():
+    """aclnnIncreFlashAttentionV3: numHeads is a multiple of
+    numKeyValueHeads; with contiguous head groups (reading R3) GQA equals
+    MHA over KV heads repeated G times.  numKeyValueHeads = 0 means N_kv = N_q."""
+    rng = np.random.default_rng(61)
+    B, Nkv, G, S, D = 2, 3, 4, 20, 8
+    q = _rand(rng, B, Nkv * G, D)
+    k = _rand(rng, B, Nkv, S, D)
+    v = _rand(rng, B, Nkv, S, D)
+    lens = [20, 13]
+    o1, l1 = oracle.decode(q, k, v, "bnsd", lens, Nkv, 0.35)
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    o2, l2 = oracle.decode(q, kr, vr, "bnsd", lens, Nkv * G, 0.35)
+    np.testing.assert_array_equal(o1, o2)
+    o3, l3 = oracle.decode(q, kr, vr, "bnsd", lens, 0, 0.35)
+    np.testing.assert_array_equal(o3, o2)
+    np.testing.assert_array_equal(l3, l2)
+
+
+# ---------------------------------------------------------------- P10
+def test_int8_antiquant_identity_and_affine():
+    """aclnnIncreFlashAttentionV3 antiquantScale/antiquantOffset (per channel,
+    index 0 = K, 1 = V), reading R2 x_hat = (x + offset) * scale.  Pins:
+    scale 1, offset 0 is attention over the integer values; the V offset and
+    scale act affinely on the output; the K offset shifts every score of a
+    head by one constant, so the output is unchanged and the lse moves."""
+    w = make_workload(batch=2, n_q=4, n_kv=2, qk_dim=16, kv_dtype="i8", layout="paged",
+                      block_size=32, lengths=[40, 70], seed=9)
+    kw = dict(block_table=w.block_table, block_size=32)
+    ones, zeros = torch.ones_like(w.antiquant_scale), torch.zeros_like(w.antiquant_offset)
+    o_q, l_q = oracle.decode(w.q, w.k_cache, w.v_cache, "paged", w.seq_lens, 2, w.scale,
+                             antiquant_scale=ones, antiquant_offset=zeros, **kw)
+    o_f, l_f = oracle.decode(w.q, w.k_cache.float(), w.v_cache.float(), "paged", w.seq_lens, 2, w.scale, **kw)
+    np.testing.assert_array_equal(o_q, o_f)
+    np.testing.assert_array_equal(l_q, l_f)
+
+    sc, off = w.antiquant_scale.double().numpy(), w.antiquant_offset.double().numpy()
+    # V side only: out = sc_v * (out_int + off_v)
+    s_v = ones.clone(); s_v[1] = w.antiquant_scale[1]
+    o_v_off = zeros.clone(); o_v_off[1] = w.antiquant_offset[1]
+    o_a, l_a = oracle.decode(w.q, w.k_cache, w.v_cache, "paged", w.seq_lens, 2, w.scale,
+                             antiquant_scale=s_v, antiquant_offset=o_v_off, **kw)
+    for h in range(4):
+        g = h // 2
+        np.testing.assert_allclose(o_a[:, h], sc[1, g] * (o_f[:, h] + off[1, g]), atol=1e-12)
+    np.testing.assert_allclose(l_a, l_f, atol=1e-12)
+    # K side: offset shifts the scores by scale * sum_d q_d sc_d off_d
+    s_k = ones.clone(); s_k[0] = w.antiquant_scale[0]
+    o_k0, l_k0 = oracle.decode(w.q, w.k_cache, w.v_cache, "paged", w.seq_lens, 2, w.scale,
+                               antiquant_scale=s_k, antiquant_offset=zeros, **kw)
+    o_k_off = zeros.clone(); o_k_off[0] = w.antiquant_offset[0]
+    o_k1, l_k1 = oracle.decode(w.q, w.k_cache, w.v_cache, "paged", w.seq_lens, 2, w.scale,
+                               antiquant_scale=s_k, antiquant_offset=o_k_off, **kw)
+    np.testing.assert_allclose(o_k1, o_k0, atol=1e-12)
+    qf = w.q.double().numpy()
+    for b in range(2):
+        for h in range(4):
+            g = h // 2
+            c = w.scale * float(np.sum(qf[b, h] * sc[0, g] * off[0, g]))
+            assert abs(l_k1[b, h] - (l_k0[b, h] + c)) < 1e-10
+
+
+# ---------------------------------------------------------------- P11
+def test_mla_equals_mqa_with_value_prefix():
+    """MLA decode (aclnnMlaPrologV3WeightNz shapes: 512 latent + 64 rope,
+    Nkv = 1): one cache row serves as K (all 576 channels) and, through its
+    first 512 channels, as V.  It equals MQA with a separate V cache holding
+    those channels."""
+    w = make_workload(batch=2, n_q=8, n_kv=1, qk_dim=576, v_dim=512, kv_dtype="bf16", layout="paged",
+                      block_size=16, lengths=[20, 33], seed=4, scale=1 / math.sqrt(192), v_aliases_k=True)
+    o1, l1 = oracle.decode_workload(w)
+    vsep = w.k_cache[..., :512].clone()
+    o2, l2 = oracle.decode(w.q, w.k_cache, vsep, "paged", w.seq_lens, 1, w.scale,
+                           block_table=w.block_table, block_size=16, v_dim=512)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    assert o1.shape == (2, 8, 512)
+
+
+# ---------------------------------------------------------------- P12
+def test_blocknum_worked_example():
+    """Golden: aclnnMlaPrologV3WeightNz Constraints, BlockNum row."""
+    g = json.load(open(os.path.join(GOLDEN, "mla_blocknum_example.json")))
+    lens = oracle.lengths_from_prefix_sums(g["actual_seq_len_prefix_sums"])
+    assert lens == g["expected_lengths"]
+    assert oracle.block_count(lens, g["block_size"]) == g["expected_block_num"]
+
+
+# ---------------------------------------------------------------- attn_update rows
+def test_attn_update_rows_match_full_attention():
+    """Row-wise aclnnRingAttentionUpdate over several (b, h) rows: merging the
+    two halves' triples reproduces full attention per row."""
+    rng = np.random.default_rng(71)
+    rows, D = 6, 32
+    q = _rand(rng, rows, D)
+    K, V = _rand(rng, rows, 50, D), _rand(rng, rows, 50, D)
+    prev = [oracle.partial_triple(q[r], K[r, :20], V[r, :20], 0.2) for r in range(rows)]
+    cur = [oracle.partial_triple(q[r], K[r, 20:], V[r, 20:], 0.2) for r in range(rows)]
+    po = np.stack([p[0] for p in prev]); pm = np.array([p[1] for p in prev]); ps = np.array([p[2] for p in prev])
+    co = np.stack([p[0] for p in cur]); cm = np.array([p[1] for p in cur]); cs = np.array([p[2] for p in cur])
+    o, m, s = oracle.attn_update(po, pm, ps, co, cm, cs)
+    for r in range(rows):
+        full, lse = oracle.attention_row(q[r], K[r], V[r], 0.2)
+        np.testing.assert_allclose(o[r], full, atol=1e-12)
+        assert abs(m[r] + math.log(s[r]) - lse) < 1e-12
+
+
+# ---------------------------------------------------------------- sensitivity
+def test_planted_mistakes_are_caught(monkeypatch):
+    """Plant plausible slips in the oracle (on the CPU) and check that the
+    brute-force pin, the split pin or the GQA pin notices each one."""
+    orig_row = attn_ref.attention_row
+    orig_merge = attn_ref.merge
+    orig_gather = attn_ref.gather_kv
+
+    def run_pins():
+        failed = []
+        for name, fn in [("bruteforce", lambda: test_bruteforce_tiny(1)),
+                         ("split", lambda: test_split_invariance_merge_equals_full(0)),
+                         ("sink", lambda: test_sink_closed_form(8.0)),
+                         ("paged", lambda: test_paged_equals_contiguous(16, [1, 15, 16, 17, 40]))]:
+            try:
+                fn()
+            except AssertionError:
+                failed.append(name)
+        return failed
+
+    def no_scale(q, K, V, scale, sink=None):
+        return orig_row(q, K, V, 1.0, sink)
+
+    def sink_in_numerator(q, K, V, scale, sink=None):
+        o, l = orig_row(q, K, V, scale, None)
+        return o, l if sink is None else np.logaddexp(l, sink)
+
+    def transposed(q, K, V, scale, sink=None):
+        return orig_row(q, K, V[::-1].copy(), scale, sink)
+
+    def unweighted_merge(po, pm, ps, co, cm, cs):
+        return orig_merge(po, pm, 1.0 + 0 * np.asarray(ps), co, cm, 1.0 + 0 * np.asarray(cs))
+
+    def wrong_batch_row(cache, layout, b, g, length, block_table=None, block_size=0, dim=None):
+        return orig_gather(cache, layout, 0 if layout == "paged" else b, g, length, block_table, block_size, dim)
+
+    def wrong_head(cache, layout, b, g, length, block_table=None, block_size=0, dim=None):
+        return orig_gather(cache, layout, b, (g + 1) % cache.shape[1], length, block_table, block_size, dim)
+
+    slips = [("attention_row", no_scale), ("attention_row", sink_in_numerator),
+             ("attention_row", transposed), ("merge", unweighted_merge),
+             ("gather_kv", wrong_batch_row), ("gather_kv", wrong_head)]
+    for fn_name, bad in slips:
+        with monkeypatch.context() as mp:
+            mp.setattr(attn_ref, fn_name, bad)
+            mp.setattr(oracle, fn_name, bad)
+            assert run_pins(), f"planted slip {bad.__name__} went unnoticed"
+    assert run_pins() == []
