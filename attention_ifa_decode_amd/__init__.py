@@ -1,0 +1,321 @@
+"""Python binding of the MI355X decode-attention library (ctypes).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/ifa_decode.h.  PyTorch provides device
+memory (outputs and the workspace are torch tensors) and the stream (torch's
+current stream).  There is no CPU fallback: without the built library every
+call raises.
+
+    out, lse = decode(q, k_cache, v_cache, block_table, actual_seq_lengths,
+                      num_heads, num_key_value_heads, scale_value,
+                      learnable_sink=None, antiquant_scale=None,
+                      antiquant_offset=None, num_splits=0)
+
+Layouts: q (B, N_q, D); paged KV pools (num_blocks, N_kv, block_size, D)
+with block_table int32 (B, max_blocks_per_seq); or, with block_table None,
+contiguous padded KV (B, N_kv, S_cap, D).  For the MLA shape pass the same
+tensor as k_cache and v_cache and ``v_dim=512``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libifa_decode.so")
+
+IFA_OK = 0
+IFA_ERR_PARAM_NULLPTR = 161001
+IFA_ERR_PARAM_INVALID = 161002
+IFA_ERR_RUNTIME = 361001
+IFA_ERR_PLAN = 561002
+
+IFA_F32, IFA_F16, IFA_BF16, IFA_I8 = 0, 1, 2, 3
+IFA_KV_BNSD, IFA_KV_PAGED = 0, 1
+
+_DTYPE_CODE = {torch.float32: IFA_F32, torch.float16: IFA_F16, torch.bfloat16: IFA_BF16, torch.int8: IFA_I8}
+
+# Every function the header declares.
+EXPORTED = (
+    "ifa_decode_workspace_size",
+    "ifa_decode_num_splits",
+    "ifa_decode",
+    "ifa_decode_splitkv",
+    "ifa_decode_combine",
+    "attn_update",
+    "ifa_paged_block_count",
+    "ifa_last_error",
+)
+
+
+class IfaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"ifa status {status}: {message}")
+        self.status = status
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("query", ctypes.c_void_p),
+        ("key_cache", ctypes.c_void_p),
+        ("value_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("actual_seq_lengths", ctypes.c_void_p),
+        ("learnable_sink", ctypes.c_void_p),
+        ("antiquant_scale", ctypes.c_void_p),
+        ("antiquant_offset", ctypes.c_void_p),
+        ("attention_out", ctypes.c_void_p),
+        ("softmax_lse", ctypes.c_void_p),
+        ("batch", ctypes.c_int64),
+        ("num_heads", ctypes.c_int64),
+        ("num_key_value_heads", ctypes.c_int64),
+        ("qk_dim", ctypes.c_int64),
+        ("v_dim", ctypes.c_int64),
+        ("block_size", ctypes.c_int64),
+        ("max_blocks_per_seq", ctypes.c_int64),
+        ("num_blocks", ctypes.c_int64),
+        ("s_cap", ctypes.c_int64),
+        ("scale_value", ctypes.c_double),
+        ("q_dtype", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("kv_layout", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"HIP library not built: {p} is missing (run attention_ifa_decode_amd.build)")
+    lib = ctypes.CDLL(p)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    args_p = ctypes.POINTER(DecodeArgs)
+    lib.ifa_decode_workspace_size.argtypes = [args_p, ctypes.POINTER(SZ)]
+    lib.ifa_decode_num_splits.argtypes = [args_p, ctypes.POINTER(I32)]
+    for fn in (lib.ifa_decode, lib.ifa_decode_splitkv):
+        fn.argtypes = [args_p, P, SZ, P]
+    lib.ifa_decode_combine.argtypes = [args_p, P, SZ, P]
+    lib.attn_update.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I32, I32, P]
+    lib.ifa_paged_block_count.argtypes = [ctypes.POINTER(I64), I64, I64]
+    lib.ifa_paged_block_count.restype = I64
+    lib.ifa_last_error.argtypes = []
+    lib.ifa_last_error.restype = ctypes.c_char_p
+    for name in ("ifa_decode_workspace_size", "ifa_decode_num_splits", "ifa_decode", "ifa_decode_splitkv",
+                 "ifa_decode_combine", "attn_update"):
+        getattr(lib, name).restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().ifa_last_error().decode()
+
+
+def _check(status: int):
+    if status != IFA_OK:
+        raise IfaError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+class DecodeCall:
+    """A prepared decode call: argument struct, outputs and workspace.
+
+    ``run()`` queues the split-KV kernel and the combine on the current stream;
+    ``splitkv()`` and ``combine()`` queue the two halves separately.
+    """
+
+    def __init__(self, q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads: int,
+                 num_key_value_heads: int, scale_value: float, learnable_sink=None, antiquant_scale=None,
+                 antiquant_offset=None, num_splits: int = 0, v_dim: Optional[int] = None,
+                 out_dtype: Optional[torch.dtype] = None, with_lse: bool = True, out=None, lse=None):
+        lib = load_library()
+        _need(q, "q")
+        _need(k_cache, "k_cache")
+        _need(v_cache, "v_cache")
+        _need(actual_seq_lengths, "actual_seq_lengths", torch.int64)
+        B, n_q, qk_dim = q.shape
+        if n_q != num_heads:
+            raise ValueError("q.shape[1] must equal num_heads")
+        alias = v_cache.data_ptr() == k_cache.data_ptr()
+        if v_dim is None:
+            v_dim = qk_dim if alias else v_cache.shape[-1]
+        paged = block_table is not None
+        if paged:
+            _need(block_table, "block_table", torch.int32)
+            num_blocks, _, block_size, _ = k_cache.shape
+            max_blocks = block_table.shape[1]
+            s_cap = 0
+        else:
+            _, _, s_cap, _ = k_cache.shape
+            num_blocks = block_size = max_blocks = 0
+        for t, nm in ((learnable_sink, "learnable_sink"), (antiquant_scale, "antiquant_scale"),
+                      (antiquant_offset, "antiquant_offset")):
+            if t is not None:
+                _need(t, nm, torch.float32)
+        out_dtype = out_dtype or q.dtype
+        dev = q.device
+        self.out = out if out is not None else torch.empty((B, n_q, v_dim), dtype=out_dtype, device=dev)
+        self.lse = lse if lse is not None else (
+            torch.empty((B, n_q), dtype=torch.float32, device=dev) if with_lse else None)
+        a = DecodeArgs()
+        a.query = _ptr(q)
+        a.key_cache = _ptr(k_cache)
+        a.value_cache = _ptr(v_cache)
+        a.block_table = _ptr(block_table)
+        a.actual_seq_lengths = _ptr(actual_seq_lengths)
+        a.learnable_sink = _ptr(learnable_sink)
+        a.antiquant_scale = _ptr(antiquant_scale)
+        a.antiquant_offset = _ptr(antiquant_offset)
+        a.attention_out = _ptr(self.out)
+        a.softmax_lse = _ptr(self.lse)
+        a.batch = B
+        a.num_heads = num_heads
+        a.num_key_value_heads = num_key_value_heads
+        a.qk_dim = qk_dim
+        a.v_dim = v_dim
+        a.block_size = block_size
+        a.max_blocks_per_seq = max_blocks
+        a.num_blocks = num_blocks
+        a.s_cap = s_cap
+        a.scale_value = float(scale_value)
+        a.q_dtype = _DTYPE_CODE[q.dtype]
+        a.kv_dtype = _DTYPE_CODE[k_cache.dtype]
+        a.out_dtype = _DTYPE_CODE[out_dtype]
+        a.kv_layout = IFA_KV_PAGED if paged else IFA_KV_BNSD
+        a.num_splits = int(num_splits)
+        a.reserved = 0
+        self.args = a
+        sz = ctypes.c_size_t(0)
+        _check(lib.ifa_decode_workspace_size(ctypes.byref(a), ctypes.byref(sz)))
+        ns = ctypes.c_int32(0)
+        _check(lib.ifa_decode_num_splits(ctypes.byref(a), ctypes.byref(ns)))
+        self.num_splits = ns.value
+        self.workspace_bytes = sz.value
+        self.workspace = torch.empty(max(1, sz.value), dtype=torch.uint8, device=dev)
+        # keep the inputs alive as long as the call object
+        self._keep = (q, k_cache, v_cache, block_table, actual_seq_lengths, learnable_sink,
+                      antiquant_scale, antiquant_offset)
+        self._lib = lib
+
+    def run(self):
+        _check(self._lib.ifa_decode(ctypes.byref(self.args), self.workspace.data_ptr(), self.workspace_bytes,
+                                    _stream_handle()))
+        return self.out, self.lse
+
+    def splitkv(self):
+        _check(self._lib.ifa_decode_splitkv(ctypes.byref(self.args), self.workspace.data_ptr(),
+                                            self.workspace_bytes, _stream_handle()))
+
+    def combine(self):
+        _check(self._lib.ifa_decode_combine(ctypes.byref(self.args), self.workspace.data_ptr(),
+                                            self.workspace_bytes, _stream_handle()))
+        return self.out, self.lse
+
+    def partials(self):
+        """Views of the workspace after ``splitkv()``: (attn_out, softmax_max,
+        softmax_sum) with shapes (B, N_q, n, v_dim), (B, N_q, n), (B, N_q, n)."""
+        a = self.args
+        B, nq, n, dv = a.batch, a.num_heads, self.num_splits, a.v_dim
+        f = self.workspace.view(torch.float32) if self.workspace_bytes else None
+        rows = B * nq * n
+        al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+        off_m = al(rows * dv * 4) // 4
+        off_l = off_m + al(rows * 4) // 4
+        return (f[:rows * dv].view(B, nq, n, dv), f[off_m:off_m + rows].view(B, nq, n),
+                f[off_l:off_l + rows].view(B, nq, n))
+
+
+def decode(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads: int, num_key_value_heads: int,
+           scale_value: float, learnable_sink=None, antiquant_scale=None, antiquant_offset=None,
+           num_splits: int = 0, v_dim: Optional[int] = None,
+           out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode attention; returns (attention_out (B, N_q, v_dim), softmax_lse (B, N_q) fp32)."""
+    call = DecodeCall(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads, num_key_value_heads,
+                      scale_value, learnable_sink, antiquant_scale, antiquant_offset, num_splits, v_dim,
+                      out_dtype)
+    out, lse = call.run()
+    # the workspace must outlive the queued kernels: the caching allocator
+    # keeps it reserved for this stream
+    call.workspace.record_stream(torch.cuda.current_stream())
+    return out, lse
+
+
+def attn_update(prev_out, prev_max, prev_sum, cur_out, cur_max, cur_sum, out=None, max_out=None,
+                sum_out=None):
+    """RingAttentionUpdate of two results.  *_out: (rows, D) or (..., D);
+    *_max / *_sum: fp32 with one value per row, optionally repeated 8 times in
+    a trailing dimension of size 8.  Returns (attn_out, softmax_max,
+    softmax_sum); outputs may alias inputs."""
+    lib = load_library()
+    D = prev_out.shape[-1]
+    rows = prev_out.numel() // D if D else 0
+    for t, nm in ((prev_out, "prev_out"), (cur_out, "cur_out")):
+        _need(t, nm, prev_out.dtype)
+    for t, nm in ((prev_max, "prev_max"), (prev_sum, "prev_sum"), (cur_max, "cur_max"), (cur_sum, "cur_sum")):
+        _need(t, nm, torch.float32)
+    stride = prev_max.numel() // rows if rows else 1
+    out = out if out is not None else torch.empty_like(prev_out)
+    max_out = max_out if max_out is not None else torch.empty_like(prev_max)
+    sum_out = sum_out if sum_out is not None else torch.empty_like(prev_sum)
+    _check(lib.attn_update(prev_out.data_ptr(), prev_max.data_ptr(), prev_sum.data_ptr(), cur_out.data_ptr(),
+                           cur_max.data_ptr(), cur_sum.data_ptr(), out.data_ptr(), max_out.data_ptr(),
+                           sum_out.data_ptr(), rows, D, _DTYPE_CODE[prev_out.dtype], stride,
+                           _stream_handle()))
+    return out, max_out, sum_out
+
+
+def paged_block_count(lengths, block_size: int) -> int:
+    """Pool size sum_b ceil(L_b / block_size) (host helper of the C ABI)."""
+    lib = load_library()
+    vals = [int(x) for x in lengths]
+    arr = (ctypes.c_int64 * max(1, len(vals)))(*vals)
+    r = lib.ifa_paged_block_count(arr, len(vals), int(block_size))
+    if r < 0:
+        raise ValueError("invalid lengths or block_size")
+    return r
+
+
+def decode_workload(w, num_splits: Optional[int] = None, **kw):
+    """Convenience: decode a synthetic workload object on its device."""
+    return decode(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.n_q, w.n_kv, w.scale,
+                  learnable_sink=w.sink, antiquant_scale=w.antiquant_scale, antiquant_offset=w.antiquant_offset,
+                  num_splits=w.num_splits if num_splits is None else num_splits,
+                  v_dim=w.v_dim, out_dtype=w.out_dtype, **kw)
+
+
+def call_for_workload(w, num_splits: Optional[int] = None, **kw) -> DecodeCall:
+    return DecodeCall(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.n_q, w.n_kv, w.scale,
+                      learnable_sink=w.sink, antiquant_scale=w.antiquant_scale,
+                      antiquant_offset=w.antiquant_offset,
+                      num_splits=w.num_splits if num_splits is None else num_splits, v_dim=w.v_dim,
+                      out_dtype=w.out_dtype, **kw)

@@ -1,0 +1,367 @@
+// Host side of the C ABI: argument validation, split planning, workspace
+// sizing and kernel launches.  No allocation, no synchronisation.
+//
+// The call shape follows the two-phase API of aclnnIncreFlashAttentionV3
+// ("Function Prototype": GetWorkspaceSize validates and sizes, then the
+// second call runs on a stream) and its checks follow "Constraints"
+// (N <= 256, numHeads a multiple of numKeyValueHeads, page-attention blockSize
+// alignment, blockTable with B rows) and "Return Value" (161001 null pointer,
+// 161002 invalid parameter, 361001 runtime error).  561002 (tiling error,
+// aclnnMlaPrologV3WeightNz "Return Value") reports an unusable workspace.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/ifa_decode.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+ifa_status fail(ifa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ifa_status ok() {
+  g_last_error.clear();
+  return IFA_OK;
+}
+
+constexpr int kTargetCUs = 256;       // MI355X compute units
+constexpr int kMaxSplits = 256;
+constexpr int64_t kMaxBatch = 65536;  // aclnnIncreFlashAttentionV3 Constraints: B <= 65536
+constexpr int64_t kMaxHeads = 256;    // N <= 256
+
+enum class Path { kGqa, kMla };
+
+struct Plan {
+  Path path;
+  int64_t n_kv;
+  int group;
+  int heads_per_wg;
+  int n_split;
+  size_t off_o, off_m, off_l, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool is_float_dtype(int32_t d) { return d == IFA_F32 || d == IFA_F16 || d == IFA_BF16; }
+
+int auto_splits_gqa(const ifa_decode_args* a, int64_t n_kv, int group, int gh, int64_t max_len) {
+  const int64_t per_split = a->batch * n_kv * (group / gh);
+  int64_t n = (4LL * 2 * kTargetCUs + per_split - 1) / per_split;  // ~8 workgroups per CU
+  const int64_t by_len = (max_len + 255) / 256;                   // >= 256 tokens per split
+  if (n > by_len) n = by_len;
+  if (n < 1) n = 1;
+  if (n > 64) n = 64;
+  return (int)n;
+}
+
+int auto_splits_mla(const ifa_decode_args* a, int64_t max_len) {
+  int64_t n = (2LL * kTargetCUs + a->batch - 1) / a->batch;
+  const int64_t by_len = (max_len + 511) / 512;
+  if (n > by_len) n = by_len;
+  if (n < 1) n = 1;
+  if (n > 64) n = 64;
+  return (int)n;
+}
+
+ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
+  if (!a) return fail(IFA_ERR_PARAM_NULLPTR, "args is NULL");
+  if (a->reserved != 0) return fail(IFA_ERR_PARAM_INVALID, "reserved field must be 0");
+  if (a->batch < 0 || a->batch > kMaxBatch)
+    return fail(IFA_ERR_PARAM_INVALID, "batch %lld outside [0, %lld]", (long long)a->batch, (long long)kMaxBatch);
+  if (a->num_heads < 1 || a->num_heads > kMaxHeads)
+    return fail(IFA_ERR_PARAM_INVALID, "num_heads %lld outside [1, 256]", (long long)a->num_heads);
+  if (a->num_key_value_heads < 0 || a->num_key_value_heads > a->num_heads)
+    return fail(IFA_ERR_PARAM_INVALID, "num_key_value_heads %lld outside [0, num_heads]",
+                (long long)a->num_key_value_heads);
+  const int64_t n_kv = a->num_key_value_heads == 0 ? a->num_heads : a->num_key_value_heads;
+  if (a->num_heads % n_kv)
+    return fail(IFA_ERR_PARAM_INVALID, "num_heads %lld is not a multiple of num_key_value_heads %lld",
+                (long long)a->num_heads, (long long)n_kv);
+  if (!is_float_dtype(a->q_dtype)) return fail(IFA_ERR_PARAM_INVALID, "q_dtype %d not supported", a->q_dtype);
+  if (!is_float_dtype(a->out_dtype)) return fail(IFA_ERR_PARAM_INVALID, "out_dtype %d not supported", a->out_dtype);
+  if (a->kv_dtype == IFA_I8) {
+    if (a->antiquant_scale == nullptr || a->antiquant_offset == nullptr)
+      return fail(IFA_ERR_PARAM_NULLPTR, "int8 KV needs antiquant_scale and antiquant_offset");
+  } else if (!is_float_dtype(a->kv_dtype)) {
+    return fail(IFA_ERR_PARAM_INVALID, "kv_dtype %d not supported", a->kv_dtype);
+  } else if (a->kv_dtype != a->q_dtype) {
+    return fail(IFA_ERR_PARAM_INVALID, "float KV must have the query dtype");
+  } else if (a->antiquant_scale || a->antiquant_offset) {
+    return fail(IFA_ERR_PARAM_INVALID, "antiquant parameters given for a non-int8 KV cache");
+  }
+  if (a->kv_layout != IFA_KV_BNSD && a->kv_layout != IFA_KV_PAGED)
+    return fail(IFA_ERR_PARAM_INVALID, "kv_layout %d not supported", a->kv_layout);
+  if (a->num_splits < 0 || a->num_splits > kMaxSplits)
+    return fail(IFA_ERR_PARAM_INVALID, "num_splits %d outside [0, %d]", a->num_splits, kMaxSplits);
+
+  // head dims: (64|128, same) through the VALU path, (576, 512) with V
+  // aliasing K through the MLA path
+  const bool alias = a->value_cache != nullptr && a->value_cache == a->key_cache;
+  Path path;
+  if (a->qk_dim == 576 && a->v_dim == 512) {
+    if (!alias) return fail(IFA_ERR_PARAM_INVALID, "qk_dim 576 / v_dim 512 needs value_cache == key_cache");
+    if (a->kv_dtype != IFA_BF16) return fail(IFA_ERR_PARAM_INVALID, "the MLA shape supports bf16 only");
+    if (n_kv != 1) return fail(IFA_ERR_PARAM_INVALID, "the MLA shape needs num_key_value_heads 1");
+    if (a->num_heads % 16) return fail(IFA_ERR_PARAM_INVALID, "the MLA shape needs num_heads % 16 == 0");
+    path = Path::kMla;
+  } else if ((a->qk_dim == 64 || a->qk_dim == 128) && a->v_dim == a->qk_dim) {
+    if (alias) return fail(IFA_ERR_PARAM_INVALID, "value_cache may equal key_cache only for the MLA shape");
+    path = Path::kGqa;
+  } else {
+    return fail(IFA_ERR_PARAM_INVALID, "head dims (qk %lld, v %lld) not supported: use (64,64), (128,128) or (576,512)",
+                (long long)a->qk_dim, (long long)a->v_dim);
+  }
+
+  int64_t max_len = 0;
+  if (a->kv_layout == IFA_KV_PAGED) {
+    const int align = a->kv_dtype == IFA_I8 ? 32 : 16;
+    if (a->block_size < 16 || a->block_size > 1024 || a->block_size % align)
+      return fail(IFA_ERR_PARAM_INVALID, "block_size %lld must be a multiple of %d in [16, 1024]",
+                  (long long)a->block_size, align);
+    if (a->max_blocks_per_seq < 1) return fail(IFA_ERR_PARAM_INVALID, "max_blocks_per_seq must be >= 1");
+    if (a->num_blocks < 1 || a->num_blocks > (int64_t)1 << 31)
+      return fail(IFA_ERR_PARAM_INVALID, "num_blocks %lld outside [1, 2^31]", (long long)a->num_blocks);
+    max_len = a->max_blocks_per_seq * a->block_size;
+    if (max_len > (int64_t)1 << 31) return fail(IFA_ERR_PARAM_INVALID, "max_blocks_per_seq * block_size too large");
+  } else {
+    if (a->s_cap < 1 || a->s_cap > (int64_t)1 << 31)
+      return fail(IFA_ERR_PARAM_INVALID, "s_cap %lld outside [1, 2^31]", (long long)a->s_cap);
+    max_len = a->s_cap;
+  }
+  if (!std::isfinite(a->scale_value)) return fail(IFA_ERR_PARAM_INVALID, "scale_value is not finite");
+
+  if (a->batch > 0) {
+    if (!a->query) return fail(IFA_ERR_PARAM_NULLPTR, "query is NULL");
+    if (!a->key_cache) return fail(IFA_ERR_PARAM_NULLPTR, "key_cache is NULL");
+    if (!a->value_cache) return fail(IFA_ERR_PARAM_NULLPTR, "value_cache is NULL");
+    if (!a->actual_seq_lengths) return fail(IFA_ERR_PARAM_NULLPTR, "actual_seq_lengths is NULL");
+    if (!a->attention_out) return fail(IFA_ERR_PARAM_NULLPTR, "attention_out is NULL");
+    if (a->kv_layout == IFA_KV_PAGED && !a->block_table)
+      return fail(IFA_ERR_PARAM_NULLPTR, "block_table is NULL in the paged layout");
+  }
+
+  Plan p{};
+  p.path = path;
+  p.n_kv = n_kv;
+  p.group = (int)(a->num_heads / n_kv);
+  if (path == Path::kGqa) {
+    const int gh_max = ifa::gqa_max_heads_per_wg(a->kv_dtype, (int)a->qk_dim);
+    int gh = 1;
+    for (int c = gh_max; c >= 1; c >>= 1)
+      if (p.group % c == 0) { gh = c; break; }
+    p.heads_per_wg = gh;
+    if (!ifa::gqa_supported(a->q_dtype, a->kv_dtype, (int)a->qk_dim, gh))
+      return fail(IFA_ERR_PARAM_INVALID, "dtype combination (q %d, kv %d) not supported", a->q_dtype, a->kv_dtype);
+    p.n_split = a->num_splits ? a->num_splits : auto_splits_gqa(a, n_kv, p.group, gh, max_len);
+  } else {
+    p.heads_per_wg = (int)a->num_heads;
+    p.n_split = a->num_splits ? a->num_splits : auto_splits_mla(a, max_len);
+  }
+  const size_t rows = (size_t)a->batch * (size_t)a->num_heads * (size_t)p.n_split;
+  p.off_o = 0;
+  p.off_m = align256(rows * (size_t)a->v_dim * sizeof(float));
+  p.off_l = p.off_m + align256(rows * sizeof(float));
+  p.bytes = p.off_l + align256(rows * sizeof(float));
+  if (rows == 0) p.bytes = 0;
+  *plan = p;
+  return IFA_OK;
+}
+
+ifa_status check_workspace(const Plan& p, const void* ws, size_t ws_bytes) {
+  if (ws_bytes < p.bytes)
+    return fail(IFA_ERR_PLAN, "workspace of %zu bytes is smaller than the %zu bytes needed", ws_bytes, p.bytes);
+  if (p.bytes && !ws) return fail(IFA_ERR_PARAM_NULLPTR, "workspace is NULL");
+  if (p.bytes && (reinterpret_cast<uintptr_t>(ws) & 255))
+    return fail(IFA_ERR_PARAM_INVALID, "workspace must be 256-byte aligned");
+  return IFA_OK;
+}
+
+ifa_status runtime(hipError_t e, const char* what) {
+  if (e == hipSuccess) return IFA_OK;
+  return fail(IFA_ERR_RUNTIME, "%s: %s", what, hipGetErrorString(e));
+}
+
+ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStream_t stream) {
+  char* w = static_cast<char*>(ws);
+  const int64_t max_len = a->kv_layout == IFA_KV_PAGED ? a->max_blocks_per_seq * a->block_size : a->s_cap;
+  const float scale_log2 = (float)(a->scale_value * 1.4426950408889634);
+  if (p.path == Path::kGqa) {
+    ifa::GqaLaunch L{};
+    L.q = a->query;
+    L.k = a->key_cache;
+    L.v = a->value_cache;
+    L.block_table = a->block_table;
+    L.seq_lens = a->actual_seq_lengths;
+    L.aq_scale = a->antiquant_scale;
+    L.aq_offset = a->antiquant_offset;
+    L.ws_o = reinterpret_cast<float*>(w + p.off_o);
+    L.ws_m = reinterpret_cast<float*>(w + p.off_m);
+    L.ws_l = reinterpret_cast<float*>(w + p.off_l);
+    L.batch = (int)a->batch;
+    L.n_q = (int)a->num_heads;
+    L.n_kv = (int)p.n_kv;
+    L.group = p.group;
+    L.heads_per_wg = p.heads_per_wg;
+    L.n_split = p.n_split;
+    L.s_cap = max_len;
+    L.block_size = (int)a->block_size;
+    L.max_blocks = (int)a->max_blocks_per_seq;
+    L.num_blocks = (int)a->num_blocks;
+    L.scale_log2 = scale_log2;
+    L.q_dtype = a->q_dtype;
+    L.kv_dtype = a->kv_dtype;
+    L.head_dim = (int)a->qk_dim;
+    L.paged = a->kv_layout == IFA_KV_PAGED;
+    return runtime(ifa::launch_gqa_splitkv(L, stream), "split-KV decode launch");
+  }
+  ifa::MlaLaunch M{};
+  M.q = a->query;
+  M.kv = a->key_cache;
+  M.block_table = a->block_table;
+  M.seq_lens = a->actual_seq_lengths;
+  M.ws_o = reinterpret_cast<float*>(w + p.off_o);
+  M.ws_m = reinterpret_cast<float*>(w + p.off_m);
+  M.ws_l = reinterpret_cast<float*>(w + p.off_l);
+  M.batch = (int)a->batch;
+  M.n_q = (int)a->num_heads;
+  M.n_split = p.n_split;
+  M.s_cap = max_len;
+  M.block_size = (int)a->block_size;
+  M.max_blocks = (int)a->max_blocks_per_seq;
+  M.num_blocks = (int)a->num_blocks;
+  M.scale_log2 = scale_log2;
+  M.qk_dim = (int)a->qk_dim;
+  M.v_dim = (int)a->v_dim;
+  M.paged = a->kv_layout == IFA_KV_PAGED;
+  return runtime(ifa::launch_mla_splitkv(M, stream), "MLA split-KV decode launch");
+}
+
+ifa_status run_combine(const ifa_decode_args* a, const Plan& p, const void* ws, hipStream_t stream) {
+  const char* w = static_cast<const char*>(ws);
+  ifa::CombineLaunch C{};
+  C.ws_o = reinterpret_cast<const float*>(w + p.off_o);
+  C.ws_m = reinterpret_cast<const float*>(w + p.off_m);
+  C.ws_l = reinterpret_cast<const float*>(w + p.off_l);
+  C.seq_lens = a->actual_seq_lengths;
+  C.sink = a->learnable_sink;
+  C.out = a->attention_out;
+  C.lse = a->softmax_lse;
+  C.batch = (int)a->batch;
+  C.n_q = (int)a->num_heads;
+  C.n_split = p.n_split;
+  C.v_dim = (int)a->v_dim;
+  C.out_dtype = a->out_dtype;
+  C.s_cap = a->kv_layout == IFA_KV_PAGED ? a->max_blocks_per_seq * a->block_size : a->s_cap;
+  return runtime(ifa::launch_combine(C, stream), "combine launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+ifa_status ifa_decode_workspace_size(const ifa_decode_args* args, size_t* workspace_bytes) {
+  if (!workspace_bytes) return fail(IFA_ERR_PARAM_NULLPTR, "workspace_bytes is NULL");
+  Plan p;
+  ifa_status st = validate_and_plan(args, &p);
+  if (st != IFA_OK) return st;
+  *workspace_bytes = p.bytes;
+  return ok();
+}
+
+ifa_status ifa_decode_num_splits(const ifa_decode_args* args, int32_t* num_splits) {
+  if (!num_splits) return fail(IFA_ERR_PARAM_NULLPTR, "num_splits is NULL");
+  Plan p;
+  ifa_status st = validate_and_plan(args, &p);
+  if (st != IFA_OK) return st;
+  *num_splits = p.n_split;
+  return ok();
+}
+
+ifa_status ifa_decode_splitkv(const ifa_decode_args* args, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  Plan p;
+  ifa_status st = validate_and_plan(args, &p);
+  if (st != IFA_OK) return st;
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != IFA_OK) return st;
+  if (args->batch == 0) return ok();
+  if ((st = run_splitkv(args, p, workspace, stream)) != IFA_OK) return st;
+  return ok();
+}
+
+ifa_status ifa_decode_combine(const ifa_decode_args* args, const void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  Plan p;
+  ifa_status st = validate_and_plan(args, &p);
+  if (st != IFA_OK) return st;
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != IFA_OK) return st;
+  if (args->batch == 0) return ok();
+  if ((st = run_combine(args, p, workspace, stream)) != IFA_OK) return st;
+  return ok();
+}
+
+ifa_status ifa_decode(const ifa_decode_args* args, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Plan p;
+  ifa_status st = validate_and_plan(args, &p);
+  if (st != IFA_OK) return st;
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != IFA_OK) return st;
+  if (args->batch == 0) return ok();
+  if ((st = run_splitkv(args, p, workspace, stream)) != IFA_OK) return st;
+  if ((st = run_combine(args, p, workspace, stream)) != IFA_OK) return st;
+  return ok();
+}
+
+ifa_status attn_update(const void* prev_attn_out, const float* prev_softmax_max, const float* prev_softmax_sum,
+                       const void* cur_attn_out, const float* cur_softmax_max, const float* cur_softmax_sum,
+                       void* attn_out, float* softmax_max_out, float* softmax_sum_out, int64_t rows,
+                       int64_t head_dim, int32_t dtype, int32_t stat_stride, hipStream_t stream) {
+  if (rows < 0) return fail(IFA_ERR_PARAM_INVALID, "rows must be >= 0");
+  if (head_dim < 1 || head_dim > 65536) return fail(IFA_ERR_PARAM_INVALID, "head_dim outside [1, 65536]");
+  if (!is_float_dtype(dtype)) return fail(IFA_ERR_PARAM_INVALID, "dtype %d not supported", dtype);
+  if (stat_stride != 1 && stat_stride != 8) return fail(IFA_ERR_PARAM_INVALID, "stat_stride must be 1 or 8");
+  if (rows == 0) return ok();
+  if (!prev_attn_out || !prev_softmax_max || !prev_softmax_sum || !cur_attn_out || !cur_softmax_max ||
+      !cur_softmax_sum || !attn_out || !softmax_max_out || !softmax_sum_out)
+    return fail(IFA_ERR_PARAM_NULLPTR, "attn_update: a required pointer is NULL");
+  ifa::UpdateLaunch U{};
+  U.prev_out = prev_attn_out;
+  U.prev_max = prev_softmax_max;
+  U.prev_sum = prev_softmax_sum;
+  U.cur_out = cur_attn_out;
+  U.cur_max = cur_softmax_max;
+  U.cur_sum = cur_softmax_sum;
+  U.out = attn_out;
+  U.max_out = softmax_max_out;
+  U.sum_out = softmax_sum_out;
+  U.rows = rows;
+  U.head_dim = (int)head_dim;
+  U.dtype = dtype;
+  U.stat_stride = stat_stride;
+  ifa_status st = runtime(ifa::launch_update(U, stream), "attn_update launch");
+  if (st != IFA_OK) return st;
+  return ok();
+}
+
+int64_t ifa_paged_block_count(const int64_t* lengths, int64_t batch, int64_t block_size) {
+  if (!lengths || batch < 0 || block_size < 1) return -1;
+  int64_t total = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    if (lengths[b] < 0) return -1;
+    total += (lengths[b] + block_size - 1) / block_size;
+  }
+  return total;
+}
+
+const char* ifa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

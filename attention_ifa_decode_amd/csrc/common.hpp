@@ -1,0 +1,138 @@
+// Device helpers shared by the decode, combine and update kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ifa {
+
+enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3 };
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf162_t;
+typedef __attribute__((ext_vector_type(4))) float float4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <int DT>
+__device__ __forceinline__ float load_as_f32(const void* base, int64_t idx);
+
+template <>
+__device__ __forceinline__ float load_as_f32<kF32>(const void* base, int64_t idx) {
+  return static_cast<const float*>(base)[idx];
+}
+template <>
+__device__ __forceinline__ float load_as_f32<kF16>(const void* base, int64_t idx) {
+  return (float)static_cast<const _Float16*>(base)[idx];
+}
+template <>
+__device__ __forceinline__ float load_as_f32<kBF16>(const void* base, int64_t idx) {
+  return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
+}
+template <>
+__device__ __forceinline__ float load_as_f32<kI8>(const void* base, int64_t idx) {
+  return (float)static_cast<const int8_t*>(base)[idx];
+}
+
+template <int DT>
+__device__ __forceinline__ void store_from_f32(void* base, int64_t idx, float v);
+
+template <>
+__device__ __forceinline__ void store_from_f32<kF32>(void* base, int64_t idx, float v) {
+  static_cast<float*>(base)[idx] = v;
+}
+template <>
+__device__ __forceinline__ void store_from_f32<kF16>(void* base, int64_t idx, float v) {
+  static_cast<_Float16*>(base)[idx] = (_Float16)v;  // v_cvt_f16_f32: round to nearest even
+}
+template <>
+__device__ __forceinline__ void store_from_f32<kBF16>(void* base, int64_t idx, float v) {
+  static_cast<uint16_t*>(base)[idx] = f32_to_bf16_bits(v);
+}
+
+// ---------------------------------------------------------------------------
+// cross-lane reductions
+// ---------------------------------------------------------------------------
+
+// DPP controls (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of N consecutive lanes (N in 1,2,4,8,16); every lane
+// of the group receives the group sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  if constexpr (N >= 2) x += dpp_f32<kDppQuadXor1>(x);
+  if constexpr (N >= 4) x += dpp_f32<kDppQuadXor2>(x);
+  if constexpr (N >= 8) x += dpp_f32<kDppRowHalfMirror>(x);
+  if constexpr (N >= 16) x += dpp_f32<kDppRowMirror>(x);
+  return x;
+}
+
+// All-reduce over the lanes that differ only in lane-id bits log2(STRIDE)..5
+// (STRIDE in 4, 8, 16, 32).  Inside a 16-lane row, rotations by 4 and 8 visit
+// the four quads; rows are combined with lane shuffles.
+template <int STRIDE>
+__device__ __forceinline__ float strided_sum(float x) {
+  static_assert(STRIDE == 4 || STRIDE == 8 || STRIDE == 16 || STRIDE == 32, "stride");
+  if constexpr (STRIDE <= 4) x += dpp_f32<kDppRowRor4>(x);
+  if constexpr (STRIDE <= 8) x += dpp_f32<kDppRowRor8>(x);
+  if constexpr (STRIDE <= 16) x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+template <int STRIDE>
+__device__ __forceinline__ float strided_max(float x) {
+  static_assert(STRIDE == 4 || STRIDE == 8 || STRIDE == 16 || STRIDE == 32, "stride");
+  if constexpr (STRIDE <= 4) x = fmaxf(x, dpp_f32<kDppRowRor4>(x));
+  if constexpr (STRIDE <= 8) x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
+  if constexpr (STRIDE <= 16) x = fmaxf(x, __shfl_xor(x, 16));
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// XCD-aware work mapping.  Consecutive workgroup ids are dispatched round
+// robin over the 8 XCDs; this maps a linear id to a work index so that
+// consecutive work indices sit on the same XCD (and so share its L2).
+// `padded` is the grid size, a multiple of 8.
+// ---------------------------------------------------------------------------
+constexpr int kNumXcd = 8;
+
+__device__ __forceinline__ int xcd_remap(int id, int padded) {
+  const int per = padded / kNumXcd;
+  return (id % kNumXcd) * per + id / kNumXcd;
+}
+
+}  // namespace ifa

@@ -1,0 +1,89 @@
+// Launch descriptors shared by the host library and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ifa {
+
+// Split-KV decode over one KV head group per workgroup (VALU path).
+struct GqaLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const int64_t* seq_lens;
+  const float* aq_scale;   // (2, n_kv, D) or null
+  const float* aq_offset;  // (2, n_kv, D) or null
+  float* ws_o;             // [B][n_q][n_split][D]
+  float* ws_m;             // [B][n_q][n_split]
+  float* ws_l;             // [B][n_q][n_split]
+  int batch, n_q, n_kv, group, heads_per_wg, n_split;
+  int64_t s_cap;           // lengths are clamped to this
+  int block_size, max_blocks, num_blocks;
+  float scale_log2;        // scale * log2(e)
+  int q_dtype, kv_dtype, head_dim;
+  bool paged;
+};
+
+// MLA-shaped decode: all query heads share one latent KV head (MFMA path).
+struct MlaLaunch {
+  const void* q;           // (B, n_q, qk_dim) bf16
+  const void* kv;          // pool (num_blocks, 1, block_size, qk_dim) bf16; V = first v_dim channels
+  const int32_t* block_table;
+  const int64_t* seq_lens;
+  float* ws_o;
+  float* ws_m;
+  float* ws_l;
+  int batch, n_q, n_split;
+  int64_t s_cap;
+  int block_size, max_blocks, num_blocks;
+  float scale_log2;
+  int qk_dim, v_dim;
+  bool paged;
+};
+
+struct CombineLaunch {
+  const float* ws_o;
+  const float* ws_m;
+  const float* ws_l;
+  const int64_t* seq_lens;
+  const float* sink;  // (n_q) or null
+  void* out;          // (B, n_q, v_dim)
+  float* lse;         // (B, n_q) or null
+  int batch, n_q, n_split, v_dim, out_dtype;
+  int64_t s_cap;
+};
+
+struct UpdateLaunch {
+  const void* prev_out;
+  const float* prev_max;
+  const float* prev_sum;
+  const void* cur_out;
+  const float* cur_max;
+  const float* cur_sum;
+  void* out;
+  float* max_out;
+  float* sum_out;
+  int64_t rows;
+  int head_dim, dtype, stat_stride;
+};
+
+// Token span of split `split` out of `n_split` for a sequence of length L:
+// [split * c, min(L, (split + 1) * c)), c = 16 * ceil(ceil(L / n) / 16).
+__host__ __device__ inline int64_t split_chunk(int64_t L, int n_split) {
+  int64_t per = (L + n_split - 1) / n_split;
+  return (per + 15) & ~int64_t(15);
+}
+
+hipError_t launch_gqa_splitkv(const GqaLaunch& p, hipStream_t stream);
+hipError_t launch_mla_splitkv(const MlaLaunch& p, hipStream_t stream);
+hipError_t launch_combine(const CombineLaunch& p, hipStream_t stream);
+hipError_t launch_update(const UpdateLaunch& p, hipStream_t stream);
+
+// Which (q dtype, kv dtype, head dim, heads per workgroup) the VALU path has
+// kernels for.
+bool gqa_supported(int q_dtype, int kv_dtype, int head_dim, int heads_per_wg);
+int gqa_max_heads_per_wg(int kv_dtype, int head_dim);
+
+}  // namespace ifa

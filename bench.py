@@ -1,0 +1,223 @@
+"""Benchmark: paged decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+                    [--num-splits N] [--no-cpu-baseline]
+
+One step = one pass of the whole path over one batch: the split-KV decode
+kernel (block-table gather, QK^T, online softmax, PV, partial triples) and the
+combine kernel (n-way merge, sink, output cast, lse).  Inputs are synthetic,
+seeded and resident in HBM before timing starts.  The default workload is the
+paged bf16 GQA decode: B=64, N_q=32, N_kv=8, D=128, block size 128, lengths
+U[512, 8192], 4 KV splits.
+
+Prints one JSON line.  ``value`` is KV-cache GB/s: the bytes of K and V that
+belong to valid tokens, per step, divided by the step time.  ``roofline``
+relates the split-KV kernel's own average duration (HIP events on the launch
+stream around every launch in the timed region) to the 8 TB/s HBM peak.
+``cpu_baseline`` times the float64 oracle on a bounded sample of the same
+workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_splitkv_c3_bf16_paged_traffic.txt")
+KERNEL_SOURCES = ["attention_ifa_decode_amd/csrc/decode_gqa.hip", "attention_ifa_decode_amd/csrc/common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(config_idx: int):
+    """HBM bytes per launch of the split-KV kernel from the committed counter
+    summary, or None if absent or taken on a different kernel source."""
+    if config_idx != 3 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, budget_s: float = 20.0):
+    """The float64 oracle on the host: batches are added to the sample until
+    the estimated work reaches the time budget."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    wc = w.to("cpu")
+    lens = wc.lengths()
+    esz = wc.k_cache.element_size()
+    per_tok = wc.n_kv * wc.qk_dim * esz + (0 if wc.v_aliases_k else wc.n_kv * wc.v_dim * esz)
+    # calibrate on one batch
+    t0 = time.perf_counter()
+    oracle.decode_workload(wc, rows=[(0, h) for h in range(wc.n_q)])
+    t1 = time.perf_counter() - t0
+    rate = max(lens[0], 1) / max(t1, 1e-6)  # tokens (all heads) per second
+    sample, tok = [], 0
+    for b in range(1, wc.batch):
+        if tok / rate > budget_s:
+            break
+        sample.append(b)
+        tok += lens[b]
+    if not sample:
+        sample, tok = [0], lens[0]
+    rows = [(b, h) for b in sample for h in range(wc.n_q)]
+    t0 = time.perf_counter()
+    oracle.decode_workload(wc, rows=rows)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(tok * per_tok / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"batches {sample[0]}..{sample[-1]} ({len(sample)} of {wc.batch}, {tok} tokens, all heads), "
+                  f"{dt:.1f} s float64 NumPy",
+        "qtok_per_s": round(len(sample) / dt, 3),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the decode shards by batch, KV head or sequence; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_ifa_decode_amd as ifa
+    from synth import config_workload
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = config_workload(args.config, seed=args.seed, device=dev)
+    kv_bytes = w.kv_bytes()
+    # enough independent copies that the 256 MB infinity cache never serves KV
+    copies = 1 if kv_bytes > 3 * MALL_BYTES else min(4, -(-3 * MALL_BYTES // max(kv_bytes, 1)))
+    works = [w] + [config_workload(args.config, seed=(args.seed or 1000 + args.config) + 17 * i, device=dev)
+                   for i in range(1, copies)]
+    for x in works[1:]:  # same lengths and table, fresh values
+        x.seq_lens.copy_(w.seq_lens)
+        if x.block_table is not None:
+            x.block_table.copy_(w.block_table)
+    calls = [ifa.call_for_workload(x, num_splits=args.num_splits) for x in works]
+
+    for i in range(args.warmup):
+        calls[i % copies].run()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    stream = torch.cuda.current_stream()
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        c = calls[i % copies]
+        ev_a[i].record(stream)
+        c.splitkv()
+        ev_b[i].record(stream)
+        c.combine()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / K
+    kern_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / K
+
+    achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    traffic = read_traffic(args.config)
+    dtype_name = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}
+    lens = w.lengths()
+    result = {
+        "metric": "Paged decode attention: KV-cache HBM GB/s (% of MI355X peak) and query tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name[w.kv_dtype],
+        "data": "synthetic",
+        "qtok_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "config": {
+            "workload": w.name,
+            "batch": w.batch,
+            "num_heads": w.n_q,
+            "num_kv_heads": w.n_kv,
+            "qk_dim": w.qk_dim,
+            "v_dim": w.v_dim,
+            "kv_layout": w.layout,
+            "block_size": w.block_size,
+            "seq_len_mean": round(sum(lens) / len(lens), 1),
+            "seq_len_range": [min(lens), max(lens)],
+            "num_splits": calls[0].num_splits,
+            "kv_bytes_per_step": kv_bytes,
+            "input_copies": copies,
+            "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "gqa_splitkv_kernel" if w.qk_dim != 576 else "mla_splitkv_kernel",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel_us": round(kern_ms * 1e3, 2),
+            "combine_and_gaps_us": round((ms_step - kern_ms) * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

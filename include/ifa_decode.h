@@ -1,0 +1,185 @@
+/*
+ * ifa_decode.h — C ABI of the MI355X (gfx950) incremental decode-attention
+ * library: paged split-KV decode attention, its combine step, and the
+ * pairwise update of two attention results.
+ *
+ * What is computed (per batch b and query head h, query sequence length 1):
+ *
+ *   out[b,h] = sum_j e^(s_j - m) V_j / (sum_j e^(s_j - m) + e^(sink_h - m))
+ *   s_j      = scale_value * q[b,h] . K_j,   j < actual_seq_lengths[b]
+ *   m        = max(sink_h, max_j s_j)
+ *   lse[b,h] = m + ln(sum_j e^(s_j - m) + e^(sink_h - m))
+ *
+ * Sources (page title, section):
+ *   aclnnIncreFlashAttentionV3, "Function": Softmax(Q K^T / sqrt(d)) V for a
+ *     query whose S axis is 1, per-batch actual KV lengths; "Function
+ *     Prototype": the two-phase call (workspace size first, then launch on a
+ *     stream); "Parameters": numHeads, numKeyValueHeads (0 = numHeads),
+ *     scaleValue, blockSize, blocktable, antiquantScale/antiquantOffset;
+ *     "Constraints": page attention scenario and the KV layout
+ *     (blocknum, KV_N, blocksize, D); "Return Value": status codes.
+ *   aclnnFlashAttentionScoreV4, "计算公式": learnable sink term.
+ *   aclnnRingAttentionUpdate, "功能说明": update of an attention output from
+ *     two (attn_out, softmax_max, softmax_sum) results.
+ *   FusedInferAttentionScore blog (lpqz.cn): softmaxLse output, empty-tensor
+ *     semantics.
+ *
+ * Conventions that the pages leave open, fixed here:
+ *   - GQA: query head h reads KV head h / (num_heads / num_key_value_heads).
+ *   - antiquant (int8 K/V): x_hat = (x + offset[i][g][d]) * scale[i][g][d],
+ *     i = 0 for K, 1 for V, per KV head g and channel d, fp32 parameters.
+ *   - the sink is a logit in the units of the scaled score s_j.
+ *   - lse is a natural-log log-sum-exp and includes the sink term.
+ *   - a sequence of length 0 gives out = 0 and lse = -inf (lse = sink_h with
+ *     a sink).
+ *   - RingAttentionUpdate is applied in its sum-weighted form:
+ *       M = max(pm, cm); wp = ps e^(pm-M); wc = cs e^(cm-M) (0 when the max
+ *       is -inf); sum = wp + wc; out = (wp po + wc co) / sum (0 when sum=0).
+ *     With both sums equal to 1 this is the printed formula.
+ *
+ * Memory: the library never allocates and never synchronises.  Every pointer
+ * is a device pointer owned by the caller unless stated otherwise, and must
+ * stay valid until the work queued on `stream` has finished.  Calls are
+ * asynchronous on `stream`.  Results are deterministic: split boundaries and
+ * the merge order depend only on the arguments and the lengths.
+ *
+ * Errors: every entry point returns an ifa_status; no C++ exception crosses
+ * the ABI.  On error nothing has been queued.  ifa_last_error() returns a
+ * description of the most recent error on the calling thread.
+ */
+#ifndef IFA_DECODE_H
+#define IFA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes, mirroring the aclnn return codes of the pages
+ * (aclnnIncreFlashAttentionV3 "Return Value"; aclnnMlaPrologV3WeightNz
+ * "Return Value" for the tiling error). */
+typedef enum {
+  IFA_OK = 0,
+  IFA_ERR_PARAM_NULLPTR = 161001, /* a required pointer is NULL */
+  IFA_ERR_PARAM_INVALID = 161002, /* dtype, layout, shape or constraint */
+  IFA_ERR_RUNTIME = 361001,       /* a HIP runtime call or launch failed */
+  IFA_ERR_PLAN = 561002           /* workspace too small / no valid plan */
+} ifa_status;
+
+typedef enum { IFA_F32 = 0, IFA_F16 = 1, IFA_BF16 = 2, IFA_I8 = 3 } ifa_dtype;
+
+typedef enum {
+  /* contiguous, padded: (B, N_kv, s_cap, D); token j of batch b, KV head g
+   * at ((b * N_kv + g) * s_cap + j) * D */
+  IFA_KV_BNSD = 0,
+  /* paged pool (num_blocks, N_kv, block_size, D): token j of batch b, KV
+   * head g in block blk = block_table[b * max_blocks_per_seq + j / block_size]
+   * at ((blk * N_kv + g) * block_size + j % block_size) * D */
+  IFA_KV_PAGED = 1
+} ifa_kv_layout;
+
+/* Arguments of one decode call.  Element strides are implied by the shapes;
+ * every tensor is dense and row-major as described. */
+typedef struct {
+  const void* query;          /* (B, N_q, qk_dim), q_dtype */
+  const void* key_cache;      /* layout per kv_layout, row length qk_dim, kv_dtype */
+  const void* value_cache;    /* row length v_dim; MAY EQUAL key_cache, then V is
+                                 the first v_dim channels of each key row (MLA) */
+  const int32_t* block_table; /* (B, max_blocks_per_seq), IFA_KV_PAGED only */
+  const int64_t* actual_seq_lengths; /* (B), device; values in [0, s_cap] */
+  const float* learnable_sink;       /* (N_q) or NULL */
+  const float* antiquant_scale;      /* (2, N_kv, qk_dim) fp32; required iff kv_dtype is IFA_I8 */
+  const float* antiquant_offset;     /* (2, N_kv, qk_dim) fp32; required iff kv_dtype is IFA_I8 */
+  void* attention_out;               /* (B, N_q, v_dim), out_dtype */
+  float* softmax_lse;                /* (B, N_q) fp32, or NULL */
+  int64_t batch;                     /* B >= 0; B == 0 is a no-op */
+  int64_t num_heads;                 /* N_q, 1..256 */
+  int64_t num_key_value_heads;       /* N_kv; 0 means N_q; N_q % N_kv == 0 */
+  int64_t qk_dim;                    /* 64, 128, or 576 (MLA) */
+  int64_t v_dim;                     /* == qk_dim, or 512 with qk_dim 576 (MLA) */
+  int64_t block_size;                /* IFA_KV_PAGED: multiple of 16 (32 for int8), 16..1024 */
+  int64_t max_blocks_per_seq;        /* IFA_KV_PAGED: second dim of block_table */
+  int64_t num_blocks;                /* IFA_KV_PAGED: pool size; block ids are clamped to it */
+  int64_t s_cap;                     /* IFA_KV_BNSD: padded length; lengths are clamped to it */
+  double scale_value;                /* usually 1/sqrt(d) */
+  int32_t q_dtype;                   /* IFA_F32 / IFA_F16 / IFA_BF16 */
+  int32_t kv_dtype;                  /* == q_dtype, or IFA_I8 */
+  int32_t out_dtype;                 /* IFA_F32 / IFA_F16 / IFA_BF16 */
+  int32_t kv_layout;                 /* ifa_kv_layout */
+  int32_t num_splits;                /* KV-axis splits per sequence, 1..256; 0 = auto */
+  int32_t reserved;                  /* must be 0 */
+} ifa_decode_args;
+
+/* Phase 1 (aclnnIncreFlashAttentionV3GetWorkspaceSize): validate `args` and
+ * return in *workspace_bytes the device scratch the decode needs for its
+ * split partials.  Pure host code; never touches device memory.  Device
+ * pointers are checked for NULL only. */
+ifa_status ifa_decode_workspace_size(const ifa_decode_args* args, size_t* workspace_bytes);
+
+/* The number of KV-axis splits per sequence that a call with `args` uses
+ * (args->num_splits, or the automatic choice when it is 0).  Split i of a
+ * sequence of length L covers tokens [i*c, min(L, (i+1)*c)) with
+ * c = 16 * ceil(ceil(L / n) / 16); splits past the end are empty. */
+ifa_status ifa_decode_num_splits(const ifa_decode_args* args, int32_t* num_splits);
+
+/* Phase 2 (aclnnIncreFlashAttentionV3): split-KV decode followed by the
+ * combine, queued on `stream`.  `workspace` must hold at least the bytes
+ * phase 1 returned (IFA_ERR_PLAN otherwise); it may be NULL when that size
+ * is 0.  Writes attention_out and, when non-NULL, softmax_lse. */
+ifa_status ifa_decode(const ifa_decode_args* args, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* First half of ifa_decode: computes, for every (batch, query head, split),
+ * the partial triple over the split's tokens and stores it in `workspace`:
+ *   attn_out    fp32 [B][N_q][n][v_dim]   softmax-normalised over the split
+ *   softmax_max fp32 [B][N_q][n]          max of the scaled logits (natural units)
+ *   softmax_sum fp32 [B][N_q][n]          sum of e^(s_j - softmax_max)
+ * in that order, each array starting at a 256-byte aligned offset
+ * (n = ifa_decode_num_splits).  Empty splits are not written; the sink is not
+ * applied here. */
+ifa_status ifa_decode_splitkv(const ifa_decode_args* args, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Second half of ifa_decode: merges the non-empty split partials of each
+ * (batch, query head) in split order with the RingAttentionUpdate rule, folds
+ * in the learnable sink as one more partial (attn_out 0, max sink_h, sum 1),
+ * and writes attention_out (cast with round-to-nearest-even) and
+ * softmax_lse. */
+ifa_status ifa_decode_combine(const ifa_decode_args* args, const void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* aclnnRingAttentionUpdate: updates one attention result with another.
+ *   prev_attn_out, cur_attn_out, attn_out: (rows, head_dim), dtype
+ *     IFA_F32 / IFA_F16 / IFA_BF16 (all three the same dtype);
+ *   *_softmax_max, *_softmax_sum: fp32 (rows, stat_stride); stat_stride is
+ *     1, or 8 for the pages' layout whose last dimension repeats each value
+ *     8 times (only element 0 of each row is read; all stat_stride elements
+ *     are written).
+ * Outputs may alias the prev or cur inputs (in-place accumulation).  A max of
+ * -inf with a sum of 0 marks an empty result.  rows == 0 is a no-op. */
+ifa_status attn_update(const void* prev_attn_out, const float* prev_softmax_max,
+                       const float* prev_softmax_sum, const void* cur_attn_out,
+                       const float* cur_softmax_max, const float* cur_softmax_sum,
+                       void* attn_out, float* softmax_max_out, float* softmax_sum_out,
+                       int64_t rows, int64_t head_dim, int32_t dtype, int32_t stat_stride,
+                       hipStream_t stream);
+
+/* Block count of a paged pool (aclnnMlaPrologV3WeightNz "Constraints",
+ * BlockNum row): sum over b of ceil(lengths[b] / block_size).  Host pointer;
+ * returns -1 for a NULL pointer, a negative batch or length, or a block_size
+ * below 1. */
+int64_t ifa_paged_block_count(const int64_t* lengths, int64_t batch, int64_t block_size);
+
+/* Description of the last error on the calling thread ("" if none).  The
+ * string is owned by the library and valid until the next call on the
+ * thread. */
+const char* ifa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IFA_DECODE_H */

@@ -1,0 +1,191 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel launched).
+
+The library loads, exports every function include/ifa_decode.h declares, sizes
+workspaces, and rejects bad arguments with the pages' status codes
+(aclnnIncreFlashAttentionV3 "Return Value": 161001 null pointer, 161002
+invalid parameter; 561002 for an unusable workspace) before queueing any work.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_ifa_decode_amd as ifa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ifa_decode.h")
+FAKE = 0x1000  # a non-NULL placeholder; never dereferenced on the host
+
+
+def lib():
+    if not os.path.exists(ifa.LIB_PATH):
+        pytest.fail("library not built: run __graft_entry__.build() first")
+    return ifa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(ifa.EXPORTED), names
+    L = lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported"
+    # the symbols are plain C (unmangled) in the dynamic symbol table
+    out = os.popen(f"nm -D --defined-only {ifa.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, re.M), n
+
+
+def base_args(**kw):
+    a = ifa.DecodeArgs()
+    a.query = a.key_cache = FAKE
+    a.value_cache = FAKE + 0x100
+    a.block_table = FAKE + 0x200
+    a.actual_seq_lengths = FAKE + 0x300
+    a.attention_out = FAKE + 0x400
+    a.batch, a.num_heads, a.num_key_value_heads = 64, 32, 8
+    a.qk_dim = a.v_dim = 128
+    a.block_size, a.max_blocks_per_seq, a.num_blocks = 128, 64, 2300
+    a.scale_value = 128 ** -0.5
+    a.q_dtype = a.kv_dtype = a.out_dtype = ifa.IFA_BF16
+    a.kv_layout = ifa.IFA_KV_PAGED
+    a.num_splits = 4
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def ws_size(a):
+    sz = ctypes.c_size_t(0)
+    st = lib().ifa_decode_workspace_size(ctypes.byref(a), ctypes.byref(sz))
+    return st, sz.value
+
+
+def test_workspace_size_formula():
+    st, sz = ws_size(base_args())
+    assert st == ifa.IFA_OK, ifa.last_error()
+    rows = 64 * 32 * 4
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert sz == al(rows * 128 * 4) + 2 * al(rows * 4)
+    n = ctypes.c_int32()
+    assert lib().ifa_decode_num_splits(ctypes.byref(base_args()), ctypes.byref(n)) == 0 and n.value == 4
+
+
+def test_auto_splits_are_positive_and_deterministic():
+    a = base_args(num_splits=0)
+    n1, n2 = ctypes.c_int32(), ctypes.c_int32()
+    assert lib().ifa_decode_num_splits(ctypes.byref(a), ctypes.byref(n1)) == 0
+    assert lib().ifa_decode_num_splits(ctypes.byref(a), ctypes.byref(n2)) == 0
+    assert 1 <= n1.value <= 256 and n1.value == n2.value
+
+
+def test_batch_zero_needs_no_workspace():
+    st, sz = ws_size(base_args(batch=0))
+    assert st == 0 and sz == 0
+    # and the launch with batch 0 is a no-op that queues nothing
+    a = base_args(batch=0)
+    assert lib().ifa_decode(ctypes.byref(a), None, 0, None) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("query", 0, ifa.IFA_ERR_PARAM_NULLPTR),
+    ("key_cache", 0, ifa.IFA_ERR_PARAM_NULLPTR),
+    ("actual_seq_lengths", 0, ifa.IFA_ERR_PARAM_NULLPTR),
+    ("attention_out", 0, ifa.IFA_ERR_PARAM_NULLPTR),
+    ("block_table", 0, ifa.IFA_ERR_PARAM_NULLPTR),
+    ("num_heads", 257, ifa.IFA_ERR_PARAM_INVALID),
+    ("num_heads", 0, ifa.IFA_ERR_PARAM_INVALID),
+    ("num_key_value_heads", 5, ifa.IFA_ERR_PARAM_INVALID),   # 32 % 5 != 0
+    ("batch", 65537, ifa.IFA_ERR_PARAM_INVALID),
+    ("block_size", 120, ifa.IFA_ERR_PARAM_INVALID),           # not 16-aligned
+    ("block_size", 2048, ifa.IFA_ERR_PARAM_INVALID),
+    ("qk_dim", 96, ifa.IFA_ERR_PARAM_INVALID),
+    ("v_dim", 64, ifa.IFA_ERR_PARAM_INVALID),
+    ("q_dtype", ifa.IFA_I8, ifa.IFA_ERR_PARAM_INVALID),
+    ("kv_dtype", ifa.IFA_F16, ifa.IFA_ERR_PARAM_INVALID),      # float KV must match q
+    ("out_dtype", 7, ifa.IFA_ERR_PARAM_INVALID),
+    ("kv_layout", 5, ifa.IFA_ERR_PARAM_INVALID),
+    ("num_splits", -1, ifa.IFA_ERR_PARAM_INVALID),
+    ("num_splits", 300, ifa.IFA_ERR_PARAM_INVALID),
+    ("reserved", 1, ifa.IFA_ERR_PARAM_INVALID),
+    ("scale_value", float("nan"), ifa.IFA_ERR_PARAM_INVALID),
+    ("max_blocks_per_seq", 0, ifa.IFA_ERR_PARAM_INVALID),
+])
+def test_invalid_arguments_are_rejected(field, value, code):
+    a = base_args(**{field: value})
+    st, _ = ws_size(a)
+    assert st == code, (st, ifa.last_error())
+    assert ifa.last_error()
+    # phase 2 rejects the same arguments before touching the GPU
+    assert lib().ifa_decode(ctypes.byref(a), FAKE, 1 << 30, None) == code
+
+
+def test_int8_rules():
+    a = base_args(kv_dtype=ifa.IFA_I8)
+    assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_NULLPTR  # antiquant parameters missing
+    a = base_args(kv_dtype=ifa.IFA_I8, antiquant_scale=FAKE, antiquant_offset=FAKE)
+    assert ws_size(a)[0] == ifa.IFA_OK
+    a = base_args(kv_dtype=ifa.IFA_I8, antiquant_scale=FAKE, antiquant_offset=FAKE, block_size=48)
+    assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_INVALID  # int8 needs 32-aligned blocks
+    a = base_args(antiquant_scale=FAKE, antiquant_offset=FAKE)
+    assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_INVALID  # antiquant with float KV
+
+
+def test_mla_shape_rules():
+    mla = dict(num_heads=128, num_key_value_heads=1, qk_dim=576, v_dim=512, max_blocks_per_seq=256)
+    a = base_args(**mla)
+    assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_INVALID  # V must alias K
+    a = base_args(value_cache=FAKE, **mla)
+    assert ws_size(a)[0] == ifa.IFA_OK, ifa.last_error()
+    a = base_args(value_cache=FAKE, **dict(mla, num_key_value_heads=2))
+    assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_INVALID
+
+
+def test_workspace_too_small_or_misaligned():
+    a = base_args()
+    st, sz = ws_size(a)
+    assert lib().ifa_decode(ctypes.byref(a), FAKE, sz - 1, None) == ifa.IFA_ERR_PLAN
+    assert lib().ifa_decode_splitkv(ctypes.byref(a), FAKE, sz - 1, None) == ifa.IFA_ERR_PLAN
+    assert lib().ifa_decode_combine(ctypes.byref(a), FAKE, sz - 1, None) == ifa.IFA_ERR_PLAN
+    assert lib().ifa_decode(ctypes.byref(a), FAKE + 8, sz, None) == ifa.IFA_ERR_PARAM_INVALID
+    assert lib().ifa_decode(ctypes.byref(a), None, sz, None) == ifa.IFA_ERR_PARAM_NULLPTR
+
+
+def test_null_args_and_outputs():
+    L = lib()
+    sz = ctypes.c_size_t()
+    assert L.ifa_decode_workspace_size(None, ctypes.byref(sz)) == ifa.IFA_ERR_PARAM_NULLPTR
+    assert L.ifa_decode_workspace_size(ctypes.byref(base_args()), None) == ifa.IFA_ERR_PARAM_NULLPTR
+
+
+def test_attn_update_argument_checks():
+    L = lib()
+    p = [FAKE] * 9
+    assert L.attn_update(*p, 4, 64, ifa.IFA_BF16, 3, None) == ifa.IFA_ERR_PARAM_INVALID  # stride
+    assert L.attn_update(*p, 4, 64, ifa.IFA_I8, 1, None) == ifa.IFA_ERR_PARAM_INVALID   # dtype
+    assert L.attn_update(*p, -1, 64, ifa.IFA_F16, 1, None) == ifa.IFA_ERR_PARAM_INVALID
+    assert L.attn_update(*p, 4, 0, ifa.IFA_F16, 1, None) == ifa.IFA_ERR_PARAM_INVALID
+    q = list(p)
+    q[4] = None
+    assert L.attn_update(*q, 4, 64, ifa.IFA_F32, 8, None) == ifa.IFA_ERR_PARAM_NULLPTR
+    assert L.attn_update(*p, 0, 64, ifa.IFA_F32, 8, None) == ifa.IFA_OK  # rows == 0: no-op
+
+
+def test_block_count_worked_example():
+    """aclnnMlaPrologV3WeightNz Constraints, BlockNum row: lengths
+    [47, 104, 110, 161] at block size 128 occupy 5 blocks."""
+    import json
+
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "mla_blocknum_example.json")))
+    assert ifa.paged_block_count(g["expected_lengths"], g["block_size"]) == g["expected_block_num"]
+    assert ifa.paged_block_count([], 128) == 0
+    with pytest.raises(ValueError):
+        ifa.paged_block_count([-1], 128)

@@ -1,0 +1,217 @@
+"""GPU parity: the HIP decode path (through the C ABI) against the float64
+oracle on the same seeded inputs.
+
+Tolerances (max-abs over every output element, against the unrounded oracle):
+1e-5 for fp32 inputs, 1e-2 for fp16 / bf16 / int8-KV inputs; |lse| within
+1e-3.  An empty row must give out == 0 and lse == -inf exactly (or lse ==
+sink with a sink).  Stored KV slots that must never be read are NaN-poisoned
+(127 for int8), and unused block-table entries are -1.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_ifa_decode_amd as ifa
+import oracle
+from synth import config_workload, make_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_LOWP = 1e-2
+TOL_LSE = 1e-3
+
+
+def _announce(msg):
+    print(f"[gpu case] {msg}", flush=True)
+
+
+def _gpu(w, num_splits=None):
+    wg = w.to("cuda")
+    out, lse = ifa.decode_workload(wg, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def _compare(w, out, lse, ref_out, ref_lse, rows=None):
+    tol = TOL_F32 if w.kv_dtype == torch.float32 else TOL_LOWP
+    if rows is not None:
+        out = np.stack([out[b, h] for b, h in rows])
+        lse = np.array([lse[b, h] for b, h in rows])
+    assert out.shape == ref_out.shape
+    assert not np.isnan(out).any(), "NaN in GPU output"
+    err = np.max(np.abs(out - ref_out)) if out.size else 0.0
+    assert err <= tol, f"max-abs error {err:.3e} > {tol}"
+    fin = np.isfinite(ref_lse)
+    np.testing.assert_array_equal(lse[~fin], ref_lse[~fin])
+    if fin.any():
+        lerr = np.max(np.abs(lse[fin] - ref_lse[fin]))
+        assert lerr <= TOL_LSE, f"lse error {lerr:.3e}"
+    return err
+
+
+def _full_check(w, num_splits=None):
+    _announce(f"{w.name} B={w.batch} nq={w.n_q} nkv={w.n_kv} d={w.qk_dim} kv={w.kv_dtype} "
+              f"layout={w.layout} bs={w.block_size} lens={w.lengths()[:8]} splits={num_splits}")
+    out, lse = _gpu(w, num_splits)
+    ref_out, ref_lse = oracle.decode_workload(w)
+    return _compare(w, out, lse, ref_out, ref_lse)
+
+
+# ------------------------------------------------------------ the configs
+@pytest.mark.parametrize("splits", [2, 1, 3])
+def test_c1_tiny_fp32(splits):
+    """Tiny fp32 config at full size: B=2, N=4, D=64, 128 tokens; 2 splits
+    are the two halves of 64."""
+    w = config_workload(1, seed=100)
+    _full_check(w, splits)
+
+
+@pytest.mark.parametrize("seed", [200, 201, 202])
+def test_c2_f16_gqa_padded_reduced(seed):
+    w = config_workload(2, seed=seed, batch=5, lengths=("uniform", 1, 700), s_cap=768)
+    _full_check(w)
+
+
+@pytest.mark.parametrize("seed", [300, 301, 302])
+def test_c3_bf16_paged_reduced(seed):
+    w = config_workload(3, seed=seed, batch=6, lengths=("uniform", 100, 1100), max_blocks_per_seq=9)
+    _full_check(w)
+
+
+@pytest.mark.parametrize("seed", [400, 401])
+def test_c4_int8_antiquant_sink_reduced(seed):
+    w = config_workload(4, seed=seed, batch=3, lengths=[300, 1, 129], max_blocks_per_seq=3)
+    _full_check(w)
+
+
+# ------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("kv", ["f32", "f16", "bf16", "i8"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_ragged_lengths_every_dtype(kv, d):
+    lens = [0, 1, 15, 16, 17, 31, 127, 128, 129, 300]
+    w = make_workload(batch=len(lens), n_q=8, n_kv=2, qk_dim=d, kv_dtype=kv, layout="paged",
+                      block_size=32, lengths=lens, seed=7, sink=(kv == "i8"), extra_blocks=2)
+    _full_check(w, 3)
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
+def test_block_sizes(bs):
+    kv = "bf16"
+    w = make_workload(batch=4, n_q=8, n_kv=8, qk_dim=128, kv_dtype=kv, layout="paged", block_size=bs,
+                      lengths=[bs - 1, bs, bs + 1, 3 * bs + 5], seed=11)
+    _full_check(w, 2)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4, 7, 16, 64])
+def test_split_counts(splits):
+    """More splits than tiles leaves empty splits; every count gives the same answer."""
+    w = make_workload(batch=3, n_q=16, n_kv=4, qk_dim=128, kv_dtype="f16", layout="bnsd",
+                      lengths=[1000, 17, 1], s_cap=1024, seed=12)
+    _full_check(w, splits)
+
+
+@pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
+def test_gqa_group_sizes(group):
+    w = make_workload(batch=2, n_q=8 * group if group < 16 else 32, n_kv=8 if group < 16 else 2,
+                      qk_dim=128, kv_dtype="bf16", layout="paged", block_size=64, lengths=[200, 77], seed=13)
+    _full_check(w)
+
+
+def test_num_key_value_heads_zero_means_mha():
+    w = make_workload(batch=2, n_q=4, n_kv=0, qk_dim=64, kv_dtype="f16", layout="bnsd",
+                      lengths=[50, 64], s_cap=64, seed=14)
+    assert w.n_kv == 4
+    wg = w.to("cuda")
+    out, lse = ifa.decode(wg.q, wg.k_cache, wg.v_cache, None, wg.seq_lens, 4, 0, wg.scale)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.decode_workload(w)
+    _compare(w, out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("length", [0, 1, 7, 128])
+@pytest.mark.parametrize("sink", [-5.0, 0.0, 8.0])
+def test_sink_dedicated(length, sink):
+    """The sink adds e^(sink - m) to the denominator (aclnnFlashAttentionScoreV4
+    formula); short rows make its effect large enough to see."""
+    w = make_workload(batch=2, n_q=8, n_kv=2, qk_dim=128, kv_dtype="bf16", layout="paged", block_size=32,
+                      lengths=[length, max(1, length)], seed=15, sink=True)
+    w.sink = torch.full_like(w.sink, sink)
+    _full_check(w, 2)
+
+
+def test_empty_batch_gives_zero_and_neg_inf_lse():
+    w = make_workload(batch=3, n_q=4, n_kv=4, qk_dim=64, kv_dtype="f32", layout="bnsd",
+                      lengths=[0, 0, 0], s_cap=16, seed=16)
+    out, lse = _gpu(w, 2)
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+def test_output_dtype_f32_from_bf16():
+    w = make_workload(batch=2, n_q=8, n_kv=2, qk_dim=128, kv_dtype="bf16", out_dtype="f32", layout="paged",
+                      block_size=128, lengths=[333, 1], seed=17)
+    _full_check(w)
+
+
+def test_deterministic_bitwise():
+    w = config_workload(3, seed=303, batch=4, lengths=("uniform", 100, 1100), max_blocks_per_seq=9).to("cuda")
+    o1, l1 = ifa.decode_workload(w)
+    o2, l2 = ifa.decode_workload(w)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_partials_match_oracle_triples():
+    """ifa_decode_splitkv leaves, per (b, h, split), the triple of the
+    split's token span [i*c, min(L, (i+1)*c)), c = 16*ceil(ceil(L/n)/16)."""
+    w = make_workload(batch=3, n_q=8, n_kv=2, qk_dim=128, kv_dtype="f16", layout="paged", block_size=16,
+                      lengths=[250, 33, 1], seed=18)
+    wg = w.to("cuda")
+    call = ifa.call_for_workload(wg, num_splits=4)
+    call.splitkv()
+    torch.cuda.synchronize()
+    po, pm, ps = (x.double().cpu().numpy() for x in call.partials())
+    n = call.num_splits
+    qf = w.q.double().numpy()
+    for b, L in enumerate(w.lengths()):
+        c = 16 * math.ceil(math.ceil(L / n) / 16)
+        for g in range(2):
+            K = oracle.gather_kv(w.k_cache, "paged", b, g, L, w.block_table, 16)
+            V = oracle.gather_kv(w.v_cache, "paged", b, g, L, w.block_table, 16)
+            for h in range(g * 4, g * 4 + 4):
+                for i in range(n):
+                    a, e = i * c, min(L, (i + 1) * c)
+                    if a >= e:
+                        continue
+                    o, m, s = oracle.partial_triple(qf[b, h], K[a:e], V[a:e], w.scale)
+                    assert np.max(np.abs(po[b, h, i] - o)) < 1e-3
+                    assert abs(pm[b, h, i] - m) < 1e-4 * max(1, abs(m))
+                    assert abs(ps[b, h, i] - s) < 1e-4 * s
+
+
+# ------------------------------------------------------------ full sizes, sampled rows
+def _sampled_rows(w, k, seed):
+    rng = np.random.default_rng(seed)
+    return [(int(rng.integers(0, w.batch)), int(rng.integers(0, w.n_q))) for _ in range(k)]
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4])
+def test_full_size_sampled_rows(cfg):
+    """Each config at its full size and in the launch configuration the
+    benchmark times; the oracle recomputes a sample of rows one by one."""
+    wg = config_workload(cfg, device="cuda")
+    _announce(f"full size config {cfg}: {wg.name}")
+    out, lse = ifa.decode_workload(wg)
+    torch.cuda.synchronize()
+    out = out.double().cpu().numpy()
+    lse = lse.double().cpu().numpy()
+    assert not np.isnan(out).any()
+    w = wg.to("cpu")
+    del wg
+    torch.cuda.empty_cache()
+    rows = _sampled_rows(w, 12, cfg)
+    ref_out, ref_lse = oracle.decode_workload(w, rows=rows)
+    _compare(w, out, lse, ref_out, ref_lse, rows=rows)
