@@ -133,10 +133,14 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
     if (a->num_blocks < 1 || a->num_blocks > (int64_t)1 << 31)
       return fail(IFA_ERR_PARAM_INVALID, "num_blocks %lld outside [1, 2^31]", (long long)a->num_blocks);
     max_len = a->max_blocks_per_seq * a->block_size;
-    if (max_len > (int64_t)1 << 31) return fail(IFA_ERR_PARAM_INVALID, "max_blocks_per_seq * block_size too large");
+    if (max_len > (int64_t)1 << 30) return fail(IFA_ERR_PARAM_INVALID, "max_blocks_per_seq * block_size too large");
+    if (a->num_blocks * n_kv * a->block_size >= (int64_t)1 << 32)
+      return fail(IFA_ERR_PARAM_INVALID, "the KV pool holds 2^32 or more token rows");
   } else {
-    if (a->s_cap < 1 || a->s_cap > (int64_t)1 << 31)
-      return fail(IFA_ERR_PARAM_INVALID, "s_cap %lld outside [1, 2^31]", (long long)a->s_cap);
+    if (a->s_cap < 1 || a->s_cap > (int64_t)1 << 30)
+      return fail(IFA_ERR_PARAM_INVALID, "s_cap %lld outside [1, 2^30]", (long long)a->s_cap);
+    if (a->batch * n_kv * a->s_cap >= (int64_t)1 << 32)
+      return fail(IFA_ERR_PARAM_INVALID, "the KV buffer holds 2^32 or more token rows");
     max_len = a->s_cap;
   }
   if (!std::isfinite(a->scale_value)) return fail(IFA_ERR_PARAM_INVALID, "scale_value is not finite");
@@ -218,11 +222,13 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
     L.block_size = (int)a->block_size;
     L.max_blocks = (int)a->max_blocks_per_seq;
     L.num_blocks = (int)a->num_blocks;
+    L.paged = a->kv_layout == IFA_KV_PAGED;
     L.scale_log2 = scale_log2;
+    if (L.paged) ifa::make_divisor((uint32_t)a->block_size, &L.bs_magic, &L.bs_shift);
+    L.longest_first = a->batch <= ifa::kLongestFirstMaxBatch;
     L.q_dtype = a->q_dtype;
     L.kv_dtype = a->kv_dtype;
     L.head_dim = (int)a->qk_dim;
-    L.paged = a->kv_layout == IFA_KV_PAGED;
     return runtime(ifa::launch_gqa_splitkv(L, stream), "split-KV decode launch");
   }
   ifa::MlaLaunch M{};
@@ -241,6 +247,8 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
   M.max_blocks = (int)a->max_blocks_per_seq;
   M.num_blocks = (int)a->num_blocks;
   M.scale_log2 = scale_log2;
+  if (a->kv_layout == IFA_KV_PAGED) ifa::make_divisor((uint32_t)a->block_size, &M.bs_magic, &M.bs_shift);
+  M.longest_first = a->batch <= ifa::kLongestFirstMaxBatch;
   M.qk_dim = (int)a->qk_dim;
   M.v_dim = (int)a->v_dim;
   M.paged = a->kv_layout == IFA_KV_PAGED;

@@ -17,6 +17,14 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf162_t;
 typedef __attribute__((ext_vector_type(4))) float float4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
+// Element i of a 4-dword vector, by value.  Always go through this before a
+// __builtin_bit_cast: applied directly to a vector-element lvalue, the bit
+// cast reads element 0 with the ROCm 7.2 clang (observed on gfx950 code).
+__device__ __forceinline__ uint32_t word(const u32x4& v, int i) {
+  const uint32_t w = v[i];
+  return w;
+}
+
 // ---------------------------------------------------------------------------
 // scalar conversions
 // ---------------------------------------------------------------------------
@@ -97,17 +105,38 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Cross-row exchanges (gfx950 v_permlane16/32_swap).  Called with the same
+// value for both operands, the two results hold, at every lane, the value of
+// that lane's row and of its partner row (rows of 16 lanes: partner = row^1
+// for the 16-swap, row^2 for the 32-swap), so their sum / max is the
+// all-reduce over lanes l and l^16 (l^32).
+__device__ __forceinline__ float xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // All-reduce over the lanes that differ only in lane-id bits log2(STRIDE)..5
 // (STRIDE in 4, 8, 16, 32).  Inside a 16-lane row, rotations by 4 and 8 visit
-// the four quads; rows are combined with lane shuffles.
+// the four quads; rows are combined with the permlane swaps.
 template <int STRIDE>
 __device__ __forceinline__ float strided_sum(float x) {
   static_assert(STRIDE == 4 || STRIDE == 8 || STRIDE == 16 || STRIDE == 32, "stride");
   if constexpr (STRIDE <= 4) x += dpp_f32<kDppRowRor4>(x);
   if constexpr (STRIDE <= 8) x += dpp_f32<kDppRowRor8>(x);
-  if constexpr (STRIDE <= 16) x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  if constexpr (STRIDE <= 16) x = xor16_sum(x);
+  return xor32_sum(x);
 }
 
 template <int STRIDE>
@@ -115,9 +144,8 @@ __device__ __forceinline__ float strided_max(float x) {
   static_assert(STRIDE == 4 || STRIDE == 8 || STRIDE == 16 || STRIDE == 32, "stride");
   if constexpr (STRIDE <= 4) x = fmaxf(x, dpp_f32<kDppRowRor4>(x));
   if constexpr (STRIDE <= 8) x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
-  if constexpr (STRIDE <= 16) x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  if constexpr (STRIDE <= 16) x = xor16_max(x);
+  return xor32_max(x);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -133,6 +161,39 @@ constexpr int kNumXcd = 8;
 __device__ __forceinline__ int xcd_remap(int id, int padded) {
   const int per = padded / kNumXcd;
   return (id % kNumXcd) * per + id / kNumXcd;
+}
+
+// Batch that comes `rank`-th when sequences are ordered by descending clamped
+// length (ties by batch index).  Every thread of the workgroup must call it;
+// `sm_len` holds `batch` ints rounded up to a multiple of 4.  Dispatching long
+// sequences first keeps the last workgroups short (longest-processing-time
+// first list scheduling).
+__device__ inline int batch_of_rank(int rank, const int64_t* lens, int batch, int64_t cap, int* sm_len,
+                                    int* sm_pick) {
+  const int padded = (batch + 3) & ~3;
+  for (int i = threadIdx.x; i < padded; i += blockDim.x) {
+    int64_t L = i < batch ? lens[i] : -1;  // padding sorts last and never matches
+    L = L < -1 ? 0 : (L > cap ? cap : L);
+    sm_len[i] = (int)L;
+  }
+  __syncthreads();
+  const int4* l4 = reinterpret_cast<const int4*>(sm_len);
+  for (int i = threadIdx.x; i < batch; i += blockDim.x) {
+    const int li = sm_len[i];
+    int r = 0;
+#pragma unroll 8
+    for (int j4 = 0; j4 < padded / 4; ++j4) {
+      const int4 q = l4[j4];
+      const int j = 4 * j4;
+      r += (q.x > li) | ((q.x == li) & (j < i));
+      r += (q.y > li) | ((q.y == li) & (j + 1 < i));
+      r += (q.z > li) | ((q.z == li) & (j + 2 < i));
+      r += (q.w > li) | ((q.w == li) & (j + 3 < i));
+    }
+    if (r == rank) *sm_pick = i;
+  }
+  __syncthreads();
+  return *sm_pick;
 }
 
 }  // namespace ifa

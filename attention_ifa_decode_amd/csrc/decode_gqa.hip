@@ -46,226 +46,319 @@ __device__ __forceinline__ float elem_f32(const u32x4 (&r)[KvInfo<KV>::esz], int
   constexpr int E = 16 / KvInfo<KV>::esz;
   const int i = e / E, k = e % E;
   if constexpr (KV == kF32) {
-    return __uint_as_float(r[i][k]);
+    return __uint_as_float(word(r[i], k));
   } else if constexpr (KV == kBF16) {
-    const uint32_t w = r[i][k >> 1];
+    const uint32_t w = word(r[i], k >> 1);
     return (k & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
   } else if constexpr (KV == kF16) {
-    const uint32_t w = r[i][k >> 1];
+    const uint32_t w = word(r[i], k >> 1);
     half2_t h = __builtin_bit_cast(half2_t, w);
     return (k & 1) ? (float)h[1] : (float)h[0];
   } else {
     // (float)(byte) of the biased word maps to v_cvt_f32_ubyte{0..3}
-    const uint32_t w = r[0][k >> 2] ^ 0x80808080u;
+    const uint32_t w = word(r[0], k >> 2) ^ 0x80808080u;
     return (float)((w >> (8 * (k & 3))) & 0xffu);
   }
 }
 
+// Direct HBM -> LDS load of 16 bytes per lane (gfx950
+// global_load_lds_dwordx4): lane l reads base + voff and its 16 bytes land at
+// LDS byte address lds + 16 * l.  `base` and `lds` are wave-uniform.
+//
+// Issued from inline asm on purpose: the compiler then neither tracks these
+// loads nor guards LDS reads against them (it would wait for every
+// outstanding load before each LDS read), and the kernel orders the ring with
+// explicit vmcnt waits instead (wait_vmem).  No other vector-memory operation
+// is issued inside the streaming loop, so the counts are exact.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds) {
+#if IFA_GQA_NT_LOADS
+  // streaming hint: KV rows are read once
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:0 nt" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+#else
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+#endif
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Make the compiler complete the loads behind `x` here: an empty asm that
+// reads the register forces the wait before this point instead of at the
+// first use inside the streaming loop, where it would also drain the ring.
+template <typename T>
+__device__ __forceinline__ void settle(const T& x) {
+  asm volatile("" ::"v"(x));
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Load through the constant address space: with a wave-uniform index this
+// becomes a scalar load (s_load), which is tracked by lgkmcnt and so never
+// waits behind the vector loads in flight.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
+// Bytes of the per-wave LDS ring that K/V steps stream through.
+#ifndef IFA_GQA_NT_LOADS
+#define IFA_GQA_NT_LOADS 1
+#endif
+#ifndef IFA_GQA_RING_BYTES
+#define IFA_GQA_RING_BYTES 12288
+#endif
+constexpr int kRingBytesPerWave = IFA_GQA_RING_BYTES;
+
+template <int QT, int KV, int D, int GH>
+struct GqaShape {
+  static constexpr int C = D / 16;           // lanes per token row
+  static constexpr int TOK = 64 / C;         // tokens per step
+  static constexpr int ESZ = KvInfo<KV>::esz;
+  static constexpr int E = 16 / ESZ;         // channels per 16-byte chunk
+  static constexpr int NCH = ESZ;            // chunks per lane per row
+  static constexpr int ROWB = D * ESZ;       // bytes per token row
+  static constexpr int STEP_BYTES = 2 * NCH * 1024;  // K and V of one step, whole wave
+  static constexpr int STAGES = kRingBytesPerWave / STEP_BYTES < 2 ? 2 : kRingBytesPerWave / STEP_BYTES;
+  static constexpr int LOADS = 2 * NCH;      // load instructions per step
+  static constexpr int RING_BYTES = 4 * STAGES * STEP_BYTES;
+  static constexpr int MERGE_BYTES = 4 * GH * D * 4;
+  static constexpr int SMEM = RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES;
+};
+
 template <int QT, int KV, int D, int GH, bool PAGED>
 __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int work_items) {
-  constexpr int C = D / 16;           // lanes per token row
-  constexpr int TOK = 64 / C;         // tokens per wave step
-  constexpr int NSTEP = 16 / TOK;     // steps per 16-token tile
-  constexpr int TILE = 16;
-  constexpr int ESZ = KvInfo<KV>::esz;
-  constexpr int E = 16 / ESZ;          // channels per 16-byte chunk
-  constexpr int NCH = ESZ;             // chunks per lane
+  using S = GqaShape<QT, KV, D, GH>;
+  constexpr int C = S::C, TOK = S::TOK, E = S::E, NCH = S::NCH, ROWB = S::ROWB;
+  constexpr int STAGES = S::STAGES, LOADS = S::LOADS;
   constexpr bool DOT2 = (KV == kF16 || KV == kBF16);
-  static_assert(D % 16 == 0 && C >= 4 && TOK * NSTEP == TILE, "head dim");
+  constexpr float kRescale = 8.f;    // log2 headroom before the running reference moves
+  constexpr float kMrefInit = -1e30f;  // finite, so exp2(-inf - mref) is 0, never NaN
+  static_assert(D % 16 == 0 && C >= 4 && STAGES >= 2, "shape");
 
-  const int w = xcd_remap(blockIdx.x, gridDim.x);
+  __shared__ __attribute__((aligned(16))) int sm_len[kLongestFirstMaxBatch];
+  __shared__ int sm_pick;
+  __shared__ __attribute__((aligned(16))) char smem[S::SMEM];
+  __shared__ float sm_m[4][GH];
+  __shared__ float sm_l[4][GH];
+
+  // Work items in dispatch order: consecutive workgroups go round robin to
+  // the XCDs, so with the longest-first order every XCD receives an equal
+  // mix of long and short items.
+  const int w = blockIdx.x;
   if (w >= work_items) return;
   const int HG = a.group / GH;
   int rem = w;
   const int hg = rem % HG; rem /= HG;
   const int split = rem % a.n_split; rem /= a.n_split;
   const int g = rem % a.n_kv; rem /= a.n_kv;
-  const int b = rem;
+  const int b = a.longest_first ? batch_of_rank(rem, a.seq_lens, a.batch, a.s_cap, sm_len, &sm_pick) : rem;
 
-  int64_t L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.s_cap ? a.s_cap : L);
-  const int64_t per = split_chunk(L, a.n_split);
-  const int64_t start = (int64_t)split * per;
-  const int64_t end = (start + per < L) ? start + per : L;
+  int64_t L64 = a.seq_lens[b];
+  L64 = L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64);
+  const int L = (int)L64;
+  const int per = (int)split_chunk(L, a.n_split);
+  const int start = split * per;
+  const int end = min(L, start + per);
   if (start >= end) return;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = lane / C, c = lane % C;
   const int h0 = g * a.group + hg * GH;
-
-  // ---- q (and the int8 K-side constant) for this lane's 16 channels ----
-  // channel of element e: E * ((e / E) * C + c) + e % E
-  float qf[DOT2 ? 1 : GH][DOT2 ? 1 : 16];
-  uint32_t qp[DOT2 ? GH : 1][DOT2 ? 8 : 1];
-  float kconst[GH];  // int8: sum_d q'_d (offset_d - 128), in score units
-#pragma unroll
-  for (int h = 0; h < GH; ++h) {
-    const int64_t qrow = ((int64_t)b * a.n_q + h0 + h) * D;
-    float part = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int d = E * ((e / E) * C + c) + e % E;
-      float qv = DOT2 ? 0.f : load_as_f32<QT>(a.q, qrow + d);
-      if constexpr (KV == kI8) {
-        const float sc = a.aq_scale[(int64_t)g * D + d];
-        const float off = a.aq_offset[(int64_t)g * D + d];
-        qv *= sc;
-        part = fmaf(qv, off - 128.f, part);
-      }
-      if constexpr (DOT2) {
-        // q has the same dtype as K here: repack its raw bits
-        const uint16_t* q16 = static_cast<const uint16_t*>(a.q);
-        const uint32_t bits = q16[qrow + d];
-        if (e & 1) qp[h][e >> 1] |= bits << 16; else qp[h][e >> 1] = bits;
-      } else {
-        qf[h][e] = qv;
-      }
-    }
-    kconst[h] = (KV == kI8) ? group_sum<C>(part) : 0.f;
-  }
+  const int nsteps = (end - start + TOK - 1) / TOK;
 
   const char* kbase = static_cast<const char*>(a.k);
   const char* vbase = static_cast<const char*>(a.v);
+  char* ring = smem + wave * (STAGES * S::STEP_BYTES);  // this wave's stages: [K chunks | V chunks]
+  const uint32_t ring_lds = lds_addr(ring);
 
-  // row index (in token rows) of token j of this (b, g); j must be < end
-  auto token_row = [&](int64_t j) -> int64_t {
+  // First cache row of step `st`: TOK tokens that lie inside one block
+  // (splits start on 16-token boundaries, the block size is a multiple of 16).
+  auto step_row = [&](int st) -> uint32_t {
+    const int j0 = start + TOK * st;
     if constexpr (PAGED) {
-      int blk = a.block_table[(int64_t)b * a.max_blocks + j / a.block_size];
+      const uint32_t bi = fast_div((uint32_t)j0, a.bs_magic, a.bs_shift);
+      int blk = ld_uniform(a.block_table, (int64_t)b * a.max_blocks + bi);
       blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-      return ((int64_t)blk * a.n_kv + g) * a.block_size + j % a.block_size;
+      return ((uint32_t)blk * (uint32_t)a.n_kv + (uint32_t)g) * (uint32_t)a.block_size + (uint32_t)j0 -
+             bi * (uint32_t)a.block_size;
     } else {
-      return ((int64_t)b * a.n_kv + g) * a.s_cap + j;
+      return ((uint32_t)b * (uint32_t)a.n_kv + (uint32_t)g) * (uint32_t)a.s_cap + (uint32_t)j0;
     }
   };
 
-  auto load_tile = [&](int tile, u32x4 (&kr)[NSTEP][NCH], u32x4 (&vr)[NSTEP][NCH]) {
+  // Queue the direct-to-LDS loads of step `st` into ring stage `slot`.  Steps
+  // past the end re-read the last one, so every iteration queues the same
+  // number of loads (those reads hit L2).  Lanes past the split's end read its
+  // last valid row: finite data that the softmax weights with exactly 0.
+  auto issue = [&](int st, int slot) {
+    st = st < nsteps ? st : nsteps - 1;
+    const uint32_t row0 = step_row(st);
+    const int r = min(t, end - 1 - (start + TOK * st));
+    const uint32_t off = (uint32_t)r * ROWB + 16u * c;
+    const char* kb = kbase + (uint64_t)row0 * ROWB;
+    const char* vb = vbase + (uint64_t)row0 * ROWB;
+    const uint32_t dst = ring_lds + slot * S::STEP_BYTES;
 #pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
-      const int64_t j0 = start + (int64_t)tile * TILE + st * TOK;  // wave-uniform
-      const bool valid = j0 + t < end;
-      const int64_t row = token_row(j0 < end ? j0 : start) + t;
-      const u32x4* kp = reinterpret_cast<const u32x4*>(kbase + row * (D * ESZ)) + c;
-      const u32x4* vp = reinterpret_cast<const u32x4*>(vbase + row * (D * ESZ)) + c;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        kr[st][i] = valid ? kp[i * C] : u32x4{0u, 0u, 0u, 0u};
-        vr[st][i] = valid ? vp[i * C] : u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < NCH; ++i) {
+      dma16(kb, off + 16 * C * i, dst + 1024 * i);
+      dma16(vb, off + 16 * C * i, dst + 1024 * (NCH + i));
     }
   };
 
-  float m2[GH], lsum[GH], acc[GH][16];
+  // running state per lane (over the tokens of its lane group):
+  // mref: reference max, mtrue: true max, lsum / acc relative to mref
+  float mref[GH], mtrue[GH], lsum[GH], acc[GH][16];
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
-    m2[h] = kNegInf;
+    mref[h] = kMrefInit;
+    mtrue[h] = kNegInf;
     lsum[h] = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[h][e] = 0.f;
   }
 
-  const int64_t n_tok = end - start;
-  const int ntiles = (int)((n_tok + TILE - 1) / TILE);
-  u32x4 kc[NSTEP][NCH], vc[NSTEP][NCH], kn[NSTEP][NCH], vn[NSTEP][NCH];
-  int tile = wave;
-  if (tile < ntiles) load_tile(tile, kc, vc);
-  for (; tile < ntiles; tile += 4) {
-    if (tile + 4 < ntiles) load_tile(tile + 4, kn, vn);
-
-    float s[NSTEP][GH];
+  if (wave < nsteps) {
+    // prologue: STAGES-1 steps in flight
 #pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
-      const int64_t j = start + (int64_t)tile * TILE + st * TOK + t;
-      const bool valid = j < end;
+    for (int k = 0; k < STAGES - 1; ++k) issue(wave + 4 * k, k);
+
+    // ---- q (and the int8 K-side constant) for this lane's 16 channels ----
+    // channel of element e: E * ((e / E) * C + c) + e % E
+    float qf[DOT2 ? 1 : GH][DOT2 ? 1 : 16];
+    uint32_t qp[DOT2 ? GH : 1][DOT2 ? 8 : 1];
+    float kconst[GH];  // int8: sum_d q'_d (offset_d - 128), in score units
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+      const int64_t qrow = ((int64_t)b * a.n_q + h0 + h) * D;
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int d = E * ((e / E) * C + c) + e % E;
+        if constexpr (DOT2) {
+          // q has the dtype of K here: repack its raw bits into pairs
+          const uint32_t bits = static_cast<const uint16_t*>(a.q)[qrow + d];
+          if (e & 1) qp[h][e >> 1] |= bits << 16; else qp[h][e >> 1] = bits;
+        } else {
+          float qv = load_as_f32<QT>(a.q, qrow + d);
+          if constexpr (KV == kI8) {
+            qv *= a.aq_scale[(int64_t)g * D + d];
+            part = fmaf(qv, a.aq_offset[(int64_t)g * D + d] - 128.f, part);
+          }
+          qf[h][e] = qv;
+        }
+      }
+      kconst[h] = (KV == kI8) ? group_sum<C>(part) : 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < GH; ++h) {
+      settle(kconst[h]);
+      if constexpr (DOT2) {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) settle(qp[h][p]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) settle(qf[h][e]);
+      }
+    }
+
+    int slot = 0;
+    for (int st = wave; st < nsteps; st += 4) {
+      issue(st + 4 * (STAGES - 1), slot == 0 ? STAGES - 1 : slot - 1);
+      wait_vmem<(STAGES - 1) * LOADS>();
+      const char* src = ring + slot * S::STEP_BYTES + 16 * lane;
+      u32x4 kr[NCH];
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) kr[i] = *reinterpret_cast<const u32x4*>(src + 1024 * i);
+
+      const bool valid = start + TOK * st + t < end;
+      float s[GH];
+      bool need = false;
 #pragma unroll
       for (int h = 0; h < GH; ++h) {
         float part = 0.f;
         if constexpr (KV == kBF16) {
 #pragma unroll
-          for (int p = 0; p < 8; ++p) {
-            const uint32_t kw = kc[st][p / 4][p % 4];
+          for (int p = 0; p < 8; ++p)
             part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qp[h][p]),
-                                                   __builtin_bit_cast(bf162_t, kw), part, false);
-          }
+                                                   __builtin_bit_cast(bf162_t, word(kr[p / 4], p % 4)), part, false);
         } else if constexpr (KV == kF16) {
 #pragma unroll
-          for (int p = 0; p < 8; ++p) {
-            const uint32_t kw = kc[st][p / 4][p % 4];
+          for (int p = 0; p < 8; ++p)
             part = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qp[h][p]),
-                                          __builtin_bit_cast(half2_t, kw), part, false);
-          }
+                                          __builtin_bit_cast(half2_t, word(kr[p / 4], p % 4)), part, false);
         } else {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) part = fmaf(qf[h][e], elem_f32<KV>(kc[st], e), part);
+          for (int e = 0; e < 16; ++e) part = fmaf(qf[h][e], elem_f32<KV>(kr, e), part);
         }
-        const float dot = group_sum<C>(part);
-        s[st][h] = valid ? (dot + kconst[h]) * a.scale_log2 : kNegInf;
+        float dot = group_sum<C>(part);
+        if constexpr (KV == kI8) dot += kconst[h];
+        s[h] = valid ? dot * a.scale_log2 : kNegInf;
+        mtrue[h] = fmaxf(mtrue[h], s[h]);
+        need |= s[h] > mref[h] + kRescale;
       }
-    }
-
+      if (__builtin_amdgcn_ballot_w64(need)) {  // rare after the first step
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
-      float mx = s[0][h];
+        for (int h = 0; h < GH; ++h) {
+          const float mnew = s[h] > mref[h] + kRescale ? s[h] : mref[h];
+          const float alpha = fast_exp2(mref[h] - mnew);  // 0 on the first valid token
+          lsum[h] *= alpha;
 #pragma unroll
-      for (int st = 1; st < NSTEP; ++st) mx = fmaxf(mx, s[st][h]);
-      mx = strided_max<C>(mx);
-      const float mnew = fmaxf(m2[h], mx);
-      if (mnew > m2[h]) {
-        const float alpha = fast_exp2(m2[h] - mnew);
-        lsum[h] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
-        m2[h] = mnew;
+          for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
+          mref[h] = mnew;
+        }
       }
-    }
-
+      u32x4 vr[NCH];
 #pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
+      for (int i = 0; i < NCH; ++i) vr[i] = *reinterpret_cast<const u32x4*>(src + 1024 * (NCH + i));
       float p[GH];
 #pragma unroll
       for (int h = 0; h < GH; ++h) {
-        p[h] = fast_exp2(s[st][h] - m2[h]);
+        p[h] = fast_exp2(s[h] - mref[h]);  // <= 2^8; 0 for invalid lanes
         lsum[h] += p[h];
       }
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float vf = elem_f32<KV>(vc[st], e);
+        const float vf = elem_f32<KV>(vr, e);
 #pragma unroll
         for (int h = 0; h < GH; ++h) acc[h][e] = fmaf(p[h], vf, acc[h][e]);
       }
+      slot = slot == STAGES - 1 ? 0 : slot + 1;
     }
-
-#pragma unroll
-    for (int st = 0; st < NSTEP; ++st)
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        kc[st][i] = kn[st][i];
-        vc[st][i] = vn[st][i];
-      }
   }
+  wait_vmem<0>();  // the ring is reused below; no load may still write it
 
-  // ---- reduce over the token lanes of the wave ----
+  // ---- merge the lane groups of the wave: common max, rescale, sum ----
+  float mw[GH];
 #pragma unroll
   for (int h = 0; h < GH; ++h) {
-    lsum[h] = strided_sum<C>(lsum[h]);
+    mw[h] = strided_max<C>(mtrue[h]);
+    // lanes that saw no valid token hold lsum = acc = 0 and mref = kMrefInit
+    const float f = mref[h] == kMrefInit ? 0.f : fast_exp2(mref[h] - mw[h]);
+    lsum[h] = strided_sum<C>(lsum[h] * f);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[h][e] = strided_sum<C>(acc[h][e]);
+    for (int e = 0; e < 16; ++e) acc[h][e] = strided_sum<C>(acc[h][e] * f);
   }
 
-  // ---- merge the 4 waves through LDS and write the partial ----
-  __shared__ float sm_acc[4][GH][D];
-  __shared__ float sm_m[4][GH];
-  __shared__ float sm_l[4][GH];
+  // ---- merge the 4 waves through LDS (reusing the ring) and write ----
+  __syncthreads();
+  float* sm_acc = reinterpret_cast<float*>(smem);  // [4][GH][D]
   if (t == 0) {
 #pragma unroll
     for (int h = 0; h < GH; ++h)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sm_acc[wave][h][E * ((e / E) * C + c) + e % E] = acc[h][e];
+      for (int e = 0; e < 16; ++e) sm_acc[(wave * GH + h) * D + E * ((e / E) * C + c) + e % E] = acc[h][e];
   }
   if (lane == 0) {
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
-      sm_m[wave][h] = m2[h];
+      sm_m[wave][h] = mw[h];
       sm_l[wave][h] = lsum[h];
     }
   }
@@ -278,11 +371,11 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
     float tot = 0.f, o = 0.f;
 #pragma unroll
     for (int wv = 0; wv < 4; ++wv) {
-      const float mw = sm_m[wv][h];
-      if (mw != kNegInf) {
-        const float f = fast_exp2(mw - M);
+      const float mwv = sm_m[wv][h];
+      if (mwv != kNegInf) {
+        const float f = fast_exp2(mwv - M);
         tot = fmaf(sm_l[wv][h], f, tot);
-        o = fmaf(sm_acc[wv][h][d], f, o);
+        o = fmaf(sm_acc[(wv * GH + h) * D + d], f, o);
       }
     }
     o = o / tot;
@@ -303,7 +396,7 @@ template <int QT, int KV, int D, int GH>
 hipError_t launch_typed(const GqaLaunch& p, hipStream_t stream) {
   const int items = p.batch * p.n_kv * (p.group / GH) * p.n_split;
   if (items == 0) return hipSuccess;
-  const int padded = (items + kNumXcd - 1) / kNumXcd * kNumXcd;
+  const int padded = items;
   if (p.paged)
     hipLaunchKernelGGL((gqa_splitkv_kernel<QT, KV, D, GH, true>), dim3(padded), dim3(256), 0, stream, p, items);
   else

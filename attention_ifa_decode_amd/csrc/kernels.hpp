@@ -21,9 +21,11 @@ struct GqaLaunch {
   int batch, n_q, n_kv, group, heads_per_wg, n_split;
   int64_t s_cap;           // lengths are clamped to this
   int block_size, max_blocks, num_blocks;
+  uint32_t bs_magic, bs_shift;  // n / block_size == (umulhi(n, magic) + n) >> shift
   float scale_log2;        // scale * log2(e)
   int q_dtype, kv_dtype, head_dim;
   bool paged;
+  bool longest_first;      // order work by descending sequence length
 };
 
 // MLA-shaped decode: all query heads share one latent KV head (MFMA path).
@@ -38,9 +40,11 @@ struct MlaLaunch {
   int batch, n_q, n_split;
   int64_t s_cap;
   int block_size, max_blocks, num_blocks;
+  uint32_t bs_magic, bs_shift;
   float scale_log2;
   int qk_dim, v_dim;
   bool paged;
+  bool longest_first;
 };
 
 struct CombineLaunch {
@@ -75,6 +79,23 @@ __host__ __device__ inline int64_t split_chunk(int64_t L, int n_split) {
   int64_t per = (L + n_split - 1) / n_split;
   return (per + 15) & ~int64_t(15);
 }
+
+// Magic-number division by a runtime divisor d in [1, 2^31): for n < 2^31,
+// n / d == (umulhi(n, magic) + n) >> shift  (Granlund-Montgomery).
+inline void make_divisor(uint32_t d, uint32_t* magic, uint32_t* shift) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  *shift = s;
+  *magic = (uint32_t)((((1ull << s) - d) << 32) / d + 1);
+  if (d == 1) *magic = 0;  // (0 + n) >> 0
+}
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, uint32_t magic, uint32_t shift) {
+  return (__umulhi(n, magic) + n) >> shift;
+}
+
+// Largest batch for which the workgroups rank sequences by length on the device.
+constexpr int kLongestFirstMaxBatch = 256;
 
 hipError_t launch_gqa_splitkv(const GqaLaunch& p, hipStream_t stream);
 hipError_t launch_mla_splitkv(const MlaLaunch& p, hipStream_t stream);

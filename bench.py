@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first, so that HBM byte "
+                         "counters can be scaled against a transfer of known size")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -130,6 +133,13 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = config_workload(args.config, seed=args.seed, device=dev)
     kv_bytes = w.kv_bytes()
     # enough independent copies that the 256 MB infinity cache never serves KV
