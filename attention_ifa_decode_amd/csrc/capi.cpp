@@ -65,12 +65,25 @@ int auto_splits_gqa(const ifa_decode_args* a, int64_t n_kv, int group, int gh, i
   return (int)n;
 }
 
+// Fewest splits for which one split of the longest sequence touches at most
+// kMlaMaxTableSlice block-table entries (paged layout).
+int64_t min_splits_mla(const ifa_decode_args* a, int64_t max_len) {
+  if (a->kv_layout != IFA_KV_PAGED) return 1;
+  for (int64_t n = 1; n <= kMaxSplits; ++n)
+    if (ifa::split_chunk(max_len, (int)n) <= (int64_t)(ifa::kMlaMaxTableSlice - 2) * a->block_size) return n;
+  return kMaxSplits + 1;
+}
+
 int auto_splits_mla(const ifa_decode_args* a, int64_t max_len) {
+  // one workgroup per compute unit at a time: about two items per CU, each
+  // split at least 512 tokens long
   int64_t n = (2LL * kTargetCUs + a->batch - 1) / a->batch;
   const int64_t by_len = (max_len + 511) / 512;
   if (n > by_len) n = by_len;
   if (n < 1) n = 1;
   if (n > 64) n = 64;
+  const int64_t lo = min_splits_mla(a, max_len);
+  if (n < lo) n = lo;
   return (int)n;
 }
 
@@ -113,7 +126,8 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
     if (!alias) return fail(IFA_ERR_PARAM_INVALID, "qk_dim 576 / v_dim 512 needs value_cache == key_cache");
     if (a->kv_dtype != IFA_BF16) return fail(IFA_ERR_PARAM_INVALID, "the MLA shape supports bf16 only");
     if (n_kv != 1) return fail(IFA_ERR_PARAM_INVALID, "the MLA shape needs num_key_value_heads 1");
-    if (a->num_heads % 16) return fail(IFA_ERR_PARAM_INVALID, "the MLA shape needs num_heads % 16 == 0");
+    if (!ifa::mla_supported((int)a->num_heads))
+      return fail(IFA_ERR_PARAM_INVALID, "the MLA shape needs num_heads to be a multiple of 32");
     path = Path::kMla;
   } else if ((a->qk_dim == 64 || a->qk_dim == 128) && a->v_dim == a->qk_dim) {
     if (alias) return fail(IFA_ERR_PARAM_INVALID, "value_cache may equal key_cache only for the MLA shape");
@@ -171,6 +185,10 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
   } else {
     p.heads_per_wg = (int)a->num_heads;
     p.n_split = a->num_splits ? a->num_splits : auto_splits_mla(a, max_len);
+    if (p.n_split > kMaxSplits || p.n_split < min_splits_mla(a, max_len))
+      return fail(IFA_ERR_PARAM_INVALID,
+                  "the MLA shape needs num_splits >= %lld so that a split spans at most %d cache blocks",
+                  (long long)min_splits_mla(a, max_len), ifa::kMlaMaxTableSlice - 2);
   }
   const size_t rows = (size_t)a->batch * (size_t)a->num_heads * (size_t)p.n_split;
   p.off_o = 0;

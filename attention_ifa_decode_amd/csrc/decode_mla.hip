@@ -1,13 +1,375 @@
-// MLA-shaped split-KV decode (MFMA path): not built yet.
+// MLA-shaped split-KV decode on the matrix cores (gfx950).
+//
+// The absorbed multi-head latent attention decode of the MlaProlog pages
+// (aclnnMlaPrologV3WeightNz: query (B, S, N, 512 + 64), one combined
+// latent + rope cache row of 576 channels per token, V = the first 512
+// channels of that row) computes, per batch b and query head h,
+//   Softmax(scale * q_h K^T) V                (aclnnIncreFlashAttentionV3, "Function")
+// over the paged cache (page attention layout (blocknum, 1, blocksize, 576)).
+// All N query heads share the one KV head, so QK^T and PV are dense
+// contractions with M = heads: this path runs them on MFMA
+// (v_mfma_f32_32x32x16_bf16) and writes the split partial triples
+// (aclnnRingAttentionUpdate, "功能说明") that the combine kernel merges.
+//
+// Work decomposition.  One workgroup = one (batch, split, group of up to 128
+// heads); wave w owns 32 heads.  The split's tokens stream through LDS in
+// tiles of 32 rows x 1152 bytes, fetched straight from HBM into a 4-deep ring
+// (global_load_lds_dwordx4, issued by all waves, one barrier per tile).  Per
+// tile and wave:
+//   S^T (32 tokens x 32 heads) = K (32 x 576) . Q^T (576 x 32): 36 MFMAs, K
+//       read from LDS (ds_read_b128), Q^T held in registers for the item;
+//   online softmax per head (each lane holds one head column), with a lazy
+//       rescale that only moves the running reference when a score exceeds
+//       it by 2^8;
+//   O^T (512 x 32) += V^T (512 x 32 tokens) . P^T (32 tokens x 32): 32 MFMAs.
+//       P^T comes straight from the S^T accumulator (rounded to bf16); V^T is
+//       read from the same K rows with the transposing LDS read
+//       ds_read_b64_tr_b16, so V costs neither HBM nor LDS space of its own.
+// Rows of a tile sit in LDS with their 16-byte chunks XOR-swizzled
+// (position = chunk ^ f(row), f(row) = 2 (row & 3) + ((row >> 2) & 1)) so that
+// both the row-wise K reads and the column-wise V^T reads are free of bank
+// conflicts.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace ifa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kDqk = 576, kDv = 512;
+constexpr int kRowBytes = kDqk * 2;             // 1152 bytes per cached token row
+constexpr int kChunks = kRowBytes / 16;         // 72 chunks of 16 bytes
+constexpr int kTile = 32;                       // tokens per tile
+constexpr int kTileBytes = kTile * kRowBytes;   // 36 KB
+constexpr int kTileLoads = kTile * kChunks / 64;  // 36 wave-wide 1-KB loads per tile
+constexpr int kKSteps = kDqk / 16;              // 36 MFMA k-steps for S^T
+constexpr int kMTiles = kDv / 32;               // 16 row tiles of O^T
+constexpr float kRescale = 8.f;                 // log2 headroom of the lazy rescale
+constexpr float kMrefInit = -1e30f;
+constexpr int kPrefetchK = 4;                   // K operand reads in flight in QK^T
+constexpr int kPrefetchV = 2;                   // V^T operand pairs in flight in PV
+
+// Swizzle of row t: the 16-byte chunk c of the row is stored at position
+// c ^ swz(t) (only the low 3 bits change, so chunks stay inside their group
+// of 8).
+__device__ __forceinline__ int swz(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
+
+// Direct HBM -> LDS load of 16 bytes per lane from a per-lane address; the
+// 64 lanes' bytes land contiguously at LDS byte address `lds` (+16 per lane).
+// Issued from asm so that the compiler neither tracks it nor guards LDS
+// reads against it; the ring is ordered with explicit vmcnt waits.
+__device__ __forceinline__ void dma16_lane(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off offset:0 nt" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Make the compiler complete the loads behind `x` here rather than at its
+// first use inside the streaming loop (where the wait would drain the ring).
+template <typename T>
+__device__ __forceinline__ void settle(const T& x) {
+  asm volatile("" ::"v"(x));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+__device__ __forceinline__ bf16x8_t lds_read_b128(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) bf16x8_t*)(uintptr_t)addr;
+}
+
+__device__ __forceinline__ s16x4_t lds_read_tr16(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(uintptr_t)addr);
+}
+
+// Multiply the 16 accumulator registers of one MFMA tile by `s` in place.
+// Written as an accumulator-register read / multiply / write so that the
+// tile stays in AGPRs: a plain VALU multiply would make the register
+// allocator keep all 256 accumulator registers in VGPRs and spill.
+__device__ __forceinline__ void scale_acc(f32x16_t& v, float s) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = v[r];
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(tmp)
+                 : "v"(s));
+    v[r] = x;
+  }
+}
+
+template <int NW>
+struct MlaShape {
+  static constexpr int LOADS_W = kTileLoads / NW;  // DMA instructions per wave per tile
+  // tiles in flight, bounded by LDS (4 x 36 KB) and by the 6-bit vmcnt
+  static constexpr int STAGES = (1 + 63 / LOADS_W) < 4 ? (1 + 63 / LOADS_W) : 4;
+  static_assert(kTileLoads % NW == 0, "waves");
+};
+
+template <int NW, bool PAGED>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mla_splitkv_kernel(const MlaLaunch a) {
+  using S = MlaShape<NW>;
+  constexpr int STAGES = S::STAGES, LOADS_W = S::LOADS_W;
+  __shared__ __attribute__((aligned(16))) char ring[STAGES * kTileBytes];
+  __shared__ int sm_blk[kMlaMaxTableSlice];
+  __shared__ __attribute__((aligned(16))) int sm_len[kLongestFirstMaxBatch];
+  __shared__ int sm_pick;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5;  // which half of the MFMA k-range this lane feeds
+
+  // ---- work item: (head group, split, batch rank), longest sequences first ----
+  const int HGM = a.n_q / (32 * NW);
+  int id = blockIdx.x;
+  const int hg = id % HGM;
+  id /= HGM;
+  const int split = id % a.n_split;
+  const int rank = id / a.n_split;
+  const int b = a.longest_first ? batch_of_rank(rank, a.seq_lens, a.batch, a.s_cap, sm_len, &sm_pick) : rank;
+  int64_t L64 = a.seq_lens[b];
+  L64 = L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64);
+  const int L = (int)L64;
+  const int per = (int)split_chunk(L, a.n_split);
+  const int start = split * per;
+  const int end = min(L, start + per);
+  if (start >= end) return;  // empty split: nothing is written for it
+  const int ntiles = (end - start + kTile - 1) / kTile;
+
+  // ---- block-table slice of the split, staged in LDS ----
+  const int blk0 = PAGED ? start / a.block_size : 0;
+  if constexpr (PAGED) {
+    const int nblk = (end - 1) / a.block_size - blk0 + 1;  // <= kMlaMaxTableSlice (host check)
+    const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks + blk0;
+    for (int i = threadIdx.x; i < nblk; i += NW * 64) {
+      int v = bt[i];
+      sm_blk[i] = v < 0 ? 0 : (v >= a.num_blocks ? a.num_blocks - 1 : v);
+    }
+    __syncthreads();
+  }
+
+  const char* kv = static_cast<const char*>(a.kv);
+  const uint32_t ring_lds = lds_addr(ring);
+
+  // Queue the direct-to-LDS loads of tile j (this wave's share) into `slot`.
+  // LDS chunk position P of the tile holds row t = P / 72, chunk (P % 72) ^
+  // swz(t) of that row; rows past the split's end repeat its last row.
+  auto issue_tile = [&](int j, int slot) {
+    const int tstart = start + kTile * j;
+    const uint32_t dst = ring_lds + slot * kTileBytes;
+#pragma unroll
+    for (int i = 0; i < LOADS_W; ++i) {
+      const int ins = wave + NW * i;
+      const int P = 64 * ins + lane;
+      const int t = P / kChunks;
+      const int c = (P - kChunks * t) ^ swz(t);
+      const int tok = min(tstart + t, end - 1);
+      uint64_t row;
+      if constexpr (PAGED) {
+        const uint32_t bi = fast_div((uint32_t)tok, a.bs_magic, a.bs_shift);
+        row = (uint64_t)sm_blk[bi - blk0] * (uint32_t)a.block_size + ((uint32_t)tok - bi * (uint32_t)a.block_size);
+      } else {
+        row = (uint64_t)b * (uint64_t)a.s_cap + (uint32_t)tok;
+      }
+      dma16_lane(kv + row * kRowBytes + 16 * c, dst + 1024 * ins);
+    }
+  };
+
+  // ---- Q^T operand: this wave's 32 heads, 8 channels per lane per k-step ----
+  const int head = hg * (32 * NW) + wave * 32 + (lane & 31);
+  const bf16x8_t* qrow =
+      reinterpret_cast<const bf16x8_t*>(static_cast<const char*>(a.q) + ((int64_t)b * a.n_q + head) * kRowBytes) + h;
+  bf16x8_t qreg[kKSteps];
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = qrow[2 * ks];
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) settle(qreg[ks]);
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < ntiles) issue_tile(s, s);
+
+  // ---- per-lane LDS offsets (relative to a tile's slot) ----
+  // S^T A operand: token t = lane % 32, chunk 2 ks + h at position
+  // 8 (ks / 4) + ((2 (ks % 4) + h) ^ swz(t)).
+  uint32_t offS[4];
+  {
+    const int t = lane & 31;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) offS[j] = t * kRowBytes + 16 * ((2 * j + h) ^ swz(t));
+  }
+  // V^T A operand through the transposing read.  In each 16-lane group g,
+  // source lane s reads 4 channels (8 bytes) of row kbase + s / 4 at column
+  // nbase + 4 (s % 4); the read hands lane i of the group the 4 tokens
+  // kbase..kbase+3 of column nbase + i.  MFMA row (V channel) = lane % 32,
+  // i.e. nbase = 32 mt + 16 (g % 2); the k-slots of lane half h are the
+  // tokens 4h..4h+3 (first read) and 8+4h..8+4h+3 (second read) of each
+  // 16-token k-step, which is the token order of the S^T accumulator rows
+  // that feed P^T.
+  uint32_t offV[2];  // for even and odd mt
+  {
+    const int s = lane & 15, g = lane >> 4;
+    const int r = s >> 2, q = s & 3;
+    const int t = 4 * (g >> 1) + r;  // row within the 8-row group (+16 ks + 8 read)
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) {
+      const int x = 4 * odd + 2 * (g & 1) + (q >> 1);  // chunk within the 8-chunk group
+      offV[odd] = t * kRowBytes + 16 * (x ^ swz(t)) + 8 * (q & 1);
+    }
+  }
+
+  // lsum: sum of the fp32 weights (the partial's softmax_sum, hence lse);
+  // lsum_r: sum of the bf16-rounded weights that enter PV (normalises out)
+  float mref = kMrefInit, mtrue = kNegInf, lsum = 0.f, lsum_r = 0.f;
+  f32x16_t acc[kMTiles];
+#pragma unroll
+  for (int mt = 0; mt < kMTiles; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+
+  for (int i = 0; i < ntiles; ++i) {
+    // tile i has landed once at most the loads of the tiles queued after it
+    // are in flight (vmcnt retires in order)
+    const int after = min(STAGES - 2, ntiles - 1 - i);
+    if constexpr (STAGES >= 4) {
+      if (after >= 2) wait_vmem<2 * LOADS_W>();
+      else if (after == 1) wait_vmem<LOADS_W>();
+      else wait_vmem<0>();
+    } else if constexpr (STAGES == 3) {
+      if (after >= 1) wait_vmem<LOADS_W>();
+      else wait_vmem<0>();
+    } else {
+      wait_vmem<0>();
+    }
+    __syncthreads();  // every wave's share of tile i is in; tile i-1 is consumed
+    if (i + STAGES - 1 < ntiles) issue_tile(i + STAGES - 1, (i + STAGES - 1) % STAGES);
+    const uint32_t slot = ring_lds + (i % STAGES) * kTileBytes;
+    const int tstart = start + kTile * i;
+
+    // ---- S^T = K . Q^T ----
+    f32x16_t sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    uint32_t bS[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bS[j] = slot + offS[j];
+    bf16x8_t kbuf[kPrefetchK];  // K operands read ahead of their MFMA
+#pragma unroll
+    for (int ks = 0; ks < kPrefetchK; ++ks) kbuf[ks] = lds_read_b128(bS[ks & 3] + 128 * (ks >> 2));
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const bf16x8_t ka = kbuf[ks % kPrefetchK];
+      if (ks + kPrefetchK < kKSteps)
+        kbuf[ks % kPrefetchK] = lds_read_b128(bS[(ks + kPrefetchK) & 3] + 128 * ((ks + kPrefetchK) >> 2));
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sacc, 0, 0, 0);
+    }
+
+    // ---- online softmax over this lane's head (column) ----
+    // accumulator register r holds token 8 (r / 4) + 4 h + r % 4 of the tile
+    float sv[16];
+    float smax = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tok = tstart + 8 * (r >> 2) + 4 * h + (r & 3);
+      sv[r] = tok < end ? sacc[r] * a.scale_log2 : kNegInf;
+      smax = fmaxf(smax, sv[r]);
+    }
+    smax = xor32_max(smax);  // the other 16 tokens of the column sit in lane ^ 32
+    mtrue = fmaxf(mtrue, smax);
+    if (__builtin_amdgcn_ballot_w64(smax > mref + kRescale)) {  // rare after the first tile
+      const float mnew = smax > mref + kRescale ? smax : mref;
+      const float alpha = fast_exp2(mref - mnew);  // 0 on the first tile
+      lsum *= alpha;
+      lsum_r *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < kMTiles; ++mt) scale_acc(acc[mt], alpha);
+      mref = mnew;
+    }
+    // P^T operand: k-slot j of lane half h is accumulator register j (k-step 0)
+    // or 8 + j (k-step 1)
+    bf16x8_t pb[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pf = fast_exp2(sv[r] - mref);  // <= 2^8; 0 past the end
+      const __bf16 pr = (__bf16)pf;
+      pb[r >> 3][r & 7] = pr;
+      lsum += pf;
+      lsum_r += (float)pr;
+    }
+
+    // keep the softmax out of the PV schedule: interleaving it would lengthen
+    // register live ranges and starve the V^T read-ahead
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- O^T += V^T . P^T (MFMA n: k-step n / 16, row tile n % 16) ----
+    const uint32_t bV0 = slot + offV[0], bV1 = slot + offV[1];
+    auto vread = [&](int n) -> bf16x8_t {
+      const int kk = n / kMTiles, mt = n % kMTiles;
+      const uint32_t base = ((mt & 1) ? bV1 : bV0) + (kRowBytes * 16 * kk + 128 * (mt >> 1));
+      const s16x4_t lo = lds_read_tr16(base);
+      const s16x4_t hi = lds_read_tr16(base + kRowBytes * 8);
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8_t vbuf[kPrefetchV];
+#pragma unroll
+    for (int n = 0; n < kPrefetchV; ++n) vbuf[n] = vread(n);
+#pragma unroll
+    for (int n = 0; n < 2 * kMTiles; ++n) {
+      const bf16x8_t va = vbuf[n % kPrefetchV];
+      if (n + kPrefetchV < 2 * kMTiles) vbuf[n % kPrefetchV] = vread(n + kPrefetchV);
+      acc[n % kMTiles] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[n / kMTiles], acc[n % kMTiles], 0, 0, 0);
+    }
+  }
+
+  // ---- partial triple: normalised out, true max, sum relative to it ----
+  const float ltot = xor32_sum(lsum);
+  const float inv = 1.f / xor32_sum(lsum_r);
+#pragma unroll
+  for (int mt = 0; mt < kMTiles; ++mt) scale_acc(acc[mt], inv);
+  const int64_t row = (int64_t)b * a.n_q + head;
+  float* o = a.ws_o + (row * a.n_split + split) * kDv;
+#pragma unroll
+  for (int mt = 0; mt < kMTiles; ++mt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      f32x4_t v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[mt][4 * r4 + e];
+      *reinterpret_cast<f32x4_t*>(o + 32 * mt + 8 * r4 + 4 * h) = v;
+    }
+  if (h == 0) {
+    a.ws_m[row * a.n_split + split] = mtrue * kLn2;
+    a.ws_l[row * a.n_split + split] = ltot * fast_exp2(mref - mtrue);
+  }
+}
+
+template <int NW>
+hipError_t launch_nw(const MlaLaunch& p, hipStream_t stream) {
+  const int items = p.batch * p.n_split * (p.n_q / (32 * NW));
+  if (items == 0) return hipSuccess;
+  auto kern = p.paged ? mla_splitkv_kernel<NW, true> : mla_splitkv_kernel<NW, false>;
+  hipLaunchKernelGGL(kern, dim3(items), dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool mla_supported(int n_q) { return n_q >= 32 && n_q % 32 == 0; }
 
 hipError_t launch_mla_splitkv(const MlaLaunch& p, hipStream_t stream) {
-  (void)p;
-  (void)stream;
-  return hipErrorNotSupported;
+  if (p.qk_dim != kDqk || p.v_dim != kDv || !mla_supported(p.n_q)) return hipErrorInvalidValue;
+  if (p.n_q % 128 == 0) return launch_nw<4>(p, stream);
+  if (p.n_q % 64 == 0) return launch_nw<2>(p, stream);
+  return launch_nw<1>(p, stream);
 }
 
 }  // namespace ifa

@@ -97,6 +97,9 @@ __device__ __forceinline__ uint32_t fast_div(uint32_t n, uint32_t magic, uint32_
 // Largest batch for which the workgroups rank sequences by length on the device.
 constexpr int kLongestFirstMaxBatch = 256;
 
+// Most block-table entries one split of the MLA path may touch (staged in LDS).
+constexpr int kMlaMaxTableSlice = 1024;
+
 hipError_t launch_gqa_splitkv(const GqaLaunch& p, hipStream_t stream);
 hipError_t launch_mla_splitkv(const MlaLaunch& p, hipStream_t stream);
 hipError_t launch_combine(const CombineLaunch& p, hipStream_t stream);
@@ -106,5 +109,8 @@ hipError_t launch_update(const UpdateLaunch& p, hipStream_t stream);
 // kernels for.
 bool gqa_supported(int q_dtype, int kv_dtype, int head_dim, int heads_per_wg);
 int gqa_max_heads_per_wg(int kv_dtype, int head_dim);
+
+// Query head counts the MLA (MFMA) path has kernels for: multiples of 32.
+bool mla_supported(int n_q);
 
 }  // namespace ifa

@@ -31,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_splitkv_c3_bf16_paged_traffic.txt")
 KERNEL_SOURCES = ["attention_ifa_decode_amd/csrc/decode_gqa.hip", "attention_ifa_decode_amd/csrc/common.hpp"]
@@ -178,6 +179,8 @@ def main():
 
     achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
+    # algorithmic flops: QK^T and PV for every valid token and query head
+    flops = sum(w.lengths()) * w.n_q * 2 * (w.qk_dim + w.v_dim)
     traffic = read_traffic(args.config)
     dtype_name = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}
     lens = w.lengths()
@@ -221,6 +224,10 @@ def main():
             "traffic": traffic,
             "kernel_us": round(kern_ms * 1e3, 2),
             "combine_and_gaps_us": round((ms_step - kern_ms) * 1e3, 2),
+            "flops_per_launch": flops,
+            "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2) if w.qk_dim == 576 else None,
+            "mfma_frac_bf16_dense": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+            if w.qk_dim == 576 else None,
         },
         "cpu_baseline": None,
     }

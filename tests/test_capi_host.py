@@ -147,6 +147,19 @@ def test_mla_shape_rules():
     assert ws_size(a)[0] == ifa.IFA_OK, ifa.last_error()
     a = base_args(value_cache=FAKE, **dict(mla, num_key_value_heads=2))
     assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_INVALID
+    # the MFMA path takes query heads in groups of 32
+    a = base_args(value_cache=FAKE, **dict(mla, num_heads=48))
+    assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_INVALID
+    a = base_args(value_cache=FAKE, **dict(mla, num_heads=96))
+    assert ws_size(a)[0] == ifa.IFA_OK, ifa.last_error()
+    # one split may touch at most 1022 cache blocks (its block-table slice sits in LDS)
+    long_seq = dict(mla, block_size=16, max_blocks_per_seq=4096, num_blocks=1 << 20)
+    a = base_args(value_cache=FAKE, **dict(long_seq, num_splits=1))
+    assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_INVALID
+    a = base_args(value_cache=FAKE, **dict(long_seq, num_splits=0))
+    n = ctypes.c_int32()
+    assert lib().ifa_decode_num_splits(ctypes.byref(a), ctypes.byref(n)) == ifa.IFA_OK, ifa.last_error()
+    assert (4096 * 16 + n.value - 1) // n.value <= 1022 * 16
 
 
 def test_workspace_too_small_or_misaligned():
