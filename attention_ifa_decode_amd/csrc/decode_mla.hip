@@ -26,9 +26,10 @@
 //       read from the same K rows with the transposing LDS read
 //       ds_read_b64_tr_b16, so V costs neither HBM nor LDS space of its own.
 // Rows of a tile sit in LDS with their 16-byte chunks XOR-swizzled
-// (position = chunk ^ f(row), f(row) = 2 (row & 3) + ((row >> 2) & 1)) so that
-// both the row-wise K reads and the column-wise V^T reads are free of bank
-// conflicts.
+// (position = chunk ^ f(row), f(row) = (2 (row & 3) + ((row >> 2) & 1)) ^
+// (2 ((row >> 3) & 1))) so that both the row-wise K reads and the column-wise
+// V^T reads are free of bank conflicts, whether the LDS serves 16-byte reads
+// in phases of 8 lanes over 32 banks or of 16 lanes over 64 banks.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -50,13 +51,12 @@ constexpr int kKSteps = kDqk / 16;              // 36 MFMA k-steps for S^T
 constexpr int kMTiles = kDv / 32;               // 16 row tiles of O^T
 constexpr float kRescale = 8.f;                 // log2 headroom of the lazy rescale
 constexpr float kMrefInit = -1e30f;
-constexpr int kPrefetchK = 4;                   // K operand reads in flight in QK^T
-constexpr int kPrefetchV = 2;                   // V^T operand pairs in flight in PV
 
 // Swizzle of row t: the 16-byte chunk c of the row is stored at position
 // c ^ swz(t) (only the low 3 bits change, so chunks stay inside their group
-// of 8).
-__device__ __forceinline__ int swz(int t) { return 2 * (t & 3) + ((t >> 2) & 1); }
+// of 8).  Rows t and t + 8 get different values, so 16 consecutive rows hit
+// 16 different 16-byte bank groups.
+__device__ __forceinline__ int swz(int t) { return (2 * (t & 3) + ((t >> 2) & 1)) ^ (2 * ((t >> 3) & 1)); }
 
 // Direct HBM -> LDS load of 16 bytes per lane from a per-lane address; the
 // 64 lanes' bytes land contiguously at LDS byte address `lds` (+16 per lane).
@@ -64,6 +64,11 @@ __device__ __forceinline__ int swz(int t) { return 2 * (t & 3) + ((t >> 2) & 1);
 // reads against it; the ring is ordered with explicit vmcnt waits.
 __device__ __forceinline__ void dma16_lane(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off offset:0 nt" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// Same, from a wave-uniform base plus a 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16_off(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:0 nt" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
 
 template <int N>
@@ -114,7 +119,9 @@ struct MlaShape {
   static_assert(kTileLoads % NW == 0, "waves");
 };
 
-template <int NW, bool PAGED>
+// OFF32: the whole cache lies within 4 GiB of its base (rows < 2^24), so a
+// row's address is the base plus a 32-bit offset (24-bit multiplies).
+template <int NW, bool PAGED, bool OFF32>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 mla_splitkv_kernel(const MlaLaunch a) {
   using S = MlaShape<NW>;
@@ -147,8 +154,8 @@ mla_splitkv_kernel(const MlaLaunch a) {
 
   // ---- block-table slice of the split, staged in LDS ----
   const int blk0 = PAGED ? start / a.block_size : 0;
+  const int nblk = PAGED ? (end - 1) / a.block_size - blk0 + 1 : 0;  // <= kMlaMaxTableSlice (host check)
   if constexpr (PAGED) {
-    const int nblk = (end - 1) / a.block_size - blk0 + 1;  // <= kMlaMaxTableSlice (host check)
     const int32_t* bt = a.block_table + (int64_t)b * a.max_blocks + blk0;
     for (int i = threadIdx.x; i < nblk; i += NW * 64) {
       int v = bt[i];
@@ -160,27 +167,77 @@ mla_splitkv_kernel(const MlaLaunch a) {
   const char* kv = static_cast<const char*>(a.kv);
   const uint32_t ring_lds = lds_addr(ring);
 
-  // Queue the direct-to-LDS loads of tile j (this wave's share) into `slot`.
-  // LDS chunk position P of the tile holds row t = P / 72, chunk (P % 72) ^
-  // swz(t) of that row; rows past the split's end repeat its last row.
-  auto issue_tile = [&](int j, int slot) {
-    const int tstart = start + kTile * j;
-    const uint32_t dst = ring_lds + slot * kTileBytes;
-#pragma unroll
-    for (int i = 0; i < LOADS_W; ++i) {
-      const int ins = wave + NW * i;
-      const int P = 64 * ins + lane;
-      const int t = P / kChunks;
-      const int c = (P - kChunks * t) ^ swz(t);
-      const int tok = min(tstart + t, end - 1);
-      uint64_t row;
+  // Queue the direct-to-LDS loads of tile j (this wave's share) into a ring
+  // slot.  LDS chunk position P of the tile holds row t = P / 72, chunk
+  // (P % 72) ^ swz(t) of that row; rows past the split's end repeat its last
+  // row.  plan_tile reads the ids of the (at most 3) cache blocks the tile's
+  // 32 tokens lie in and, per lane, the byte offset of one tile row;
+  // issue_loads then queues loads [i0, i0 + n) of this wave.
+  struct TilePlan {
+    int tstart;
+    uint32_t dst, tok0, adj0, adj1, adj2;
+    uint32_t rowoff;  // OFF32: lane r holds the byte offset of tile row r % 32
+  };
+  auto plan_tile = [&](int j, int slot) -> TilePlan {
+    TilePlan tp;
+    tp.tstart = start + kTile * j;
+    tp.dst = ring_lds + slot * kTileBytes;
+    tp.tok0 = tp.adj0 = tp.adj1 = tp.adj2 = 0;
+    if constexpr (PAGED) {
+      // token tok sits in block adj_sel at slot u - sel * block_size,
+      // u = tok - tok0, sel = u / block_size (at most 3 blocks per tile)
+      const uint32_t bi0 = fast_div((uint32_t)tp.tstart, a.bs_magic, a.bs_shift);
+      const int k0 = (int)bi0 - blk0;
+      tp.tok0 = bi0 * (uint32_t)a.block_size;
+      tp.adj0 = (uint32_t)__builtin_amdgcn_readfirstlane(sm_blk[k0]);
+      tp.adj1 = (uint32_t)__builtin_amdgcn_readfirstlane(sm_blk[min(k0 + 1, nblk - 1)]);
+      tp.adj2 = (uint32_t)__builtin_amdgcn_readfirstlane(sm_blk[min(k0 + 2, nblk - 1)]);
+    } else {
+      tp.adj0 = (uint32_t)b * (uint32_t)a.s_cap;  // row of token 0 of the sequence
+    }
+    tp.rowoff = 0;
+    if constexpr (OFF32) {
+      const uint32_t u = (uint32_t)min(tp.tstart + (lane & 31), end - 1) - tp.tok0;
+      uint32_t row = tp.adj0 + u;
       if constexpr (PAGED) {
-        const uint32_t bi = fast_div((uint32_t)tok, a.bs_magic, a.bs_shift);
-        row = (uint64_t)sm_blk[bi - blk0] * (uint32_t)a.block_size + ((uint32_t)tok - bi * (uint32_t)a.block_size);
-      } else {
-        row = (uint64_t)b * (uint64_t)a.s_cap + (uint32_t)tok;
+        const uint32_t bs = (uint32_t)a.block_size;
+        row = u >= 2 * bs ? tp.adj2 * bs + (u - 2 * bs) : (u >= bs ? tp.adj1 * bs + (u - bs) : tp.adj0 * bs + u);
       }
-      dma16_lane(kv + row * kRowBytes + 16 * c, dst + 1024 * ins);
+      tp.rowoff = __umul24(row, (uint32_t)kRowBytes);
+    }
+    return tp;
+  };
+  auto issue_loads = [&](const TilePlan tp, int i0, int n) {
+#pragma unroll
+    for (int i = i0; i < i0 + n; ++i) {
+      const int ins = wave + NW * i;
+      if constexpr (OFF32) {
+        // the instruction's 64 chunks are chunks lane + k1 of tile row t0 and,
+        // from lane 72 - k1 on, chunks lane + k1 - 72 of row t0 + 1
+        const int t0 = (64 * ins) / kChunks;
+        const int k1 = 64 * ins - kChunks * t0;
+        const uint32_t r0 = __builtin_amdgcn_readlane(tp.rowoff, t0);
+        const uint32_t r1 = __builtin_amdgcn_readlane(tp.rowoff, min(t0 + 1, kTile - 1));
+        const bool second = lane >= kChunks - k1;
+        const int pin = lane + k1 - (second ? kChunks : 0);
+        const int sw = second ? swz(t0 + 1) : swz(t0);
+        dma16_off(kv, (second ? r1 : r0) + 16u * (uint32_t)(pin ^ sw), tp.dst + 1024 * ins);
+      } else {
+        const int P = 64 * ins + lane;
+        const int t = P / kChunks;
+        const int c = (P - kChunks * t) ^ swz(t);
+        const int tok = min(tp.tstart + t, end - 1);
+        uint64_t row;
+        if constexpr (PAGED) {
+          const uint32_t bs = (uint32_t)a.block_size;
+          const uint32_t u = (uint32_t)tok - tp.tok0;
+          row = u >= 2 * bs ? (uint64_t)tp.adj2 * bs + (u - 2 * bs)
+                            : (u >= bs ? (uint64_t)tp.adj1 * bs + (u - bs) : (uint64_t)tp.adj0 * bs + u);
+        } else {
+          row = (uint64_t)tp.adj0 + (uint32_t)tok;
+        }
+        dma16_lane(kv + row * kRowBytes + 16 * c, tp.dst + 1024 * ins);
+      }
     }
   };
 
@@ -196,7 +253,7 @@ mla_splitkv_kernel(const MlaLaunch a) {
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < ntiles) issue_tile(s, s);
+    if (s < ntiles) issue_loads(plan_tile(s, s), 0, LOADS_W);
 
   // ---- per-lane LDS offsets (relative to a tile's slot) ----
   // S^T A operand: token t = lane % 32, chunk 2 ks + h at position
@@ -215,15 +272,18 @@ mla_splitkv_kernel(const MlaLaunch a) {
   // tokens 4h..4h+3 (first read) and 8+4h..8+4h+3 (second read) of each
   // 16-token k-step, which is the token order of the S^T accumulator rows
   // that feed P^T.
-  uint32_t offV[2];  // for even and odd mt
+  uint32_t offV[2][2];  // [odd mt][second read, 8 rows further]
   {
     const int s = lane & 15, g = lane >> 4;
     const int r = s >> 2, q = s & 3;
-    const int t = 4 * (g >> 1) + r;  // row within the 8-row group (+16 ks + 8 read)
 #pragma unroll
-    for (int odd = 0; odd < 2; ++odd) {
-      const int x = 4 * odd + 2 * (g & 1) + (q >> 1);  // chunk within the 8-chunk group
-      offV[odd] = t * kRowBytes + 16 * (x ^ swz(t)) + 8 * (q & 1);
+    for (int rd = 0; rd < 2; ++rd) {
+      const int t = 8 * rd + 4 * (g >> 1) + r;  // row within the 16-token k-step
+#pragma unroll
+      for (int odd = 0; odd < 2; ++odd) {
+        const int x = 4 * odd + 2 * (g & 1) + (q >> 1);  // chunk within the 8-chunk group
+        offV[odd][rd] = t * kRowBytes + 16 * (x ^ swz(t)) + 8 * (q & 1);
+      }
     }
   }
 
@@ -251,38 +311,51 @@ mla_splitkv_kernel(const MlaLaunch a) {
       wait_vmem<0>();
     }
     __syncthreads();  // every wave's share of tile i is in; tile i-1 is consumed
-    if (i + STAGES - 1 < ntiles) issue_tile(i + STAGES - 1, (i + STAGES - 1) % STAGES);
+    // tile i + STAGES - 1 goes into the slot of tile i - 1
+    if (i + STAGES - 1 < ntiles) issue_loads(plan_tile(i + STAGES - 1, (i + STAGES - 1) % STAGES), 0, LOADS_W);
     const uint32_t slot = ring_lds + (i % STAGES) * kTileBytes;
     const int tstart = start + kTile * i;
 
-    // ---- S^T = K . Q^T ----
+    // ---- S^T = K . Q^T (one accumulator: a second one would leave no
+    // registers for reading K ahead of the MFMAs) ----
     f32x16_t sacc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
     uint32_t bS[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) bS[j] = slot + offS[j];
-    bf16x8_t kbuf[kPrefetchK];  // K operands read ahead of their MFMA
+    // K operands are read one group of 4 k-steps ahead of their MFMAs; the
+    // scheduling fences keep the compiler from pulling each read down next to
+    // its MFMA (which would expose the full LDS latency at every step)
+    bf16x8_t kbuf[2][4];
 #pragma unroll
-    for (int ks = 0; ks < kPrefetchK; ++ks) kbuf[ks] = lds_read_b128(bS[ks & 3] + 128 * (ks >> 2));
+    for (int j = 0; j < 4; ++j) kbuf[0][j] = lds_read_b128(bS[j]);
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const bf16x8_t ka = kbuf[ks % kPrefetchK];
-      if (ks + kPrefetchK < kKSteps)
-        kbuf[ks % kPrefetchK] = lds_read_b128(bS[(ks + kPrefetchK) & 3] + 128 * ((ks + kPrefetchK) >> 2));
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sacc, 0, 0, 0);
+    for (int grp = 0; grp < kKSteps / 4; ++grp) {
+      if (grp + 1 < kKSteps / 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kbuf[(grp + 1) & 1][j] = lds_read_b128(bS[j] + 128 * (grp + 1));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kbuf[grp & 1][j], qreg[4 * grp + j], sacc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- online softmax over this lane's head (column) ----
     // accumulator register r holds token 8 (r / 4) + 4 h + r % 4 of the tile
     float sv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = sacc[r] * a.scale_log2;
+    if (tstart + kTile > end) {  // the split's last tile: tokens past its end weigh 0
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (tstart + 8 * (r >> 2) + 4 * h + (r & 3) >= end) sv[r] = kNegInf;
+    }
     float smax = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tok = tstart + 8 * (r >> 2) + 4 * h + (r & 3);
-      sv[r] = tok < end ? sacc[r] * a.scale_log2 : kNegInf;
-      smax = fmaxf(smax, sv[r]);
-    }
+    for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sv[r]);
     smax = xor32_max(smax);  // the other 16 tokens of the column sit in lane ^ 32
     mtrue = fmaxf(mtrue, smax);
     if (__builtin_amdgcn_ballot_w64(smax > mref + kRescale)) {  // rare after the first tile
@@ -300,33 +373,47 @@ mla_splitkv_kernel(const MlaLaunch a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float pf = fast_exp2(sv[r] - mref);  // <= 2^8; 0 past the end
-      const __bf16 pr = (__bf16)pf;
-      pb[r >> 3][r & 7] = pr;
+      pb[r >> 3][r & 7] = (__bf16)pf;
       lsum += pf;
-      lsum_r += (float)pr;
     }
+    const bf162_t ones = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int r = 0; r < 16; r += 2)
+      lsum_r = __builtin_amdgcn_fdot2_f32_bf16(bf162_t{pb[r >> 3][r & 7], pb[r >> 3][(r & 7) + 1]}, ones, lsum_r,
+                                               false);
 
     // keep the softmax out of the PV schedule: interleaving it would lengthen
     // register live ranges and starve the V^T read-ahead
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- O^T += V^T . P^T (MFMA n: k-step n / 16, row tile n % 16) ----
-    const uint32_t bV0 = slot + offV[0], bV1 = slot + offV[1];
+    const uint32_t bV[2][2] = {{slot + offV[0][0], slot + offV[0][1]}, {slot + offV[1][0], slot + offV[1][1]}};
     auto vread = [&](int n) -> bf16x8_t {
       const int kk = n / kMTiles, mt = n % kMTiles;
-      const uint32_t base = ((mt & 1) ? bV1 : bV0) + (kRowBytes * 16 * kk + 128 * (mt >> 1));
-      const s16x4_t lo = lds_read_tr16(base);
-      const s16x4_t hi = lds_read_tr16(base + kRowBytes * 8);
+      const uint32_t imm = kRowBytes * 16 * kk + 128 * (mt >> 1);
+      const s16x4_t lo = lds_read_tr16(bV[mt & 1][0] + imm);
+      const s16x4_t hi = lds_read_tr16(bV[mt & 1][1] + imm);
       return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    bf16x8_t vbuf[kPrefetchV];
+    // V^T operands are read one group of 4 MFMAs ahead (scheduling fences as
+    // in QK^T)
+    bf16x8_t vbuf[2][4];
 #pragma unroll
-    for (int n = 0; n < kPrefetchV; ++n) vbuf[n] = vread(n);
+    for (int j = 0; j < 4; ++j) vbuf[0][j] = vread(j);
 #pragma unroll
-    for (int n = 0; n < 2 * kMTiles; ++n) {
-      const bf16x8_t va = vbuf[n % kPrefetchV];
-      if (n + kPrefetchV < 2 * kMTiles) vbuf[n % kPrefetchV] = vread(n + kPrefetchV);
-      acc[n % kMTiles] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[n / kMTiles], acc[n % kMTiles], 0, 0, 0);
+    for (int grp = 0; grp < 2 * kMTiles / 4; ++grp) {
+      if (grp + 1 < 2 * kMTiles / 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vbuf[(grp + 1) & 1][j] = vread(4 * (grp + 1) + j);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = 4 * grp + j;
+        acc[n % kMTiles] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vbuf[grp & 1][j], pb[n / kMTiles], acc[n % kMTiles], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -356,7 +443,10 @@ template <int NW>
 hipError_t launch_nw(const MlaLaunch& p, hipStream_t stream) {
   const int items = p.batch * p.n_split * (p.n_q / (32 * NW));
   if (items == 0) return hipSuccess;
-  auto kern = p.paged ? mla_splitkv_kernel<NW, true> : mla_splitkv_kernel<NW, false>;
+  const uint64_t rows = p.paged ? (uint64_t)p.num_blocks * (uint64_t)p.block_size : (uint64_t)p.batch * (uint64_t)p.s_cap;
+  const bool off32 = rows * kRowBytes < (1ull << 32);
+  auto kern = p.paged ? (off32 ? mla_splitkv_kernel<NW, true, true> : mla_splitkv_kernel<NW, true, false>)
+                      : (off32 ? mla_splitkv_kernel<NW, false, true> : mla_splitkv_kernel<NW, false, false>);
   hipLaunchKernelGGL(kern, dim3(items), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
