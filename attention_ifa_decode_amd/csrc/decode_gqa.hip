@@ -11,16 +11,17 @@
 // (antiquantScale / antiquantOffset, "Parameters").
 //
 // Work decomposition.  One workgroup = 4 waves = one (b, g, head group,
-// split).  The waves take 16-token tiles of the split round robin.  Inside a
-// wave, C = D/16 lanes share one token row (16 channels per lane, loaded as
-// 16-byte chunks so that each load instruction reads whole 128-byte row
-// segments), so a wave step covers 64/C tokens.  q for the GH heads stays in
-// registers.  Per tile: QK^T (packed dot2 for f16/bf16), a C-lane DPP
-// reduction, the tile max over the wave, one rescale of the running
-// (max, sum, acc) if the max grew, then P V in fp32 FMAs.  The next tile's
-// K/V rows are loaded while the current one is computed.  At the end the
-// waves merge their (max, sum, acc) through LDS and the workgroup writes the
-// normalised partial.
+// split); workgroups are dispatched longest sequence first.  The waves take
+// the split's steps round robin.  Inside a wave, C = D/16 lanes share one
+// token row (16 channels per lane, loaded as 16-byte chunks so that each load
+// instruction reads whole 128-byte row segments), so a step covers 64/C
+// tokens.  Each wave streams its steps through a private LDS ring filled by
+// direct HBM -> LDS loads issued STAGES-1 steps ahead.  q for the GH heads
+// stays in registers.  Per step: QK^T (packed dot2 for f16/bf16, fp32 FMA
+// for f32 and int8), a C-lane DPP reduction, a lazy softmax rescale per lane
+// group (the running reference moves only when a score exceeds it by 2^8),
+// then P V in fp32 FMAs.  At the end the waves merge their (max, sum, acc)
+// through LDS and the workgroup writes the normalised partial.
 #include "common.hpp"
 #include "kernels.hpp"
 

@@ -38,10 +38,18 @@ KERNEL_SOURCES = ["attention_ifa_decode_amd/csrc/decode_gqa.hip", "attention_ifa
 
 
 def kernel_source_hash() -> str:
+    """Hash of the split-KV kernel's source with comments and whitespace
+    removed, so that only a change to the code itself invalidates the stored
+    counter readings."""
+    import re
+
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", "", text).encode())
     return h.hexdigest()[:16]
 
 
