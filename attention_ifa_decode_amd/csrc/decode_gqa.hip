@@ -125,7 +125,11 @@ struct GqaShape {
   static constexpr int NCH = ESZ;            // chunks per lane per row
   static constexpr int ROWB = D * ESZ;       // bytes per token row
   static constexpr int STEP_BYTES = 2 * NCH * 1024;  // K and V of one step, whole wave
-  static constexpr int STAGES = kRingBytesPerWave / STEP_BYTES < 2 ? 2 : kRingBytesPerWave / STEP_BYTES;
+  // eight heads per workgroup leave one wave per SIMD (registers), so that
+  // instantiation gets a deeper ring to keep enough loads in flight
+  static constexpr int RING_WAVE = GH == 8 ? 32768 : kRingBytesPerWave;
+  static constexpr int STAGES_FIT = RING_WAVE / STEP_BYTES < 2 ? 2 : RING_WAVE / STEP_BYTES;
+  static constexpr int STAGES = (STAGES_FIT - 1) * 2 * NCH > 63 ? 63 / (2 * NCH) + 1 : STAGES_FIT;
   static constexpr int LOADS = 2 * NCH;      // load instructions per step
   static constexpr int RING_BYTES = 4 * STAGES * STEP_BYTES;
   static constexpr int MERGE_BYTES = 4 * GH * D * 4;
@@ -138,6 +142,12 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   constexpr int C = S::C, TOK = S::TOK, E = S::E, NCH = S::NCH, ROWB = S::ROWB;
   constexpr int STAGES = S::STAGES, LOADS = S::LOADS;
   constexpr bool DOT2 = (KV == kF16 || KV == kBF16);
+  // int8 K: q' = q * K scale is kept as packed fp16 pairs and every K byte
+  // pair becomes the fp16 pair (1024 + byte ^ 0x80) with one byte permute
+  // (exact: 1024 <= value < 2048 has unit spacing), so QK^T runs on packed
+  // fp16 dot products like the f16 path
+  constexpr bool I8DOT = (KV == kI8);
+  constexpr bool PACKQ = DOT2 || I8DOT;
   constexpr float kRescale = 8.f;    // log2 headroom before the running reference moves
   constexpr float kMrefInit = -1e30f;  // finite, so exp2(-inf - mref) is 0, never NaN
   static_assert(D % 16 == 0 && C >= 4 && STAGES >= 2, "shape");
@@ -151,11 +161,15 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   // Work items in dispatch order: consecutive workgroups go round robin to
   // the XCDs, so with the longest-first order every XCD receives an equal
   // mix of long and short items.
-  const int w = blockIdx.x;
-  if (w >= work_items) return;
+  // Head groups of one KV head read the same K/V rows.  Workgroups go round
+  // robin to the 8 XCDs, so the head groups of an item are placed 8 ids
+  // apart: they run on the same XCD at about the same time and the later
+  // reads hit its L2 instead of HBM.
   const int HG = a.group / GH;
-  int rem = w;
-  const int hg = rem % HG; rem /= HG;
+  const int span = 8 * HG;
+  const int hg = (blockIdx.x % span) / 8;
+  int rem = (blockIdx.x / span) * 8 + blockIdx.x % 8;  // item without the head group
+  if (rem >= work_items / HG) return;
   const int split = rem % a.n_split; rem /= a.n_split;
   const int g = rem % a.n_kv; rem /= a.n_kv;
   const int b = a.longest_first ? batch_of_rank(rem, a.seq_lens, a.batch, a.s_cap, sm_len, &sm_pick) : rem;
@@ -232,9 +246,9 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
 
     // ---- q (and the int8 K-side constant) for this lane's 16 channels ----
     // channel of element e: E * ((e / E) * C + c) + e % E
-    float qf[DOT2 ? 1 : GH][DOT2 ? 1 : 16];
-    uint32_t qp[DOT2 ? GH : 1][DOT2 ? 8 : 1];
-    float kconst[GH];  // int8: sum_d q'_d (offset_d - 128), in score units
+    float qf[PACKQ ? 1 : GH][PACKQ ? 1 : 16];
+    uint32_t qp[PACKQ ? GH : 1][PACKQ ? 8 : 1];
+    float kconst[GH];  // int8: sum_d q'_d (offset_d - 1152), with q' as rounded to fp16
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
       const int64_t qrow = ((int64_t)b * a.n_q + h0 + h) * D;
@@ -245,6 +259,12 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
         if constexpr (DOT2) {
           // q has the dtype of K here: repack its raw bits into pairs
           const uint32_t bits = static_cast<const uint16_t*>(a.q)[qrow + d];
+          if (e & 1) qp[h][e >> 1] |= bits << 16; else qp[h][e >> 1] = bits;
+        } else if constexpr (I8DOT) {
+          // x_hat = (x + offset) * scale with x = f - 1152, f = 1024 + (x ^ 0x80)
+          const _Float16 qh = (_Float16)(load_as_f32<QT>(a.q, qrow + d) * a.aq_scale[(int64_t)g * D + d]);
+          part = fmaf((float)qh, a.aq_offset[(int64_t)g * D + d] - 1152.f, part);
+          const uint32_t bits = __builtin_bit_cast(uint16_t, qh);
           if (e & 1) qp[h][e >> 1] |= bits << 16; else qp[h][e >> 1] = bits;
         } else {
           float qv = load_as_f32<QT>(a.q, qrow + d);
@@ -260,7 +280,7 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
 #pragma unroll
     for (int h = 0; h < GH; ++h) {
       settle(kconst[h]);
-      if constexpr (DOT2) {
+      if constexpr (PACKQ) {
 #pragma unroll
         for (int p = 0; p < 8; ++p) settle(qp[h][p]);
       } else {
@@ -279,6 +299,15 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
       for (int i = 0; i < NCH; ++i) kr[i] = *reinterpret_cast<const u32x4*>(src + 1024 * i);
 
       const bool valid = start + TOK * st + t < end;
+      uint32_t kf16[I8DOT ? 8 : 1];  // int8 K as fp16 pairs (1024 + biased byte)
+      if constexpr (I8DOT) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t bw = word(kr[0], w) ^ 0x80808080u;
+          kf16[2 * w] = __builtin_amdgcn_perm(0x64646464u, bw, 0x04010400u);
+          kf16[2 * w + 1] = __builtin_amdgcn_perm(0x64646464u, bw, 0x04030402u);
+        }
+      }
       float s[GH];
       bool need = false;
 #pragma unroll
@@ -294,6 +323,11 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
           for (int p = 0; p < 8; ++p)
             part = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qp[h][p]),
                                           __builtin_bit_cast(half2_t, word(kr[p / 4], p % 4)), part, false);
+        } else if constexpr (I8DOT) {
+#pragma unroll
+          for (int p = 0; p < 8; ++p)
+            part = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qp[h][p]), __builtin_bit_cast(half2_t, kf16[p]),
+                                          part, false);
         } else {
 #pragma unroll
           for (int e = 0; e < 16; ++e) part = fmaf(qf[h][e], elem_f32<KV>(kr, e), part);
@@ -397,7 +431,9 @@ template <int QT, int KV, int D, int GH>
 hipError_t launch_typed(const GqaLaunch& p, hipStream_t stream) {
   const int items = p.batch * p.n_kv * (p.group / GH) * p.n_split;
   if (items == 0) return hipSuccess;
-  const int padded = items;
+  // head-group interleave (see the kernel): items without the head group,
+  // rounded up to a multiple of 8, times the head groups
+  const int padded = (items / (p.group / GH) + 7) / 8 * 8 * (p.group / GH);
   if (p.paged)
     hipLaunchKernelGGL((gqa_splitkv_kernel<QT, KV, D, GH, true>), dim3(padded), dim3(256), 0, stream, p, items);
   else
@@ -431,6 +467,8 @@ hipError_t launch_d(const GqaLaunch& p, hipStream_t stream) {
 
 int gqa_max_heads_per_wg(int kv_dtype, int head_dim) {
   (void)head_dim;
+  // int8 and f32 stop at 4: with 8 the int8 kernel drops to one wave per SIMD
+  // and runs slower than two workgroups of 4 heads that share K/V through L2
   return (kv_dtype == kF16 || kv_dtype == kBF16) ? 8 : 4;
 }
 
