@@ -123,3 +123,17 @@ def test_c5_full_size_sampled_rows():
     rows = _sampled_rows(w, 8, 5)
     ref_out, ref_lse = oracle.decode_workload(w, rows=rows)
     _compare(w, out, lse, ref_out, ref_lse, rows=rows)
+
+
+def test_mla_wide_offsets_path():
+    """A pool that the call declares larger than 4 GiB takes the 64-bit
+    addressing path; every block-table entry still points into the real
+    (small) pool, so the result must not change."""
+    w = _mla(lengths=[260, 97], seed=58)
+    wg = w.to("cuda")
+    call = ifa.call_for_workload(wg, num_splits=2)
+    call.args.num_blocks = 1 << 22  # 4M blocks x 128 rows x 1152 bytes > 4 GiB
+    out, lse = call.run()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.decode_workload(w)
+    _compare(w, out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse)
