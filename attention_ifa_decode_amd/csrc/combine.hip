@@ -11,8 +11,9 @@
 // attn_out 0, max sink, sum 1, and writes lse = M + ln(sum) (the softmaxLse
 // output of the FusedInferAttentionScore blog).
 //
-// Both kernels are HBM-bound elementwise passes: one wave per row, lanes
-// stride over the head dimension.
+// Both kernels are memory-bound passes with one wave per row.  The combine
+// issues every load of a row (partials, statistics, length) before waiting,
+// so a row costs one memory round trip whatever its split count.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,45 +21,146 @@ namespace ifa {
 namespace {
 
 constexpr int kRowsPerBlock = 4;
+constexpr int kMaxSplitsPerRow = 256;
 
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f32<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_f32<kDppRowHalfMirror>(x));
+  x = fmaxf(x, dpp_f32<kDppRowMirror>(x));
+  return xor32_max(xor16_max(x));
+}
+
+__device__ __forceinline__ float wave_sum(float x) { return xor32_sum(xor16_sum(group_sum<16>(x))); }
+
+// Four consecutive outputs; one vector store when the output buffer is
+// 16-byte aligned (then every row start is, VD being a multiple of 64).
 template <int OT>
+__device__ __forceinline__ void store4(void* out, int64_t idx, const float4& v) {
+  if ((reinterpret_cast<uintptr_t>(out) & 15) != 0) {
+    store_from_f32<OT>(out, idx, v.x), store_from_f32<OT>(out, idx + 1, v.y);
+    store_from_f32<OT>(out, idx + 2, v.z), store_from_f32<OT>(out, idx + 3, v.w);
+  } else if constexpr (OT == kF32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + idx) = v;
+  } else {
+    uint16_t h[4];
+    if constexpr (OT == kF16) {
+      const _Float16 f[4] = {(_Float16)v.x, (_Float16)v.y, (_Float16)v.z, (_Float16)v.w};
+      __builtin_memcpy(h, f, sizeof(h));
+    } else {
+      h[0] = f32_to_bf16_bits(v.x), h[1] = f32_to_bf16_bits(v.y);
+      h[2] = f32_to_bf16_bits(v.z), h[3] = f32_to_bf16_bits(v.w);
+    }
+    uint2 p;
+    p.x = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+    p.y = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + idx) = p;
+  }
+}
+
+// One wave per (batch, head) row.  A row's partial outputs are n_split
+// contiguous vectors of VD floats; lanes read them as float4 columns, so a
+// load instruction covers PARTS = 64 / (VD/4) splits (4 at VD 64, 2 at 128,
+// 1 at 512, where each lane holds two columns).  All loads of a batch of
+// splits are issued before the statistics are reduced, so a row costs one
+// memory round trip rather than one per split.
+template <int OT, int VD>
 __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-  if (row >= (int64_t)a.batch * a.n_q) return;
-  const int b = (int)(row / a.n_q), h = (int)(row % a.n_q);
-  int64_t L = a.seq_lens[b];
-  L = L < 0 ? 0 : (L > a.s_cap ? a.s_cap : L);
-  const int64_t per = split_chunk(L, a.n_split);
-  const int nvalid = L == 0 ? 0 : (int)((L + per - 1) / per);
+  constexpr int kQuads = VD / 4;
+  constexpr int kLanesPerSplit = kQuads < 64 ? kQuads : 64;
+  constexpr int kParts = 64 / kLanesPerSplit;
+  constexpr int kCols = kQuads / kLanesPerSplit;
+  constexpr int kSteps = kCols == 2 ? 16 : 8;  // loads in flight per lane: 32 at VD 512, 8 below
+  constexpr int kBatch = kSteps * kParts;                     // splits per batch of loads
+  __shared__ float sm_m[kRowsPerBlock][kMaxSplitsPerRow];
+  __shared__ float sm_w[kRowsPerBlock][kMaxSplitsPerRow];
 
-  const float* m = a.ws_m + row * a.n_split;
-  const float* l = a.ws_l + row * a.n_split;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerBlock + wave;  // rows < 2^31 (checked at launch)
+  if (row >= a.batch * a.n_q) return;  // uniform per wave; no block barrier below
+  const int b = row / a.n_q, h = row - b * a.n_q;
+  const int part = lane / kLanesPerSplit, col = lane % kLanesPerSplit;
+
+  // Every load of the row is issued before the length arrives: partial
+  // vectors and statistics of all n_split slots (in bounds of the workspace
+  // row), of which only the first nvalid were written by this call.
+  const float4* o = reinterpret_cast<const float4*>(a.ws_o + (int64_t)row * a.n_split * VD);
+  float4 v[kSteps][kCols];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int j = 0; j < kSteps; ++j) {
+      const int s = s0 + j * kParts + part;
+#pragma unroll
+      for (int c = 0; c < kCols; ++c)
+        v[j][c] = s < a.n_split ? o[s * kQuads + c * kLanesPerSplit + col] : float4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load_batch(0);
+  const float* m = a.ws_m + (int64_t)row * a.n_split;
+  const float* l = a.ws_l + (int64_t)row * a.n_split;
+  float m0 = 0.f, l0 = 0.f;
+  if (lane < a.n_split) m0 = m[lane], l0 = l[lane];
   const float sink = a.sink ? a.sink[h] : kNegInf;
-  float M = sink;
-  for (int i = 0; i < nvalid; ++i) M = fmaxf(M, m[i]);
-  float tot = (a.sink && M != kNegInf) ? fast_exp2((sink - M) * kLog2e) : 0.f;
 
-  const float* o = a.ws_o + row * a.n_split * (int64_t)a.v_dim;
-  const int64_t orow = row * a.v_dim;
-  constexpr int kMaxPerLane = 8;  // v_dim <= 512
-  float acc[kMaxPerLane];
+  int64_t L64 = a.seq_lens[b];
+  const int L = (int)(L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64));
+  const int per = ((L + a.n_split - 1) / a.n_split + 15) & ~15;  // split_chunk, in 32 bits
+  const int nvalid = L == 0 ? 0 : (L + per - 1) / per;
+
+  // statistics: lane s holds split s (in chunks of 64)
+  float M = sink;
+  for (int c0 = 0; c0 < nvalid; c0 += 64) {
+    const int s = c0 + lane;
+    float mv = kNegInf, lv = 0.f;
+    if (c0 == 0) {
+      if (s < nvalid) mv = m0, lv = l0;
+    } else if (s < nvalid) {
+      mv = m[s], lv = l[s];
+    }
+    sm_m[wave][s] = mv;
+    sm_w[wave][s] = lv;
+    M = fmaxf(M, wave_max(mv));
+  }
+  float part_tot = 0.f;
+  for (int c0 = 0; c0 < nvalid; c0 += 64) {
+    const int s = c0 + lane;
+    const float w = s < nvalid ? sm_w[wave][s] * fast_exp2((sm_m[wave][s] - M) * kLog2e) : 0.f;
+    sm_w[wave][s] = w;
+    part_tot += w;
+  }
+  float tot = wave_sum(part_tot);
+  if (a.sink && M != kNegInf) tot += fast_exp2((sink - M) * kLog2e);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+
+  float4 acc[kCols];
 #pragma unroll
-  for (int k = 0; k < kMaxPerLane; ++k) acc[k] = 0.f;
-  for (int i = 0; i < nvalid; ++i) {
-    const float wgt = l[i] * fast_exp2((m[i] - M) * kLog2e);
-    tot += wgt;
+  for (int c = 0; c < kCols; ++c) acc[c] = float4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nvalid; s0 += kBatch) {
+    if (s0 > 0) load_batch(s0);
 #pragma unroll
-    for (int k = 0; k < kMaxPerLane; ++k) {
-      const int d = lane + 64 * k;
-      if (d < a.v_dim) acc[k] = fmaf(wgt, o[(int64_t)i * a.v_dim + d], acc[k]);
+    for (int j = 0; j < kSteps; ++j) {
+      const int s = s0 + j * kParts + part;
+      if (s < nvalid) {  // slots past nvalid hold stale or unwritten values
+        const float w = sm_w[wave][s];
+#pragma unroll
+        for (int c = 0; c < kCols; ++c) {
+          acc[c].x = fmaf(w, v[j][c].x, acc[c].x);
+          acc[c].y = fmaf(w, v[j][c].y, acc[c].y);
+          acc[c].z = fmaf(w, v[j][c].z, acc[c].z);
+          acc[c].w = fmaf(w, v[j][c].w, acc[c].w);
+        }
+      }
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
-  for (int k = 0; k < kMaxPerLane; ++k) {
-    const int d = lane + 64 * k;
-    if (d < a.v_dim) store_from_f32<OT>(a.out, orow + d, acc[k] * inv);
+  for (int c = 0; c < kCols; ++c) {
+    float4 r = acc[c];
+    if constexpr (kParts == 4) r.x = xor16_sum(r.x), r.y = xor16_sum(r.y), r.z = xor16_sum(r.z), r.w = xor16_sum(r.w);
+    if constexpr (kParts >= 2) r.x = xor32_sum(r.x), r.y = xor32_sum(r.y), r.z = xor32_sum(r.z), r.w = xor32_sum(r.w);
+    r.x *= inv, r.y *= inv, r.z *= inv, r.w *= inv;
+    if (part == 0) store4<OT>(a.out, (int64_t)row * VD + (c * kLanesPerSplit + col) * 4, r);
   }
   if (a.lse && lane == 0) a.lse[row] = tot > 0.f ? M + __logf(tot) : kNegInf;
 }
@@ -95,17 +197,29 @@ __global__ void __launch_bounds__(256) update_kernel(const UpdateLaunch a) {
   }
 }
 
+template <int VD>
+hipError_t launch_combine_vd(const CombineLaunch& p, dim3 grid, hipStream_t stream) {
+  switch (p.out_dtype) {
+    case kF32: hipLaunchKernelGGL((combine_kernel<kF32, VD>), grid, dim3(256), 0, stream, p); break;
+    case kF16: hipLaunchKernelGGL((combine_kernel<kF16, VD>), grid, dim3(256), 0, stream, p); break;
+    case kBF16: hipLaunchKernelGGL((combine_kernel<kBF16, VD>), grid, dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(const CombineLaunch& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.batch * p.n_q;
   if (rows == 0) return hipSuccess;
-  if (p.v_dim > 512) return hipErrorInvalidValue;
+  if (rows >= (int64_t)1 << 31) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
-  switch (p.out_dtype) {
-    case kF32: hipLaunchKernelGGL(combine_kernel<kF32>, grid, dim3(256), 0, stream, p); break;
-    case kF16: hipLaunchKernelGGL(combine_kernel<kF16>, grid, dim3(256), 0, stream, p); break;
-    case kBF16: hipLaunchKernelGGL(combine_kernel<kBF16>, grid, dim3(256), 0, stream, p); break;
+  if (p.n_split < 1 || p.n_split > kMaxSplitsPerRow) return hipErrorInvalidValue;
+  switch (p.v_dim) {
+    case 64: return launch_combine_vd<64>(p, grid, stream);
+    case 128: return launch_combine_vd<128>(p, grid, stream);
+    case 512: return launch_combine_vd<512>(p, grid, stream);
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -132,6 +132,48 @@ def test_split_counts(splits):
     _full_check(w, splits)
 
 
+@pytest.mark.parametrize("d,splits", [(64, 100), (64, 256), (128, 70), (128, 256)])
+def test_many_splits(d, splits):
+    """More than 64 non-empty splits in a row (the merge reduces statistics in
+    chunks of 64 and reads partials in batches); short rows leave most of
+    their splits empty."""
+    w = make_workload(batch=4, n_q=8, n_kv=2, qk_dim=d, kv_dtype="f16", layout="bnsd",
+                      lengths=[4096, 2001, 5, 0], s_cap=4096, seed=19)
+    _full_check(w, splits)
+
+
+def test_stale_workspace_slots_ignored():
+    """Workspace slots of empty splits are never written; NaN left in them by
+    earlier use must not reach the output."""
+    w = make_workload(batch=3, n_q=16, n_kv=4, qk_dim=128, kv_dtype="bf16", layout="paged", block_size=16,
+                      lengths=[700, 17, 1], seed=20)
+    wg = w.to("cuda")
+    call = ifa.call_for_workload(wg, num_splits=16)
+    call.workspace.view(torch.float32).fill_(float("nan"))
+    out, lse = call.run()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.decode_workload(w)
+    _compare(w, out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse)
+
+
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_unaligned_output_buffer(out_dtype):
+    """attention_out one element past a 16-byte boundary (element-wise stores)."""
+    w = make_workload(batch=2, n_q=8, n_kv=2, qk_dim=128, kv_dtype="bf16", out_dtype=out_dtype, layout="paged",
+                      block_size=64, lengths=[300, 45], seed=21)
+    wg = w.to("cuda")
+    n = w.batch * w.n_q * w.v_dim
+    buf = torch.full((n + 1,), float("nan"), dtype=wg.out_dtype, device="cuda")
+    out_view = buf[1:].view(w.batch, w.n_q, w.v_dim)
+    call = ifa.call_for_workload(wg, num_splits=3, out=out_view)
+    out, lse = call.run()
+    torch.cuda.synchronize()
+    assert out.data_ptr() % 16 != 0
+    assert torch.isnan(buf[0]).item()
+    ref_out, ref_lse = oracle.decode_workload(w)
+    _compare(w, out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse)
+
+
 @pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
 def test_gqa_group_sizes(group):
     w = make_workload(batch=2, n_q=8 * group if group < 16 else 32, n_kv=8 if group < 16 else 2,

@@ -44,7 +44,7 @@ def test_mla_head_counts(n_q):
     _full_check(_mla(n_q=n_q, seed=51 + n_q), 2)
 
 
-@pytest.mark.parametrize("splits", [1, 3, 16])
+@pytest.mark.parametrize("splits", [1, 3, 16, 40])
 def test_mla_split_counts(splits):
     _full_check(_mla(lengths=[700, 33, 129], batch=3, seed=52), splits)
 
