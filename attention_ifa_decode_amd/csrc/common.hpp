@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.hpp"
+
 namespace ifa {
 
 enum DType : int { kF32 = 0, kF16 = 1, kBF16 = 2, kI8 = 3 };
@@ -163,37 +165,75 @@ __device__ __forceinline__ int xcd_remap(int id, int padded) {
   return (id % kNumXcd) * per + id / kNumXcd;
 }
 
-// Batch that comes `rank`-th when sequences are ordered by descending clamped
-// length (ties by batch index).  Every thread of the workgroup must call it;
-// `sm_len` holds `batch` ints rounded up to a multiple of 4.  Dispatching long
-// sequences first keeps the last workgroups short (longest-processing-time
+// The batch that comes `rank`-th when sequences are ordered by descending
+// clamped length (ties by batch index), and that length.  Dispatching long
+// sequences first keeps the last workgroups short (longest-processing-time-
 // first list scheduling).
-__device__ inline int batch_of_rank(int rank, const int64_t* lens, int batch, int64_t cap, int* sm_len,
-                                    int* sm_pick) {
-  const int padded = (batch + 3) & ~3;
-  for (int i = threadIdx.x; i < padded; i += blockDim.x) {
-    int64_t L = i < batch ? lens[i] : -1;  // padding sorts last and never matches
-    L = L < -1 ? 0 : (L > cap ? cap : L);
-    sm_len[i] = (int)L;
-  }
-  __syncthreads();
-  const int4* l4 = reinterpret_cast<const int4*>(sm_len);
-  for (int i = threadIdx.x; i < batch; i += blockDim.x) {
-    const int li = sm_len[i];
-    int r = 0;
-#pragma unroll 8
-    for (int j4 = 0; j4 < padded / 4; ++j4) {
-      const int4 q = l4[j4];
-      const int j = 4 * j4;
-      r += (q.x > li) | ((q.x == li) & (j < i));
-      r += (q.y > li) | ((q.y == li) & (j + 1 < i));
-      r += (q.z > li) | ((q.z == li) & (j + 2 < i));
-      r += (q.w > li) | ((q.w == li) & (j + 3 < i));
+//
+// Wave-level, with no barrier: every wave computes it alone from one vector
+// load of the lengths (lane i holds sequence i; chunks of 64 for larger
+// batches).  Each sequence gets a unique 32-bit key, (min(len, 2^23 - 1) + 1)
+// * 256 + 255 - i, so its rank is the number of larger keys; the wave writes
+// its keys to `keys` (this wave's own LDS, kLongestFirstMaxBatch entries) and
+// every lane counts against all of them through broadcast LDS reads, all in
+// vector registers.  A ballot then picks the lane whose rank matches.
+// Lengths beyond 2^23 tie in the key and are ordered by index.  The result is
+// wave-uniform.  Requires batch <= kLongestFirstMaxBatch and
+// 0 <= rank < batch.
+struct BatchPick {
+  int b, len;
+};
+
+__device__ inline BatchPick batch_of_rank(int rank, const int64_t* lens, int batch, int64_t cap, uint32_t* keys) {
+  constexpr int kChunks = kLongestFirstMaxBatch / 64;
+  static_assert(kLongestFirstMaxBatch <= 256, "8-bit index in the key");
+  const int lane = threadIdx.x & 63;
+  const int nc = (batch + 63) >> 6;
+  int lv[kChunks];
+  uint32_t key[kChunks];  // 0 for padding: below every real key, never picked
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int i = c * 64 + lane;
+    int64_t x = -1;
+    if (c < nc && i < batch) {
+      x = lens[i];
+      x = x < 0 ? 0 : (x > cap ? cap : x);
     }
-    if (r == rank) *sm_pick = i;
+    lv[c] = (int)x;
+    key[c] = x < 0 ? 0u : (((uint32_t)(x < (1 << 23) - 1 ? x : (1 << 23) - 1) + 1u) << 8) | (uint32_t)(255 - i);
+    if (c < nc) keys[i] = key[c];
   }
-  __syncthreads();
-  return *sm_pick;
+  // LDS operations of one wave complete in order: the reads below see every
+  // lane's write
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const uint4* k4 = reinterpret_cast<const uint4*>(keys);
+  int r[kChunks] = {};
+  if (nc == 1) {
+#pragma unroll 4
+    for (int j = 0; j < 16; ++j) {
+      const uint4 q = k4[j];
+      r[0] += (int)(q.x > key[0]) + (int)(q.y > key[0]) + (int)(q.z > key[0]) + (int)(q.w > key[0]);
+    }
+  } else {
+    for (int j = 0; j < nc * 16; ++j) {
+      const uint4 q = k4[j];
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c)
+        r[c] += (int)(q.x > key[c]) + (int)(q.y > key[c]) + (int)(q.z > key[c]) + (int)(q.w > key[c]);
+    }
+  }
+  BatchPick p{rank, 0};  // replaced below: the ranks of the real lanes are a permutation of 0..batch-1
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(key[c] != 0u && r[c] == rank);
+    if (m) {
+      const int k = __builtin_ctzll(m);
+      p.b = c * 64 + k;
+      p.len = __builtin_amdgcn_readlane(lv[c], k);
+    }
+  }
+  return p;
 }
 
 }  // namespace ifa

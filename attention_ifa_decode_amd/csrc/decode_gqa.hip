@@ -86,6 +86,23 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait for this wave's LDS reads (and scalar loads) to complete.
+__device__ __forceinline__ void wait_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Wait until at most n * LOADS vector-memory operations are in flight, for a
+// run-time n in [0, NMAX] (the count is an immediate of s_waitcnt).
+template <int NMAX, int LOADS>
+__device__ __forceinline__ void wait_vmem_steps(int n) {
+  if constexpr (NMAX <= 0) {
+    wait_vmem<0>();
+  } else {
+    if (n >= NMAX) wait_vmem<NMAX * LOADS>();
+    else wait_vmem_steps<NMAX - 1, LOADS>(n);
+  }
+}
+
 // Make the compiler complete the loads behind `x` here: an empty asm that
 // reads the register forces the wait before this point instead of at the
 // first use inside the streaming loop, where it would also drain the ring.
@@ -134,6 +151,7 @@ struct GqaShape {
   static constexpr int RING_BYTES = 4 * STAGES * STEP_BYTES;
   static constexpr int MERGE_BYTES = 4 * GH * D * 4;
   static constexpr int SMEM = RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES;
+  static_assert(STAGES * STEP_BYTES >= kLongestFirstMaxBatch * 4, "rank keys fit a wave's ring");
 };
 
 template <int QT, int KV, int D, int GH, bool PAGED>
@@ -152,8 +170,6 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   constexpr float kMrefInit = -1e30f;  // finite, so exp2(-inf - mref) is 0, never NaN
   static_assert(D % 16 == 0 && C >= 4 && STAGES >= 2, "shape");
 
-  __shared__ __attribute__((aligned(16))) int sm_len[kLongestFirstMaxBatch];
-  __shared__ int sm_pick;
   __shared__ __attribute__((aligned(16))) char smem[S::SMEM];
   __shared__ float sm_m[4][GH];
   __shared__ float sm_l[4][GH];
@@ -172,11 +188,17 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   if (rem >= work_items / HG) return;
   const int split = rem % a.n_split; rem /= a.n_split;
   const int g = rem % a.n_kv; rem /= a.n_kv;
-  const int b = a.longest_first ? batch_of_rank(rem, a.seq_lens, a.batch, a.s_cap, sm_len, &sm_pick) : rem;
-
-  int64_t L64 = a.seq_lens[b];
-  L64 = L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64);
-  const int L = (int)L64;
+  int b = rem, L;
+  if (a.longest_first) {
+    // the keys use this wave's part of the ring, which no load has reached yet
+    uint32_t* keys = reinterpret_cast<uint32_t*>(smem + (threadIdx.x >> 6) * (STAGES * S::STEP_BYTES));
+    const BatchPick pick = batch_of_rank(rem, a.seq_lens, a.batch, a.s_cap, keys);
+    b = pick.b;
+    L = pick.len;
+  } else {
+    const int64_t L64 = a.seq_lens[b];
+    L = (int)(L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64));
+  }
   const int per = (int)split_chunk(L, a.n_split);
   const int start = split * per;
   const int end = min(L, start + per);
@@ -193,13 +215,25 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   char* ring = smem + wave * (STAGES * S::STEP_BYTES);  // this wave's stages: [K chunks | V chunks]
   const uint32_t ring_lds = lds_addr(ring);
 
+  // Block-table slice of the split: lane k holds the id of the split's k-th
+  // cache block (one vector load; the loop reads it with v_readlane, so it
+  // issues no scalar loads, whose waits would also hold back the LDS reads).
+  // A split spanning more than 64 blocks reads the rest with scalar loads.
+  const uint32_t bi0 = PAGED ? fast_div((uint32_t)start, a.bs_magic, a.bs_shift) : 0;
+  int tbl = 0;
+  if constexpr (PAGED) {
+    if ((int)bi0 + lane < a.max_blocks) tbl = a.block_table[(int64_t)b * a.max_blocks + bi0 + lane];
+    settle(tbl);  // one wait here, before any ring load is queued
+  }
+
   // First cache row of step `st`: TOK tokens that lie inside one block
   // (splits start on 16-token boundaries, the block size is a multiple of 16).
   auto step_row = [&](int st) -> uint32_t {
     const int j0 = start + TOK * st;
     if constexpr (PAGED) {
       const uint32_t bi = fast_div((uint32_t)j0, a.bs_magic, a.bs_shift);
-      int blk = ld_uniform(a.block_table, (int64_t)b * a.max_blocks + bi);
+      const uint32_t k = bi - bi0;
+      int blk = k < 64 ? __builtin_amdgcn_readlane(tbl, k) : ld_uniform(a.block_table, (int64_t)b * a.max_blocks + bi);
       blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
       return ((uint32_t)blk * (uint32_t)a.n_kv + (uint32_t)g) * (uint32_t)a.block_size + (uint32_t)j0 -
              bi * (uint32_t)a.block_size;
@@ -208,12 +242,10 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
     }
   };
 
-  // Queue the direct-to-LDS loads of step `st` into ring stage `slot`.  Steps
-  // past the end re-read the last one, so every iteration queues the same
-  // number of loads (those reads hit L2).  Lanes past the split's end read its
-  // last valid row: finite data that the softmax weights with exactly 0.
+  // Queue the direct-to-LDS loads of step `st` (< nsteps) into ring stage
+  // `slot`.  Lanes past the split's end read its last valid row: finite data
+  // that the softmax weights with exactly 0.
   auto issue = [&](int st, int slot) {
-    st = st < nsteps ? st : nsteps - 1;
     const uint32_t row0 = step_row(st);
     const int r = min(t, end - 1 - (start + TOK * st));
     const uint32_t off = (uint32_t)r * ROWB + 16u * c;
@@ -240,9 +272,10 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   }
 
   if (wave < nsteps) {
-    // prologue: STAGES-1 steps in flight
+    // prologue: up to STAGES of this wave's steps in flight, one per stage
 #pragma unroll
-    for (int k = 0; k < STAGES - 1; ++k) issue(wave + 4 * k, k);
+    for (int k = 0; k < STAGES; ++k)
+      if (wave + 4 * k < nsteps) issue(wave + 4 * k, k);
 
     // ---- q (and the int8 K-side constant) for this lane's 16 channels ----
     // channel of element e: E * ((e / E) * C + c) + e % E
@@ -291,12 +324,25 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
 
     int slot = 0;
     for (int st = wave; st < nsteps; st += 4) {
-      issue(st + 4 * (STAGES - 1), slot == 0 ? STAGES - 1 : slot - 1);
-      wait_vmem<(STAGES - 1) * LOADS>();
+      // wait for step st; the loads of this wave's later steps already queued
+      // (at most STAGES-1 of them) stay in flight
+      const int later = (nsteps - 1 - st) / 4;
+      if (later >= STAGES - 1) wait_vmem<(STAGES - 1) * LOADS>();
+      else wait_vmem_steps<STAGES - 2, LOADS>(later);
+      // Copy the step out of its stage and queue the step STAGES ahead into
+      // it at once: the stage is free again after the LDS reads rather than
+      // after the whole step's arithmetic, so the full ring stays in flight.
       const char* src = ring + slot * S::STEP_BYTES + 16 * lane;
-      u32x4 kr[NCH];
+      u32x4 kr[NCH], vr[NCH];
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) kr[i] = *reinterpret_cast<const u32x4*>(src + 1024 * i);
+      for (int i = 0; i < NCH; ++i) {
+        kr[i] = *reinterpret_cast<const u32x4*>(src + 1024 * i);
+        vr[i] = *reinterpret_cast<const u32x4*>(src + 1024 * (NCH + i));
+      }
+      if (st + 4 * STAGES < nsteps) {
+        wait_lds();  // the direct loads below overwrite this stage
+        issue(st + 4 * STAGES, slot);
+      }
 
       const bool valid = start + TOK * st + t < end;
       uint32_t kf16[I8DOT ? 8 : 1];  // int8 K as fp16 pairs (1024 + biased byte)
@@ -349,9 +395,6 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
           mref[h] = mnew;
         }
       }
-      u32x4 vr[NCH];
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) vr[i] = *reinterpret_cast<const u32x4*>(src + 1024 * (NCH + i));
       float p[GH];
 #pragma unroll
       for (int h = 0; h < GH; ++h) {
@@ -367,7 +410,7 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
       slot = slot == STAGES - 1 ? 0 : slot + 1;
     }
   }
-  wait_vmem<0>();  // the ring is reused below; no load may still write it
+  // every queued load has been waited for: the ring is free for the merge
 
   // ---- merge the lane groups of the wave: common max, rescale, sum ----
   float mw[GH];

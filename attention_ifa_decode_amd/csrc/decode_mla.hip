@@ -128,8 +128,7 @@ mla_splitkv_kernel(const MlaLaunch a) {
   constexpr int STAGES = S::STAGES, LOADS_W = S::LOADS_W;
   __shared__ __attribute__((aligned(16))) char ring[STAGES * kTileBytes];
   __shared__ int sm_blk[kMlaMaxTableSlice];
-  __shared__ __attribute__((aligned(16))) int sm_len[kLongestFirstMaxBatch];
-  __shared__ int sm_pick;
+  __shared__ __attribute__((aligned(16))) uint32_t sm_keys[NW][kLongestFirstMaxBatch];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -142,10 +141,15 @@ mla_splitkv_kernel(const MlaLaunch a) {
   id /= HGM;
   const int split = id % a.n_split;
   const int rank = id / a.n_split;
-  const int b = a.longest_first ? batch_of_rank(rank, a.seq_lens, a.batch, a.s_cap, sm_len, &sm_pick) : rank;
-  int64_t L64 = a.seq_lens[b];
-  L64 = L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64);
-  const int L = (int)L64;
+  int b = rank, L;
+  if (a.longest_first) {
+    const BatchPick pick = batch_of_rank(rank, a.seq_lens, a.batch, a.s_cap, sm_keys[wave]);
+    b = pick.b;
+    L = pick.len;
+  } else {
+    const int64_t L64 = a.seq_lens[b];
+    L = (int)(L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64));
+  }
   const int per = (int)split_chunk(L, a.n_split);
   const int start = split * per;
   const int end = min(L, start + per);
