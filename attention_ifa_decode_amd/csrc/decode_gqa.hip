@@ -116,14 +116,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Load through the constant address space: with a wave-uniform index this
-// becomes a scalar load (s_load), which is tracked by lgkmcnt and so never
-// waits behind the vector loads in flight.
-template <typename T>
-__device__ __forceinline__ T ld_uniform(const T* p, int64_t i) {
-  return ((const __attribute__((address_space(4))) T*)p)[i];
-}
-
 // Bytes of the per-wave LDS ring that K/V steps stream through.
 #ifndef IFA_GQA_NT_LOADS
 #define IFA_GQA_NT_LOADS 1
@@ -216,14 +208,15 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   const uint32_t ring_lds = lds_addr(ring);
 
   // Block-table slice of the split: lane k holds the id of the split's k-th
-  // cache block (one vector load; the loop reads it with v_readlane, so it
-  // issues no scalar loads, whose waits would also hold back the LDS reads).
-  // A split spanning more than 64 blocks reads the rest with scalar loads.
+  // cache block, fetched once through scalar loads (which do not queue behind
+  // the CU's ring loads); the loop reads it with v_readlane, so it issues no
+  // scalar loads, whose waits would also hold back the LDS reads.  A split
+  // spanning more than 64 blocks reads the rest with scalar loads.
   const uint32_t bi0 = PAGED ? fast_div((uint32_t)start, a.bs_magic, a.bs_shift) : 0;
   int tbl = 0;
   if constexpr (PAGED) {
-    if ((int)bi0 + lane < a.max_blocks) tbl = a.block_table[(int64_t)b * a.max_blocks + bi0 + lane];
-    settle(tbl);  // one wait here, before any ring load is queued
+    const int nblk = (int)fast_div((uint32_t)(end - 1), a.bs_magic, a.bs_shift) - (int)bi0 + 1;  // in the row
+    tbl = lanes_from_scalar_loads(a.block_table + (int64_t)b * a.max_blocks + bi0, nblk < 64 ? nblk : 64, 0);
   }
 
   // First cache row of step `st`: TOK tokens that lie inside one block
