@@ -315,92 +315,193 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
       }
     }
 
-    int slot = 0;
-    for (int st = wave; st < nsteps; st += 4) {
-      // wait for step st; the loads of this wave's later steps already queued
-      // (at most STAGES-1 of them) stay in flight
-      const int later = (nsteps - 1 - st) / 4;
-      if (later >= STAGES - 1) wait_vmem<(STAGES - 1) * LOADS>();
-      else wait_vmem_steps<STAGES - 2, LOADS>(later);
-      // Copy the step out of its stage and queue the step STAGES ahead into
-      // it at once: the stage is free again after the LDS reads rather than
-      // after the whole step's arithmetic, so the full ring stays in flight.
-      const char* src = ring + slot * S::STEP_BYTES + 16 * lane;
-      u32x4 kr[NCH], vr[NCH];
-#pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        kr[i] = *reinterpret_cast<const u32x4*>(src + 1024 * i);
-        vr[i] = *reinterpret_cast<const u32x4*>(src + 1024 * (NCH + i));
-      }
-      if (st + 4 * STAGES < nsteps) {
-        wait_lds();  // the direct loads below overwrite this stage
-        issue(st + 4 * STAGES, slot);
-      }
+    if constexpr (I8DOT) {
+      // int8: two of this wave's steps per iteration, the lane's token of
+      // each.  V becomes fp16 pairs (1024 + biased byte of step j, of step
+      // j+1) per channel, so P V is one v_dot2 per channel and head on the
+      // pair of softmax weights rounded to fp16.  The row sum takes the same
+      // rounded weights, so the 1024 bias divides out exactly (the epilogue
+      // removes 1024 + 128 with the V offset).
+      int slot = 0;
+      for (int st = wave; st < nsteps; st += 8) {
+        const bool two = st + 4 < nsteps;
+        // wait for both steps; the loads of this wave's steps queued after
+        // the second one (at most STAGES-2 of them: two stages are refilled
+        // per iteration) stay in flight
+        const int later = (nsteps - 1 - st) / 4 - (two ? 1 : 0);
+        wait_vmem_steps<STAGES - 2, LOADS>(later < STAGES - 2 ? later : STAGES - 2);
+        const int slot1 = two ? (slot + 1 == STAGES ? 0 : slot + 1) : slot;
+        const char* src0 = ring + slot * S::STEP_BYTES + 16 * lane;
+        const char* src1 = ring + slot1 * S::STEP_BYTES + 16 * lane;
+        const u32x4 kr0 = *reinterpret_cast<const u32x4*>(src0);
+        const u32x4 vr0 = *reinterpret_cast<const u32x4*>(src0 + 1024);
+        const u32x4 kr1 = *reinterpret_cast<const u32x4*>(src1);
+        const u32x4 vr1 = *reinterpret_cast<const u32x4*>(src1 + 1024);
+        if (st + 4 * STAGES < nsteps) {
+          wait_lds();  // the direct loads below overwrite these stages
+          issue(st + 4 * STAGES, slot);
+          if (st + 4 + 4 * STAGES < nsteps) issue(st + 4 + 4 * STAGES, slot1);
+        }
 
-      const bool valid = start + TOK * st + t < end;
-      uint32_t kf16[I8DOT ? 8 : 1];  // int8 K as fp16 pairs (1024 + biased byte)
-      if constexpr (I8DOT) {
+        const bool valid0 = start + TOK * st + t < end;
+        const bool valid1 = two && start + TOK * (st + 4) + t < end;
+        uint32_t k0[8], k1[8];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const uint32_t bw = word(kr[0], w) ^ 0x80808080u;
-          kf16[2 * w] = __builtin_amdgcn_perm(0x64646464u, bw, 0x04010400u);
-          kf16[2 * w + 1] = __builtin_amdgcn_perm(0x64646464u, bw, 0x04030402u);
+          const uint32_t b0 = word(kr0, w) ^ 0x80808080u, b1 = word(kr1, w) ^ 0x80808080u;
+          k0[2 * w] = __builtin_amdgcn_perm(0x64646464u, b0, 0x04010400u);
+          k0[2 * w + 1] = __builtin_amdgcn_perm(0x64646464u, b0, 0x04030402u);
+          k1[2 * w] = __builtin_amdgcn_perm(0x64646464u, b1, 0x04010400u);
+          k1[2 * w + 1] = __builtin_amdgcn_perm(0x64646464u, b1, 0x04030402u);
         }
-      }
-      float s[GH];
-      bool need = false;
-#pragma unroll
-      for (int h = 0; h < GH; ++h) {
-        float part = 0.f;
-        if constexpr (KV == kBF16) {
-#pragma unroll
-          for (int p = 0; p < 8; ++p)
-            part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qp[h][p]),
-                                                   __builtin_bit_cast(bf162_t, word(kr[p / 4], p % 4)), part, false);
-        } else if constexpr (KV == kF16) {
-#pragma unroll
-          for (int p = 0; p < 8; ++p)
-            part = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qp[h][p]),
-                                          __builtin_bit_cast(half2_t, word(kr[p / 4], p % 4)), part, false);
-        } else if constexpr (I8DOT) {
-#pragma unroll
-          for (int p = 0; p < 8; ++p)
-            part = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qp[h][p]), __builtin_bit_cast(half2_t, kf16[p]),
-                                          part, false);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) part = fmaf(qf[h][e], elem_f32<KV>(kr, e), part);
-        }
-        float dot = group_sum<C>(part);
-        if constexpr (KV == kI8) dot += kconst[h];
-        s[h] = valid ? dot * a.scale_log2 : kNegInf;
-        mtrue[h] = fmaxf(mtrue[h], s[h]);
-        need |= s[h] > mref[h] + kRescale;
-      }
-      if (__builtin_amdgcn_ballot_w64(need)) {  // rare after the first step
+        float s0[GH], s1[GH];
+        bool need = false;
 #pragma unroll
         for (int h = 0; h < GH; ++h) {
-          const float mnew = s[h] > mref[h] + kRescale ? s[h] : mref[h];
-          const float alpha = fast_exp2(mref[h] - mnew);  // 0 on the first valid token
-          lsum[h] *= alpha;
+          float d0 = 0.f, d1 = 0.f;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
-          mref[h] = mnew;
+          for (int q = 0; q < 8; ++q) {
+            d0 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qp[h][q]), __builtin_bit_cast(half2_t, k0[q]), d0,
+                                        false);
+            d1 = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qp[h][q]), __builtin_bit_cast(half2_t, k1[q]), d1,
+                                        false);
+          }
+          d0 = group_sum<C>(d0) + kconst[h];
+          d1 = group_sum<C>(d1) + kconst[h];
+          s0[h] = valid0 ? d0 * a.scale_log2 : kNegInf;
+          s1[h] = valid1 ? d1 * a.scale_log2 : kNegInf;
+          const float sm = fmaxf(s0[h], s1[h]);
+          mtrue[h] = fmaxf(mtrue[h], sm);
+          need |= sm > mref[h] + kRescale;
         }
-      }
-      float p[GH];
+        if (__builtin_amdgcn_ballot_w64(need)) {  // rare after the first steps
 #pragma unroll
-      for (int h = 0; h < GH; ++h) {
-        p[h] = fast_exp2(s[h] - mref[h]);  // <= 2^8; 0 for invalid lanes
-        lsum[h] += p[h];
-      }
+          for (int h = 0; h < GH; ++h) {
+            const float sm = fmaxf(s0[h], s1[h]);
+            const float mnew = sm > mref[h] + kRescale ? sm : mref[h];
+            const float alpha = fast_exp2(mref[h] - mnew);  // 0 on the first valid token
+            lsum[h] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float vf = elem_f32<KV>(vr, e);
+            for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
+            mref[h] = mnew;
+          }
+        }
+        // softmax weights of the two tokens as one fp16 pair (<= 2^8; 0 for
+        // invalid tokens), and the row sum of exactly those values
+        half2_t pw[GH];
+        const half2_t ones = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
-        for (int h = 0; h < GH; ++h) acc[h][e] = fmaf(p[h], vf, acc[h][e]);
+        for (int h = 0; h < GH; ++h) {
+          pw[h] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(fast_exp2(s0[h] - mref[h]), fast_exp2(s1[h] - mref[h])));
+          lsum[h] = __builtin_amdgcn_fdot2(pw[h], ones, lsum[h], false);
+        }
+        // channel pairs across the two steps: bytes (e of step j, e of step
+        // j+1) interleaved, biased, then widened to (1024 + byte) fp16
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t a0 = word(vr0, w), a1 = word(vr1, w);
+          const uint32_t lo = __builtin_amdgcn_perm(a1, a0, 0x05010400u) ^ 0x80808080u;  // e0 j, e0 j+1, e1 j, e1 j+1
+          const uint32_t hi = __builtin_amdgcn_perm(a1, a0, 0x07030602u) ^ 0x80808080u;  // e2 .., e3 ..
+          const uint32_t vp[4] = {__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u),
+                                  __builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u),
+                                  __builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u),
+                                  __builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int h = 0; h < GH; ++h)
+              acc[h][4 * w + q] = __builtin_amdgcn_fdot2(pw[h], __builtin_bit_cast(half2_t, vp[q]), acc[h][4 * w + q], false);
+        }
+        slot = slot1 + 1 == STAGES ? 0 : slot1 + 1;
       }
-      slot = slot == STAGES - 1 ? 0 : slot + 1;
+    } else {
+      int slot = 0;
+      for (int st = wave; st < nsteps; st += 4) {
+        // wait for step st; the loads of this wave's later steps already queued
+        // (at most STAGES-1 of them) stay in flight
+        const int later = (nsteps - 1 - st) / 4;
+        if (later >= STAGES - 1) wait_vmem<(STAGES - 1) * LOADS>();
+        else wait_vmem_steps<STAGES - 2, LOADS>(later);
+        // Copy the step out of its stage and queue the step STAGES ahead into
+        // it at once: the stage is free again after the LDS reads rather than
+        // after the whole step's arithmetic, so the full ring stays in flight.
+        const char* src = ring + slot * S::STEP_BYTES + 16 * lane;
+        u32x4 kr[NCH], vr[NCH];
+  #pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          kr[i] = *reinterpret_cast<const u32x4*>(src + 1024 * i);
+          vr[i] = *reinterpret_cast<const u32x4*>(src + 1024 * (NCH + i));
+        }
+        if (st + 4 * STAGES < nsteps) {
+          wait_lds();  // the direct loads below overwrite this stage
+          issue(st + 4 * STAGES, slot);
+        }
+
+        const bool valid = start + TOK * st + t < end;
+        uint32_t kf16[I8DOT ? 8 : 1];  // int8 K as fp16 pairs (1024 + biased byte)
+        if constexpr (I8DOT) {
+  #pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t bw = word(kr[0], w) ^ 0x80808080u;
+            kf16[2 * w] = __builtin_amdgcn_perm(0x64646464u, bw, 0x04010400u);
+            kf16[2 * w + 1] = __builtin_amdgcn_perm(0x64646464u, bw, 0x04030402u);
+          }
+        }
+        float s[GH];
+        bool need = false;
+  #pragma unroll
+        for (int h = 0; h < GH; ++h) {
+          float part = 0.f;
+          if constexpr (KV == kBF16) {
+  #pragma unroll
+            for (int p = 0; p < 8; ++p)
+              part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, qp[h][p]),
+                                                     __builtin_bit_cast(bf162_t, word(kr[p / 4], p % 4)), part, false);
+          } else if constexpr (KV == kF16) {
+  #pragma unroll
+            for (int p = 0; p < 8; ++p)
+              part = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qp[h][p]),
+                                            __builtin_bit_cast(half2_t, word(kr[p / 4], p % 4)), part, false);
+          } else if constexpr (I8DOT) {
+  #pragma unroll
+            for (int p = 0; p < 8; ++p)
+              part = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, qp[h][p]), __builtin_bit_cast(half2_t, kf16[p]),
+                                            part, false);
+          } else {
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) part = fmaf(qf[h][e], elem_f32<KV>(kr, e), part);
+          }
+          float dot = group_sum<C>(part);
+          if constexpr (KV == kI8) dot += kconst[h];
+          s[h] = valid ? dot * a.scale_log2 : kNegInf;
+          mtrue[h] = fmaxf(mtrue[h], s[h]);
+          need |= s[h] > mref[h] + kRescale;
+        }
+        if (__builtin_amdgcn_ballot_w64(need)) {  // rare after the first step
+  #pragma unroll
+          for (int h = 0; h < GH; ++h) {
+            const float mnew = s[h] > mref[h] + kRescale ? s[h] : mref[h];
+            const float alpha = fast_exp2(mref[h] - mnew);  // 0 on the first valid token
+            lsum[h] *= alpha;
+  #pragma unroll
+            for (int e = 0; e < 16; ++e) acc[h][e] *= alpha;
+            mref[h] = mnew;
+          }
+        }
+        float p[GH];
+  #pragma unroll
+        for (int h = 0; h < GH; ++h) {
+          p[h] = fast_exp2(s[h] - mref[h]);  // <= 2^8; 0 for invalid lanes
+          lsum[h] += p[h];
+        }
+  #pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float vf = elem_f32<KV>(vr, e);
+  #pragma unroll
+          for (int h = 0; h < GH; ++h) acc[h][e] = fmaf(p[h], vf, acc[h][e]);
+        }
+        slot = slot == STAGES - 1 ? 0 : slot + 1;
+      }
     }
   }
   // every queued load has been waited for: the ring is free for the merge
@@ -452,7 +553,7 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
     o = o / tot;
     if constexpr (KV == kI8) {
       const int64_t pi = ((int64_t)a.n_kv + g) * D + d;  // V parameters (index 1)
-      o = a.aq_scale[pi] * (o - 128.f + a.aq_offset[pi]);
+      o = a.aq_scale[pi] * (o - 1152.f + a.aq_offset[pi]);  // P V on (1024 + byte ^ 0x80)
     }
     const int64_t row = (int64_t)b * a.n_q + h0 + h;
     a.ws_o[(row * a.n_split + split) * D + d] = o;
