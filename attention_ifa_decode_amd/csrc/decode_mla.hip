@@ -128,7 +128,8 @@ mla_splitkv_kernel(const MlaLaunch a) {
   constexpr int STAGES = S::STAGES, LOADS_W = S::LOADS_W;
   __shared__ __attribute__((aligned(16))) char ring[STAGES * kTileBytes];
   __shared__ int sm_blk[kMlaMaxTableSlice];
-  __shared__ __attribute__((aligned(16))) uint32_t sm_keys[NW][kLongestFirstMaxBatch];
+  // per-lane byte offsets of this wave's loads within a contiguous tile
+  __shared__ uint32_t sm_loff[NW][LOADS_W][64];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -143,7 +144,10 @@ mla_splitkv_kernel(const MlaLaunch a) {
   const int rank = id / a.n_split;
   int b = rank, L;
   if (a.longest_first) {
-    const BatchPick pick = batch_of_rank(rank, a.seq_lens, a.batch, a.s_cap, sm_keys[wave]);
+    // the ranking keys use the ring, which no load reaches before the
+    // barrier below
+    const BatchPick pick =
+        batch_of_rank(rank, a.seq_lens, a.batch, a.s_cap, reinterpret_cast<uint32_t*>(ring) + wave * kLongestFirstMaxBatch);
     b = pick.b;
     L = pick.len;
   } else {
@@ -165,8 +169,8 @@ mla_splitkv_kernel(const MlaLaunch a) {
       int v = bt[i];
       sm_blk[i] = v < 0 ? 0 : (v >= a.num_blocks ? a.num_blocks - 1 : v);
     }
-    __syncthreads();
   }
+  __syncthreads();  // the block slice is in; every wave is done with its ranking keys
 
   const char* kv = static_cast<const char*>(a.kv);
   const uint32_t ring_lds = lds_addr(ring);
@@ -245,6 +249,48 @@ mla_splitkv_kernel(const MlaLaunch a) {
     }
   };
 
+  // A tile that holds 32 valid tokens of one cache block (or of the
+  // contiguous layout) is 36 contiguous KB: lane l of this wave's load i then
+  // reads byte t * 1152 + 16 ((P % 72) ^ swz(t)) of it, P = 64 (wave + NW i) + l,
+  // t = P / 72, the same for every such tile.  Those offsets are computed once
+  // into LDS; a tile then costs one block-id read and, per load, one LDS read.
+  // Other tiles (straddling a block boundary, or the split's last) take
+  // plan_tile / issue_loads.
+  if constexpr (OFF32) {
+#pragma unroll
+    for (int i = 0; i < LOADS_W; ++i) {
+      const int P = 64 * (wave + NW * i) + lane;
+      const int t = P / kChunks;
+      sm_loff[wave][i][lane] = (uint32_t)(t * kRowBytes + 16 * ((P - kChunks * t) ^ swz(t)));
+    }
+  }
+  auto queue_tile = [&](int j, int slot) {
+    if constexpr (OFF32) {
+      const int tstart = start + kTile * j;
+      bool whole = tstart + kTile <= end;
+      uint32_t row0 = 0;
+      if constexpr (PAGED) {
+        const uint32_t bi = fast_div((uint32_t)tstart, a.bs_magic, a.bs_shift);
+        const uint32_t u = (uint32_t)tstart - bi * (uint32_t)a.block_size;
+        whole = whole && u + kTile <= (uint32_t)a.block_size;
+        if (whole) row0 = (uint32_t)__builtin_amdgcn_readfirstlane(sm_blk[(int)bi - blk0]) * (uint32_t)a.block_size + u;
+      } else {
+        row0 = (uint32_t)b * (uint32_t)a.s_cap + (uint32_t)tstart;
+      }
+      if (whole) {
+        const char* base = kv + (uint64_t)row0 * kRowBytes;
+        const uint32_t dst = ring_lds + slot * kTileBytes;
+        uint32_t off[LOADS_W];
+#pragma unroll
+        for (int i = 0; i < LOADS_W; ++i) off[i] = sm_loff[wave][i][lane];
+#pragma unroll
+        for (int i = 0; i < LOADS_W; ++i) dma16_off(base, off[i], dst + 1024 * (wave + NW * i));
+        return;
+      }
+    }
+    issue_loads(plan_tile(j, slot), 0, LOADS_W);
+  };
+
   // ---- Q^T operand: this wave's 32 heads, 8 channels per lane per k-step ----
   const int head = hg * (32 * NW) + wave * 32 + (lane & 31);
   const bf16x8_t* qrow =
@@ -257,7 +303,7 @@ mla_splitkv_kernel(const MlaLaunch a) {
 
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s)
-    if (s < ntiles) issue_loads(plan_tile(s, s), 0, LOADS_W);
+    if (s < ntiles) queue_tile(s, s);
 
   // ---- per-lane LDS offsets (relative to a tile's slot) ----
   // S^T A operand: token t = lane % 32, chunk 2 ks + h at position
@@ -316,7 +362,7 @@ mla_splitkv_kernel(const MlaLaunch a) {
     }
     __syncthreads();  // every wave's share of tile i is in; tile i-1 is consumed
     // tile i + STAGES - 1 goes into the slot of tile i - 1
-    if (i + STAGES - 1 < ntiles) issue_loads(plan_tile(i + STAGES - 1, (i + STAGES - 1) % STAGES), 0, LOADS_W);
+    if (i + STAGES - 1 < ntiles) queue_tile(i + STAGES - 1, (i + STAGES - 1) % STAGES);
     const uint32_t slot = ring_lds + (i % STAGES) * kTileBytes;
     const int tstart = start + kTile * i;
 
