@@ -275,8 +275,24 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
     float qf[PACKQ ? 1 : GH][PACKQ ? 1 : 16];
     uint32_t qp[PACKQ ? GH : 1][PACKQ ? 8 : 1];
     float kconst[GH];  // int8: sum_d q'_d (offset_d - 1152), with q' as rounded to fp16
+    // q in K's dtype and 16-byte aligned: the lane's 16 channels are two runs
+    // of 8 (channels 8c.. and 8(C + c)..), i.e. two 16-byte loads per head
+    const bool q16 = DOT2 && (reinterpret_cast<uintptr_t>(a.q) & 15) == 0;
+    if (q16) {
 #pragma unroll
-    for (int h = 0; h < GH; ++h) {
+      for (int h = 0; h < GH; ++h) {
+        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.n_q + h0 + h) * D;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 8 * (c + C * i));
+#pragma unroll
+          for (int w = 0; w < 4; ++w) qp[h][4 * i + w] = word(v, w);
+        }
+        kconst[h] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < GH && !q16; ++h) {
       const int64_t qrow = ((int64_t)b * a.n_q + h0 + h) * D;
       float part = 0.f;
 #pragma unroll

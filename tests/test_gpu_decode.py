@@ -174,6 +174,23 @@ def test_unaligned_output_buffer(out_dtype):
     _compare(w, out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse)
 
 
+@pytest.mark.parametrize("kv", ["f16", "bf16"])
+def test_unaligned_query_buffer(kv):
+    """query one element past a 16-byte boundary (element-wise q loads)."""
+    w = make_workload(batch=2, n_q=8, n_kv=2, qk_dim=128, kv_dtype=kv, layout="paged", block_size=64,
+                      lengths=[300, 45], seed=22)
+    wg = w.to("cuda")
+    buf = torch.empty(wg.q.numel() + 1, dtype=wg.q.dtype, device="cuda")
+    q = buf[1:].view(wg.q.shape)
+    q.copy_(wg.q)
+    assert q.data_ptr() % 16 != 0
+    out, lse = ifa.decode(q, wg.k_cache, wg.v_cache, wg.block_table, wg.seq_lens, w.n_q, w.n_kv, w.scale,
+                          learnable_sink=wg.sink, num_splits=3, v_dim=w.v_dim, out_dtype=wg.out_dtype)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.decode_workload(w)
+    _compare(w, out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse)
+
+
 @pytest.mark.parametrize("group", [1, 2, 4, 8, 16])
 def test_gqa_group_sizes(group):
     w = make_workload(batch=2, n_q=8 * group if group < 16 else 32, n_kv=8 if group < 16 else 2,
