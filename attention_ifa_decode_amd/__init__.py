@@ -45,6 +45,7 @@ EXPORTED = (
     "ifa_decode_num_splits",
     "ifa_decode",
     "ifa_decode_splitkv",
+    "ifa_decode_splitkv_timed",
     "ifa_decode_combine",
     "attn_update",
     "ifa_paged_block_count",
@@ -107,6 +108,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ifa_decode_num_splits.argtypes = [args_p, ctypes.POINTER(I32)]
     for fn in (lib.ifa_decode, lib.ifa_decode_splitkv):
         fn.argtypes = [args_p, P, SZ, P]
+    lib.ifa_decode_splitkv_timed.argtypes = [args_p, P, SZ, P, P, P]
     lib.ifa_decode_combine.argtypes = [args_p, P, SZ, P]
     lib.attn_update.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I32, I32, P]
     lib.ifa_paged_block_count.argtypes = [ctypes.POINTER(I64), I64, I64]
@@ -114,7 +116,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ifa_last_error.argtypes = []
     lib.ifa_last_error.restype = ctypes.c_char_p
     for name in ("ifa_decode_workspace_size", "ifa_decode_num_splits", "ifa_decode", "ifa_decode_splitkv",
-                 "ifa_decode_combine", "attn_update"):
+                 "ifa_decode_splitkv_timed", "ifa_decode_combine", "attn_update"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -235,6 +237,16 @@ class DecodeCall:
     def splitkv(self):
         _check(self._lib.ifa_decode_splitkv(ctypes.byref(self.args), self.workspace.data_ptr(),
                                             self.workspace_bytes, _stream_handle()))
+
+    def splitkv_timed(self, start: "torch.cuda.Event", stop: "torch.cuda.Event"):
+        """splitkv() with `start` / `stop` (timing events of this device)
+        recorded at the kernel's own start and end."""
+        for e in (start, stop):
+            if not e.cuda_event:  # torch creates the event at its first record
+                e.record()
+        _check(self._lib.ifa_decode_splitkv_timed(ctypes.byref(self.args), self.workspace.data_ptr(),
+                                                  self.workspace_bytes, _stream_handle(), start.cuda_event,
+                                                  stop.cuda_event))
 
     def combine(self):
         _check(self._lib.ifa_decode_combine(ctypes.byref(self.args), self.workspace.data_ptr(),

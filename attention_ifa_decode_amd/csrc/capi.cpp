@@ -224,7 +224,8 @@ ifa_status runtime(hipError_t e, const char* what) {
   return fail(IFA_ERR_RUNTIME, "%s: %s", what, hipGetErrorString(e));
 }
 
-ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStream_t stream) {
+ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStream_t stream,
+                       const ifa::LaunchEvents* ev = nullptr) {
   char* w = static_cast<char*>(ws);
   const int64_t max_len = a->kv_layout == IFA_KV_PAGED ? a->max_blocks_per_seq * a->block_size : a->s_cap;
   const float scale_log2 = (float)(a->scale_value * 1.4426950408889634);
@@ -257,7 +258,7 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
     L.q_dtype = a->q_dtype;
     L.kv_dtype = a->kv_dtype;
     L.head_dim = (int)a->qk_dim;
-    return runtime(ifa::launch_gqa_splitkv(L, stream), "split-KV decode launch");
+    return runtime(ifa::launch_gqa_splitkv(L, stream, ev), "split-KV decode launch");
   }
   ifa::MlaLaunch M{};
   M.q = a->query;
@@ -280,7 +281,7 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
   M.qk_dim = (int)a->qk_dim;
   M.v_dim = (int)a->v_dim;
   M.paged = a->kv_layout == IFA_KV_PAGED;
-  return runtime(ifa::launch_mla_splitkv(M, stream), "MLA split-KV decode launch");
+  return runtime(ifa::launch_mla_splitkv(M, stream, ev), "MLA split-KV decode launch");
 }
 
 ifa_status run_combine(const ifa_decode_args* a, const Plan& p, const void* ws, hipStream_t stream) {
@@ -332,6 +333,19 @@ ifa_status ifa_decode_splitkv(const ifa_decode_args* args, void* workspace, size
   if ((st = check_workspace(p, workspace, workspace_bytes)) != IFA_OK) return st;
   if (args->batch == 0) return ok();
   if ((st = run_splitkv(args, p, workspace, stream)) != IFA_OK) return st;
+  return ok();
+}
+
+ifa_status ifa_decode_splitkv_timed(const ifa_decode_args* args, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+  if (!start || !stop) return fail(IFA_ERR_PARAM_NULLPTR, "start and stop events are required");
+  Plan p;
+  ifa_status st = validate_and_plan(args, &p);
+  if (st != IFA_OK) return st;
+  if ((st = check_workspace(p, workspace, workspace_bytes)) != IFA_OK) return st;
+  if (args->batch == 0) return ok();
+  const ifa::LaunchEvents ev{start, stop};
+  if ((st = run_splitkv(args, p, workspace, stream, &ev)) != IFA_OK) return st;
   return ok();
 }
 

@@ -581,37 +581,37 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
 }
 
 template <int QT, int KV, int D, int GH>
-hipError_t launch_typed(const GqaLaunch& p, hipStream_t stream) {
+hipError_t launch_typed(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
   const int items = p.batch * p.n_kv * (p.group / GH) * p.n_split;
   if (items == 0) return hipSuccess;
   // head-group interleave (see the kernel): items without the head group,
   // rounded up to a multiple of 8, times the head groups
   const int padded = (items / (p.group / GH) + 7) / 8 * 8 * (p.group / GH);
   if (p.paged)
-    hipLaunchKernelGGL((gqa_splitkv_kernel<QT, KV, D, GH, true>), dim3(padded), dim3(256), 0, stream, p, items);
+    launch_kernel(gqa_splitkv_kernel<QT, KV, D, GH, true>, dim3(padded), dim3(256), stream, ev, p, items);
   else
-    hipLaunchKernelGGL((gqa_splitkv_kernel<QT, KV, D, GH, false>), dim3(padded), dim3(256), 0, stream, p, items);
+    launch_kernel(gqa_splitkv_kernel<QT, KV, D, GH, false>, dim3(padded), dim3(256), stream, ev, p, items);
   return hipGetLastError();
 }
 
 template <int QT, int KV, int D>
-hipError_t launch_gh(const GqaLaunch& p, hipStream_t stream) {
+hipError_t launch_gh(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
   switch (p.heads_per_wg) {
-    case 1: return launch_typed<QT, KV, D, 1>(p, stream);
-    case 2: return launch_typed<QT, KV, D, 2>(p, stream);
-    case 4: return launch_typed<QT, KV, D, 4>(p, stream);
+    case 1: return launch_typed<QT, KV, D, 1>(p, stream, ev);
+    case 2: return launch_typed<QT, KV, D, 2>(p, stream, ev);
+    case 4: return launch_typed<QT, KV, D, 4>(p, stream, ev);
     case 8:
-      if constexpr (KV == kF16 || KV == kBF16) return launch_typed<QT, KV, D, 8>(p, stream);
+      if constexpr (KV == kF16 || KV == kBF16) return launch_typed<QT, KV, D, 8>(p, stream, ev);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
 template <int QT, int KV>
-hipError_t launch_d(const GqaLaunch& p, hipStream_t stream) {
+hipError_t launch_d(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
   switch (p.head_dim) {
-    case 64: return launch_gh<QT, KV, 64>(p, stream);
-    case 128: return launch_gh<QT, KV, 128>(p, stream);
+    case 64: return launch_gh<QT, KV, 64>(p, stream, ev);
+    case 128: return launch_gh<QT, KV, 128>(p, stream, ev);
     default: return hipErrorInvalidValue;
   }
 }
@@ -633,19 +633,19 @@ bool gqa_supported(int q_dtype, int kv_dtype, int head_dim, int heads_per_wg) {
   return q_dtype == kv_dtype && (kv_dtype == kF32 || kv_dtype == kF16 || kv_dtype == kBF16);
 }
 
-hipError_t launch_gqa_splitkv(const GqaLaunch& p, hipStream_t stream) {
+hipError_t launch_gqa_splitkv(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
   if (!gqa_supported(p.q_dtype, p.kv_dtype, p.head_dim, p.heads_per_wg)) return hipErrorInvalidValue;
   if (p.kv_dtype == kI8) {
     switch (p.q_dtype) {
-      case kF32: return launch_d<kF32, kI8>(p, stream);
-      case kF16: return launch_d<kF16, kI8>(p, stream);
-      default: return launch_d<kBF16, kI8>(p, stream);
+      case kF32: return launch_d<kF32, kI8>(p, stream, ev);
+      case kF16: return launch_d<kF16, kI8>(p, stream, ev);
+      default: return launch_d<kBF16, kI8>(p, stream, ev);
     }
   }
   switch (p.kv_dtype) {
-    case kF32: return launch_d<kF32, kF32>(p, stream);
-    case kF16: return launch_d<kF16, kF16>(p, stream);
-    default: return launch_d<kBF16, kBF16>(p, stream);
+    case kF32: return launch_d<kF32, kF32>(p, stream, ev);
+    case kF16: return launch_d<kF16, kF16>(p, stream, ev);
+    default: return launch_d<kBF16, kBF16>(p, stream, ev);
   }
 }
 

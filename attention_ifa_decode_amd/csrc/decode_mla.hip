@@ -490,14 +490,14 @@ mla_splitkv_kernel(const MlaLaunch a) {
 }
 
 template <int NW>
-hipError_t launch_nw(const MlaLaunch& p, hipStream_t stream) {
+hipError_t launch_nw(const MlaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
   const int items = p.batch * p.n_split * (p.n_q / (32 * NW));
   if (items == 0) return hipSuccess;
   const uint64_t rows = p.paged ? (uint64_t)p.num_blocks * (uint64_t)p.block_size : (uint64_t)p.batch * (uint64_t)p.s_cap;
   const bool off32 = rows * kRowBytes < (1ull << 32);
   auto kern = p.paged ? (off32 ? mla_splitkv_kernel<NW, true, true> : mla_splitkv_kernel<NW, true, false>)
                       : (off32 ? mla_splitkv_kernel<NW, false, true> : mla_splitkv_kernel<NW, false, false>);
-  hipLaunchKernelGGL(kern, dim3(items), dim3(NW * 64), 0, stream, p);
+  launch_kernel(kern, dim3(items), dim3(NW * 64), stream, ev, p);
   return hipGetLastError();
 }
 
@@ -505,11 +505,11 @@ hipError_t launch_nw(const MlaLaunch& p, hipStream_t stream) {
 
 bool mla_supported(int n_q) { return n_q >= 32 && n_q % 32 == 0; }
 
-hipError_t launch_mla_splitkv(const MlaLaunch& p, hipStream_t stream) {
+hipError_t launch_mla_splitkv(const MlaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
   if (p.qk_dim != kDqk || p.v_dim != kDv || !mla_supported(p.n_q)) return hipErrorInvalidValue;
-  if (p.n_q % 128 == 0) return launch_nw<4>(p, stream);
-  if (p.n_q % 64 == 0) return launch_nw<2>(p, stream);
-  return launch_nw<1>(p, stream);
+  if (p.n_q % 128 == 0) return launch_nw<4>(p, stream, ev);
+  if (p.n_q % 64 == 0) return launch_nw<2>(p, stream, ev);
+  return launch_nw<1>(p, stream, ev);
 }
 
 }  // namespace ifa

@@ -1,6 +1,7 @@
 // Launch descriptors shared by the host library and the kernel files.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -100,8 +101,22 @@ constexpr int kLongestFirstMaxBatch = 256;
 // Most block-table entries one split of the MLA path may touch (staged in LDS).
 constexpr int kMlaMaxTableSlice = 1024;
 
-hipError_t launch_gqa_splitkv(const GqaLaunch& p, hipStream_t stream);
-hipError_t launch_mla_splitkv(const MlaLaunch& p, hipStream_t stream);
+// Optional events that a launch records around the kernel itself
+// (hipExtLaunchKernel), for measuring the kernel's own duration.
+struct LaunchEvents {
+  hipEvent_t start, stop;
+};
+
+template <typename K, typename... A>
+inline void launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, const LaunchEvents* ev, A... args) {
+  if (ev)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev->start, ev->stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+}
+
+hipError_t launch_gqa_splitkv(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev = nullptr);
+hipError_t launch_mla_splitkv(const MlaLaunch& p, hipStream_t stream, const LaunchEvents* ev = nullptr);
 hipError_t launch_combine(const CombineLaunch& p, hipStream_t stream);
 hipError_t launch_update(const UpdateLaunch& p, hipStream_t stream);
 

@@ -143,6 +143,15 @@ ifa_status ifa_decode(const ifa_decode_args* args, void* workspace, size_t works
 ifa_status ifa_decode_splitkv(const ifa_decode_args* args, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/* ifa_decode_splitkv for measurement: the same work, launched so that the
+ * runtime records `start` and `stop` (events the caller created on this
+ * device with timing enabled) at the split-KV kernel's own start and end
+ * (hipExtLaunchKernel), which an event recorded around the call on the stream
+ * cannot do as tightly.  IFA_ERR_PARAM_NULLPTR if either event is NULL;
+ * with batch 0 nothing is launched and the events are not recorded. */
+ifa_status ifa_decode_splitkv_timed(const ifa_decode_args* args, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 /* Second half of ifa_decode: merges the non-empty split partials of each
  * (batch, query head) in split order with the RingAttentionUpdate rule, folds
  * in the learnable sink as one more partial (attn_out 0, max sink_h, sum 1),

@@ -172,6 +172,19 @@ def test_workspace_too_small_or_misaligned():
     assert lib().ifa_decode(ctypes.byref(a), None, sz, None) == ifa.IFA_ERR_PARAM_NULLPTR
 
 
+def test_timed_splitkv_checks_before_launching():
+    """The timed variant validates like ifa_decode_splitkv and requires both
+    events; every case here is rejected on the host, before any launch."""
+    a = base_args()
+    st, sz = ws_size(a)
+    L = lib()
+    assert L.ifa_decode_splitkv_timed(ctypes.byref(a), FAKE, sz, None, None, FAKE) == ifa.IFA_ERR_PARAM_NULLPTR
+    assert L.ifa_decode_splitkv_timed(ctypes.byref(a), FAKE, sz, None, FAKE, None) == ifa.IFA_ERR_PARAM_NULLPTR
+    assert L.ifa_decode_splitkv_timed(ctypes.byref(a), FAKE, sz - 1, None, FAKE, FAKE) == ifa.IFA_ERR_PLAN
+    bad = base_args(num_splits=-1)
+    assert L.ifa_decode_splitkv_timed(ctypes.byref(bad), FAKE, sz, None, FAKE, FAKE) == ifa.IFA_ERR_PARAM_INVALID
+
+
 def test_null_args_and_outputs():
     L = lib()
     sz = ctypes.c_size_t()

@@ -269,6 +269,25 @@ def test_partials_match_oracle_triples():
                     assert abs(ps[b, h, i] - s) < 1e-4 * s
 
 
+def test_timed_splitkv_same_partials():
+    """ifa_decode_splitkv_timed leaves the same workspace as
+    ifa_decode_splitkv and records a positive kernel time."""
+    w = make_workload(batch=3, n_q=8, n_kv=2, qk_dim=128, kv_dtype="bf16", layout="paged", block_size=64,
+                      lengths=[900, 33, 1], seed=23)
+    wg = w.to("cuda")
+    c1 = ifa.call_for_workload(wg, num_splits=4)
+    c2 = ifa.call_for_workload(wg, num_splits=4)
+    c1.workspace.zero_()  # slots of empty splits are never written
+    c2.workspace.zero_()
+    c1.splitkv()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c2.splitkv_timed(e0, e1)
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) > 0
+    for x, y in zip(c1.partials(), c2.partials()):
+        assert torch.equal(x, y)
+
+
 # ------------------------------------------------------------ full sizes, sampled rows
 def _sampled_rows(w, k, seed):
     rng = np.random.default_rng(seed)
