@@ -125,6 +125,40 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 #endif
 constexpr int kRingBytesPerWave = IFA_GQA_RING_BYTES;
 
+// The value that lane ^ X holds, X in {4, 8, 16, 32}.  The permlane swaps,
+// given one register twice, return it with the partner row's half swapped in
+// (first result: own lanes where the lane bit is clear), so the partner's
+// value is the first result in the upper half and the second in the lower.
+template <int X>
+__device__ __forceinline__ float xor_lane(float x) {
+  static_assert(X == 4 || X == 8 || X == 16 || X == 32, "lane distance");
+  if constexpr (X == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  } else if constexpr (X == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+  } else if constexpr (X == 8) {
+    return dpp_f32<kDppRowRor8>(x);  // rotation by 8 inside a row of 16 = lane ^ 8
+  } else {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (4 << 10) | 0x1f));  // lane ^ 4
+  }
+}
+
+// One halving step of a reduce-scatter over lanes l and l ^ X: the lane with
+// bit X set keeps the upper half of v[0, 2H), the other the lower half, each
+// adding the partner's copy of the half it keeps.
+template <int H, int X>
+__device__ __forceinline__ void reduce_scatter_step(float (&v)[16]) {
+  const bool upper = (threadIdx.x & X) != 0;
+#pragma unroll
+  for (int i = 0; i < H; ++i) {
+    const float lo = v[i], hi = v[i + H];
+    const float send = upper ? lo : hi;
+    v[i] = (upper ? hi : lo) + xor_lane<X>(send);
+  }
+}
+
 template <int QT, int KV, int D, int GH>
 struct GqaShape {
   static constexpr int C = D / 16;           // lanes per token row
@@ -531,17 +565,35 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
     const float f = mref[h] == kMrefInit ? 0.f : fast_exp2(mref[h] - mw[h]);
     lsum[h] = strided_sum<C>(lsum[h] * f);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[h][e] = strided_sum<C>(acc[h][e] * f);
+    for (int e = 0; e < 16; ++e) acc[h][e] *= f;
+    // reduce-scatter over the TOK token lanes (lane = t C + c, so the bits
+    // of t are lane bits 5, 4, ... down to log2 C): each step halves the
+    // element range by the next lower bit of t, and token lane t ends with
+    // the sums of elements EPL t .. EPL t + EPL - 1 in acc[h][0 .. EPL - 1]
+    reduce_scatter_step<8, 32>(acc[h]);
+    reduce_scatter_step<4, 16>(acc[h]);
+    reduce_scatter_step<2, 8>(acc[h]);
+    if constexpr (TOK == 16) reduce_scatter_step<1, 4>(acc[h]);
   }
 
   // ---- merge the 4 waves through LDS (reusing the ring) and write ----
+  // Token lane t writes the sums of elements EPL t .. EPL t + EPL - 1 of each
+  // head (EPL = 16 / TOK), which are consecutive channels.
   __syncthreads();
   float* sm_acc = reinterpret_cast<float*>(smem);  // [4][GH][D]
-  if (t == 0) {
+  {
+    constexpr int EPL = 16 / TOK;  // elements per lane: 2 at D 128, 1 at D 64
+    static_assert(EPL == 1 || EPL == 2, "lane groups");
 #pragma unroll
-    for (int h = 0; h < GH; ++h)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sm_acc[(wave * GH + h) * D + E * ((e / E) * C + c) + e % E] = acc[h][e];
+    for (int h = 0; h < GH; ++h) {
+      const int e0 = EPL * t;  // a run of EPL channels inside one chunk of E
+      float* dst = sm_acc + (wave * GH + h) * D + E * ((e0 / E) * C + c) + e0 % E;
+      if constexpr (EPL == 2) {
+        *reinterpret_cast<float2*>(dst) = float2{acc[h][0], acc[h][1]};
+      } else {
+        *dst = acc[h][0];
+      }
+    }
   }
   if (lane == 0) {
 #pragma unroll
@@ -551,28 +603,36 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < GH * D; idx += 256) {
-    const int h = idx / D, d = idx % D;
+  // 4 consecutive outputs per thread: one 16-byte LDS read per wave and one
+  // 16-byte store
+  for (int idx = threadIdx.x; idx < GH * D / 4; idx += 256) {
+    const int h = idx / (D / 4), d = 4 * (idx % (D / 4));
     float M = kNegInf;
 #pragma unroll
     for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, sm_m[wv][h]);
-    float tot = 0.f, o = 0.f;
+    float tot = 0.f;
+    float4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int wv = 0; wv < 4; ++wv) {
       const float mwv = sm_m[wv][h];
       if (mwv != kNegInf) {
         const float f = fast_exp2(mwv - M);
+        const float4 x = *reinterpret_cast<const float4*>(sm_acc + (wv * GH + h) * D + d);
         tot = fmaf(sm_l[wv][h], f, tot);
-        o = fmaf(sm_acc[(wv * GH + h) * D + d], f, o);
+        o.x = fmaf(x.x, f, o.x), o.y = fmaf(x.y, f, o.y), o.z = fmaf(x.z, f, o.z), o.w = fmaf(x.w, f, o.w);
       }
     }
-    o = o / tot;
+    const float inv = 1.f / tot;
+    o.x *= inv, o.y *= inv, o.z *= inv, o.w *= inv;
     if constexpr (KV == kI8) {
-      const int64_t pi = ((int64_t)a.n_kv + g) * D + d;  // V parameters (index 1)
-      o = a.aq_scale[pi] * (o - 1152.f + a.aq_offset[pi]);  // P V on (1024 + byte ^ 0x80)
+      // P V ran on (1024 + byte ^ 0x80): x_hat = (byte + offset) * scale
+      const float* vsc = a.aq_scale + ((int64_t)a.n_kv + g) * D + d;  // V parameters (index 1)
+      const float* vof = a.aq_offset + ((int64_t)a.n_kv + g) * D + d;
+      o.x = vsc[0] * (o.x - 1152.f + vof[0]), o.y = vsc[1] * (o.y - 1152.f + vof[1]);
+      o.z = vsc[2] * (o.z - 1152.f + vof[2]), o.w = vsc[3] * (o.w - 1152.f + vof[3]);
     }
     const int64_t row = (int64_t)b * a.n_q + h0 + h;
-    a.ws_o[(row * a.n_split + split) * D + d] = o;
+    *reinterpret_cast<float4*>(a.ws_o + (row * a.n_split + split) * D + d) = o;
     if (d == 0) {
       a.ws_m[row * a.n_split + split] = M * kLn2;
       a.ws_l[row * a.n_split + split] = tot;
