@@ -48,7 +48,7 @@ struct Plan {
   int group;
   int heads_per_wg;
   int n_split;
-  size_t off_o, off_m, off_l, bytes;
+  size_t off_o, off_m, off_l, off_plan, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -204,7 +204,9 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
   p.off_o = 0;
   p.off_m = align256(rows * (size_t)a->v_dim * sizeof(float));
   p.off_l = p.off_m + align256(rows * sizeof(float));
-  p.bytes = p.off_l + align256(rows * sizeof(float));
+  p.off_plan = p.off_l + align256(rows * sizeof(float));
+  // longest-first plan: (sequence, clamped length) per rank, int32 pairs
+  p.bytes = p.off_plan + (a->batch <= ifa::kLongestFirstMaxBatch ? align256((size_t)a->batch * 8) : 0);
   if (rows == 0) p.bytes = 0;
   *plan = p;
   return IFA_OK;
@@ -228,6 +230,20 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
                        const ifa::LaunchEvents* ev = nullptr) {
   char* w = static_cast<char*>(ws);
   const int64_t max_len = a->kv_layout == IFA_KV_PAGED ? a->max_blocks_per_seq * a->block_size : a->s_cap;
+  // Longest-first order for batches of up to 256 sequences.  The int8-KV GQA
+  // kernel, with twice the workgroups and each one's start not hidden behind
+  // streaming, takes it from a planning kernel launched first; the 16-bit GQA
+  // and MLA workgroups rank the lengths themselves, which costs less than the
+  // extra launch there.
+  const bool longest_first = a->batch <= ifa::kLongestFirstMaxBatch;
+  const bool use_plan = longest_first && p.path == Path::kGqa && a->kv_dtype == IFA_I8;
+  int2* plan = nullptr;
+  if (use_plan) {
+    plan = reinterpret_cast<int2*>(w + p.off_plan);
+    ifa_status st = runtime(ifa::launch_plan(a->actual_seq_lengths, (int)a->batch, max_len, plan, stream),
+                            "planning launch");
+    if (st != IFA_OK) return st;
+  }
   const float scale_log2 = (float)(a->scale_value * 1.4426950408889634);
   if (p.path == Path::kGqa) {
     ifa::GqaLaunch L{};
@@ -254,7 +270,8 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
     L.paged = a->kv_layout == IFA_KV_PAGED;
     L.scale_log2 = scale_log2;
     if (L.paged) ifa::make_divisor((uint32_t)a->block_size, &L.bs_magic, &L.bs_shift);
-    L.longest_first = a->batch <= ifa::kLongestFirstMaxBatch;
+    L.plan = plan;
+    L.longest_first = longest_first;
     L.q_dtype = a->q_dtype;
     L.kv_dtype = a->kv_dtype;
     L.head_dim = (int)a->qk_dim;
@@ -277,7 +294,7 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
   M.num_blocks = (int)a->num_blocks;
   M.scale_log2 = scale_log2;
   if (a->kv_layout == IFA_KV_PAGED) ifa::make_divisor((uint32_t)a->block_size, &M.bs_magic, &M.bs_shift);
-  M.longest_first = a->batch <= ifa::kLongestFirstMaxBatch;
+  M.longest_first = longest_first;
   M.qk_dim = (int)a->qk_dim;
   M.v_dim = (int)a->v_dim;
   M.paged = a->kv_layout == IFA_KV_PAGED;

@@ -1,5 +1,6 @@
 // Merge kernels (gfx950): the n-way combine of split partials with the
-// learnable sink, and the pairwise RingAttentionUpdate.
+// learnable sink, and the pairwise RingAttentionUpdate; and the small
+// planning kernel that ranks the sequences for the split-KV kernels.
 //
 // Both apply the update rule of aclnnRingAttentionUpdate ("功能说明"), in its
 // sum-weighted form: with M the largest softmax_max, every partial i enters
@@ -208,7 +209,23 @@ hipError_t launch_combine_vd(const CombineLaunch& p, dim3 grid, hipStream_t stre
   return hipGetLastError();
 }
 
+// Longest-first plan for one launch: one wave ranks all sequences.
+__global__ void __launch_bounds__(64) plan_kernel(const int64_t* lens, int batch, int64_t cap, int2* plan) {
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kLongestFirstMaxBatch];
+  int len[kLongestFirstMaxBatch / 64], rank[kLongestFirstMaxBatch / 64];
+  rank_lengths(lens, batch, cap, keys, len, rank);
+#pragma unroll
+  for (int c = 0; c < kLongestFirstMaxBatch / 64; ++c)
+    if (len[c] >= 0) plan[rank[c]] = int2{c * 64 + (int)threadIdx.x, len[c]};
+}
+
 }  // namespace
+
+hipError_t launch_plan(const int64_t* seq_lens, int batch, int64_t cap, int2* plan, hipStream_t stream) {
+  if (batch < 1 || batch > kLongestFirstMaxBatch) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(64), 0, stream, seq_lens, batch, cap, plan);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const CombineLaunch& p, hipStream_t stream) {
   const int64_t rows = (int64_t)p.batch * p.n_q;

@@ -196,32 +196,23 @@ __device__ __forceinline__ int lanes_from_scalar_loads(const int* p, int n, int 
   return v;
 }
 
-// The batch that comes `rank`-th when sequences are ordered by descending
-// clamped length (ties by batch index), and that length.  Dispatching long
-// sequences first keeps the last workgroups short (longest-processing-time-
-// first list scheduling).
-//
-// Wave-level, with no barrier: every wave computes it alone from one vector
-// load of the lengths (lane i holds sequence i; chunks of 64 for larger
-// batches).  Each sequence gets a unique 32-bit key, (min(len, 2^23 - 1) + 1)
-// * 256 + 255 - i, so its rank is the number of larger keys; the wave writes
-// its keys to `keys` (this wave's own LDS, kLongestFirstMaxBatch entries) and
-// every lane counts against all of them through broadcast LDS reads, all in
-// vector registers.  A ballot then picks the lane whose rank matches.
-// Lengths beyond 2^23 tie in the key and are ordered by index.  The result is
-// wave-uniform.  Requires batch <= kLongestFirstMaxBatch and
-// 0 <= rank < batch.
-struct BatchPick {
-  int b, len;
-};
-
-__device__ inline BatchPick batch_of_rank(int rank, const int64_t* lens, int batch, int64_t cap, uint32_t* keys) {
+// Longest-first order.  Sequences are ordered by descending clamped length
+// (ties by batch index); dispatching long sequences first keeps the last
+// workgroups short (longest-processing-time-first list scheduling).  Each
+// sequence gets a unique 32-bit key, (min(len, 2^23 - 1) + 1) * 256 + 255 - i,
+// so its rank is the number of larger keys: a wave writes the keys to LDS
+// (`keys`, kLongestFirstMaxBatch entries) and every lane counts against all
+// of them through broadcast LDS reads.  Lengths beyond 2^23 tie in the key and
+// are ordered by index.  Requires batch <= kLongestFirstMaxBatch.
+// Ranks of all sequences: lane i of chunk c gets the clamped length of
+// sequence 64 c + i in len[c] (-1 for padding) and its rank in rank[c].
+__device__ inline void rank_lengths(const int64_t* lens, int batch, int64_t cap, uint32_t* keys,
+                                    int (&len)[kLongestFirstMaxBatch / 64], int (&rank)[kLongestFirstMaxBatch / 64]) {
   constexpr int kChunks = kLongestFirstMaxBatch / 64;
   static_assert(kLongestFirstMaxBatch <= 256, "8-bit index in the key");
   const int lane = threadIdx.x & 63;
   const int nc = (batch + 63) >> 6;
-  int lv[kChunks];
-  uint32_t key[kChunks];  // 0 for padding: below every real key, never picked
+  uint32_t key[kChunks];  // 0 for padding: below every real key
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const int i = c * 64 + lane;
@@ -230,7 +221,7 @@ __device__ inline BatchPick batch_of_rank(int rank, const int64_t* lens, int bat
       x = lens[i];
       x = x < 0 ? 0 : (x > cap ? cap : x);
     }
-    lv[c] = (int)x;
+    len[c] = (int)x;
     key[c] = x < 0 ? 0u : (((uint32_t)(x < (1 << 23) - 1 ? x : (1 << 23) - 1) + 1u) << 8) | (uint32_t)(255 - i);
     if (c < nc) keys[i] = key[c];
   }
@@ -240,28 +231,36 @@ __device__ inline BatchPick batch_of_rank(int rank, const int64_t* lens, int bat
   __builtin_amdgcn_wave_barrier();
   const uint4* k4 = reinterpret_cast<const uint4*>(keys);
   int r[kChunks] = {};
-  if (nc == 1) {
-#pragma unroll 4
-    for (int j = 0; j < 16; ++j) {
-      const uint4 q = k4[j];
-      r[0] += (int)(q.x > key[0]) + (int)(q.y > key[0]) + (int)(q.z > key[0]) + (int)(q.w > key[0]);
-    }
-  } else {
-    for (int j = 0; j < nc * 16; ++j) {
-      const uint4 q = k4[j];
+  for (int j = 0; j < nc * 16; ++j) {
+    const uint4 q = k4[j];
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c)
-        r[c] += (int)(q.x > key[c]) + (int)(q.y > key[c]) + (int)(q.z > key[c]) + (int)(q.w > key[c]);
-    }
+    for (int c = 0; c < kChunks; ++c)
+      r[c] += (int)(q.x > key[c]) + (int)(q.y > key[c]) + (int)(q.z > key[c]) + (int)(q.w > key[c]);
   }
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) rank[c] = r[c];
+}
+
+// The sequence that comes `rank`-th in longest-first order, and its clamped
+// length, computed by one wave alone (no barrier) with `keys` as its own LDS.
+// Requires 0 <= rank < batch <= kLongestFirstMaxBatch.  The result is
+// wave-uniform.
+struct BatchPick {
+  int b, len;
+};
+
+__device__ inline BatchPick batch_of_rank(int rank, const int64_t* lens, int batch, int64_t cap, uint32_t* keys) {
+  constexpr int kChunks = kLongestFirstMaxBatch / 64;
+  int len[kChunks], r[kChunks];
+  rank_lengths(lens, batch, cap, keys, len, r);
   BatchPick p{rank, 0};  // replaced below: the ranks of the real lanes are a permutation of 0..batch-1
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    const uint64_t m = __builtin_amdgcn_ballot_w64(key[c] != 0u && r[c] == rank);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(len[c] >= 0 && r[c] == rank);
     if (m) {
       const int k = __builtin_ctzll(m);
       p.b = c * 64 + k;
-      p.len = __builtin_amdgcn_readlane(lv[c], k);
+      p.len = __builtin_amdgcn_readlane(len[c], k);
     }
   }
   return p;

@@ -215,8 +215,14 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   const int split = rem % a.n_split; rem /= a.n_split;
   const int g = rem % a.n_kv; rem /= a.n_kv;
   int b = rem, L;
-  if (a.longest_first) {
-    // the keys use this wave's part of the ring, which no load has reached yet
+  if (a.plan) {
+    // longest-first: the planning kernel ranked the sequences for this launch
+    const int64_t pl = ld_uniform(reinterpret_cast<const int64_t*>(a.plan), rem);  // (sequence, length)
+    b = (int)(uint32_t)pl;
+    L = (int)(pl >> 32);
+  } else if (a.longest_first) {
+    // longest-first, ranked here by every wave; the keys use this wave's part
+    // of the ring, which no load has reached yet
     uint32_t* keys = reinterpret_cast<uint32_t*>(smem + (threadIdx.x >> 6) * (STAGES * S::STEP_BYTES));
     const BatchPick pick = batch_of_rank(rem, a.seq_lens, a.batch, a.s_cap, keys);
     b = pick.b;

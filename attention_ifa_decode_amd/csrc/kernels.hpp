@@ -26,7 +26,8 @@ struct GqaLaunch {
   float scale_log2;        // scale * log2(e)
   int q_dtype, kv_dtype, head_dim;
   bool paged;
-  bool longest_first;      // order work by descending sequence length
+  const int2* plan;        // [batch] (sequence, clamped length) in longest-first order, or null
+  bool longest_first;      // without a plan: each workgroup ranks the lengths itself
 };
 
 // MLA-shaped decode: all query heads share one latent KV head (MFMA path).
@@ -45,7 +46,7 @@ struct MlaLaunch {
   float scale_log2;
   int qk_dim, v_dim;
   bool paged;
-  bool longest_first;
+  bool longest_first;      // each workgroup ranks the lengths and takes its rank's sequence
 };
 
 struct CombineLaunch {
@@ -118,6 +119,9 @@ inline void launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, c
 hipError_t launch_gqa_splitkv(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev = nullptr);
 hipError_t launch_mla_splitkv(const MlaLaunch& p, hipStream_t stream, const LaunchEvents* ev = nullptr);
 hipError_t launch_combine(const CombineLaunch& p, hipStream_t stream);
+// One workgroup: plan[r] = (sequence, clamped length) of the r-th longest
+// sequence, for the longest-first dispatch of the split-KV kernels.
+hipError_t launch_plan(const int64_t* seq_lens, int batch, int64_t cap, int2* plan, hipStream_t stream);
 hipError_t launch_update(const UpdateLaunch& p, hipStream_t stream);
 
 // Which (q dtype, kv dtype, head dim, heads per workgroup) the VALU path has

@@ -139,7 +139,12 @@ ifa_status ifa_decode(const ifa_decode_args* args, void* workspace, size_t works
  *   softmax_sum fp32 [B][N_q][n]          sum of e^(s_j - softmax_max)
  * in that order, each array starting at a 256-byte aligned offset
  * (n = ifa_decode_num_splits).  Empty splits are not written; the sink is not
- * applied here. */
+ * applied here.  When batch <= 256 a fourth array follows, int32 pairs [B]:
+ * (sequence, clamped length) in descending length order (ties by index).
+ * On the int8-KV path a small planning kernel writes it first and the
+ * split-KV kernel dispatches its work by it (longest sequences first); the
+ * other paths rank the lengths inside the split-KV kernel and leave it
+ * unused. */
 ifa_status ifa_decode_splitkv(const ifa_decode_args* args, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 

@@ -107,6 +107,19 @@ def test_c4_int8_antiquant_sink_reduced(seed):
 
 
 # ------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("batch", [65, 130, 256, 257])
+@pytest.mark.parametrize("kv", ["bf16", "i8"])
+def test_longest_first_batch_sizes(batch, kv):
+    """Batches that span one to four 64-wide chunks of the longest-first
+    ranking (bf16: each workgroup ranks; int8: the planning kernel ranks) and
+    one beyond its 256 limit (index order), with many equal lengths, so that
+    a lost, doubled or misplaced sequence would leave rows wrong."""
+    lens = [int(x) for x in np.random.default_rng(batch).choice([0, 1, 17, 40, 64, 129], size=batch)]
+    w = make_workload(batch=batch, n_q=8, n_kv=2, qk_dim=128, kv_dtype=kv, layout="paged", block_size=64,
+                      lengths=lens, antiquant=kv == "i8", seed=batch + 7)
+    _full_check(w, 2)
+
+
 @pytest.mark.parametrize("kv", ["f32", "f16", "bf16", "i8"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_ragged_lengths_every_dtype(kv, d):

@@ -49,6 +49,14 @@ def test_mla_split_counts(splits):
     _full_check(_mla(lengths=[700, 33, 129], batch=3, seed=52), splits)
 
 
+@pytest.mark.parametrize("batch", [130, 257])
+def test_mla_longest_first_batch_sizes(batch):
+    """Longest-first ranking over three chunks of 64 sequences with many
+    equal lengths, and a batch beyond its 256 limit (index order)."""
+    lens = [int(x) for x in np.random.default_rng(batch).choice([0, 1, 33, 70], size=batch)]
+    _full_check(_mla(n_q=32, batch=batch, lengths=lens, seed=batch), 2)
+
+
 @pytest.mark.parametrize("bs", [16, 64, 256])
 def test_mla_block_sizes(bs):
     """Tiles of 32 tokens that straddle cache blocks (block size 16) and
