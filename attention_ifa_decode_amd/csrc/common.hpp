@@ -200,21 +200,43 @@ __device__ __forceinline__ int lanes_from_scalar_loads(const int* p, int n, int 
 // (ties by batch index); dispatching long sequences first keeps the last
 // workgroups short (longest-processing-time-first list scheduling).  Each
 // sequence gets a unique 32-bit key, (min(len, 2^23 - 1) + 1) * 256 + 255 - i,
-// so its rank is the number of larger keys: a wave writes the keys to LDS
-// (`keys`, kLongestFirstMaxBatch entries) and every lane counts against all
-// of them through broadcast LDS reads.  Lengths beyond 2^23 tie in the key and
-// are ordered by index.  Requires batch <= kLongestFirstMaxBatch.
-// Ranks of all sequences: lane i of chunk c gets the clamped length of
-// sequence 64 c + i in len[c] (-1 for padding) and its rank in rank[c].
+// so its rank is the number of larger keys: the keys go to LDS
+// (kLongestFirstMaxBatch entries) and every lane counts against all of them
+// through broadcast LDS reads.  Lengths beyond 2^23 tie in the key and are
+// ordered by index.  Requires batch <= kLongestFirstMaxBatch.
+constexpr int kRankChunks = kLongestFirstMaxBatch / 64;
+static_assert(kLongestFirstMaxBatch <= 256, "8-bit index in the key");
+
+// Key of sequence i with clamped length x (x < 0: padding, key 0, below
+// every real key).
+__device__ __forceinline__ uint32_t longest_first_key(int64_t x, int i) {
+  return x < 0 ? 0u : (((uint32_t)(x < (1 << 23) - 1 ? x : (1 << 23) - 1) + 1u) << 8) | (uint32_t)(255 - i);
+}
+
+// r[c] = number of the nc * 64 keys in LDS that exceed key[c].
+__device__ __forceinline__ void count_larger(const uint32_t* keys, int nc, const uint32_t (&key)[kRankChunks],
+                                             int (&r)[kRankChunks]) {
+  const uint4* k4 = reinterpret_cast<const uint4*>(keys);
+#pragma unroll
+  for (int c = 0; c < kRankChunks; ++c) r[c] = 0;
+  for (int j = 0; j < nc * 16; ++j) {
+    const uint4 q = k4[j];
+#pragma unroll
+    for (int c = 0; c < kRankChunks; ++c)
+      r[c] += (int)(q.x > key[c]) + (int)(q.y > key[c]) + (int)(q.z > key[c]) + (int)(q.w > key[c]);
+  }
+}
+
+// Ranks of all sequences, by one wave alone (no barrier) with `keys` as its
+// own LDS: lane i of chunk c gets the clamped length of sequence 64 c + i in
+// len[c] (-1 for padding) and its rank in rank[c].
 __device__ inline void rank_lengths(const int64_t* lens, int batch, int64_t cap, uint32_t* keys,
-                                    int (&len)[kLongestFirstMaxBatch / 64], int (&rank)[kLongestFirstMaxBatch / 64]) {
-  constexpr int kChunks = kLongestFirstMaxBatch / 64;
-  static_assert(kLongestFirstMaxBatch <= 256, "8-bit index in the key");
+                                    int (&len)[kRankChunks], int (&rank)[kRankChunks]) {
   const int lane = threadIdx.x & 63;
   const int nc = (batch + 63) >> 6;
-  uint32_t key[kChunks];  // 0 for padding: below every real key
+  uint32_t key[kRankChunks];
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
+  for (int c = 0; c < kRankChunks; ++c) {
     const int i = c * 64 + lane;
     int64_t x = -1;
     if (c < nc && i < batch) {
@@ -222,40 +244,27 @@ __device__ inline void rank_lengths(const int64_t* lens, int batch, int64_t cap,
       x = x < 0 ? 0 : (x > cap ? cap : x);
     }
     len[c] = (int)x;
-    key[c] = x < 0 ? 0u : (((uint32_t)(x < (1 << 23) - 1 ? x : (1 << 23) - 1) + 1u) << 8) | (uint32_t)(255 - i);
+    key[c] = longest_first_key(x, i);
     if (c < nc) keys[i] = key[c];
   }
   // LDS operations of one wave complete in order: the reads below see every
   // lane's write
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const uint4* k4 = reinterpret_cast<const uint4*>(keys);
-  int r[kChunks] = {};
-  for (int j = 0; j < nc * 16; ++j) {
-    const uint4 q = k4[j];
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c)
-      r[c] += (int)(q.x > key[c]) + (int)(q.y > key[c]) + (int)(q.z > key[c]) + (int)(q.w > key[c]);
-  }
-#pragma unroll
-  for (int c = 0; c < kChunks; ++c) rank[c] = r[c];
+  count_larger(keys, nc, key, rank);
 }
 
 // The sequence that comes `rank`-th in longest-first order, and its clamped
-// length, computed by one wave alone (no barrier) with `keys` as its own LDS.
-// Requires 0 <= rank < batch <= kLongestFirstMaxBatch.  The result is
-// wave-uniform.
+// length.  Requires 0 <= rank < batch <= kLongestFirstMaxBatch.  The result
+// is wave-uniform.
 struct BatchPick {
   int b, len;
 };
 
-__device__ inline BatchPick batch_of_rank(int rank, const int64_t* lens, int batch, int64_t cap, uint32_t* keys) {
-  constexpr int kChunks = kLongestFirstMaxBatch / 64;
-  int len[kChunks], r[kChunks];
-  rank_lengths(lens, batch, cap, keys, len, r);
+__device__ __forceinline__ BatchPick pick_rank(int rank, const int (&len)[kRankChunks], const int (&r)[kRankChunks]) {
   BatchPick p{rank, 0};  // replaced below: the ranks of the real lanes are a permutation of 0..batch-1
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
+  for (int c = 0; c < kRankChunks; ++c) {
     const uint64_t m = __builtin_amdgcn_ballot_w64(len[c] >= 0 && r[c] == rank);
     if (m) {
       const int k = __builtin_ctzll(m);
@@ -264,6 +273,13 @@ __device__ inline BatchPick batch_of_rank(int rank, const int64_t* lens, int bat
     }
   }
   return p;
+}
+
+// One wave alone, no barrier: a vector load of the lengths.
+__device__ inline BatchPick batch_of_rank(int rank, const int64_t* lens, int batch, int64_t cap, uint32_t* keys) {
+  int len[kRankChunks], r[kRankChunks];
+  rank_lengths(lens, batch, cap, keys, len, r);
+  return pick_rank(rank, len, r);
 }
 
 }  // namespace ifa

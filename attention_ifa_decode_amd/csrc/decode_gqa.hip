@@ -116,14 +116,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Bytes of the per-wave LDS ring that K/V steps stream through.
 #ifndef IFA_GQA_NT_LOADS
 #define IFA_GQA_NT_LOADS 1
 #endif
+// Bytes of the per-wave LDS ring that K/V steps stream through: two 4-KB
+// steps for 16-bit K/V (measured on the paged bf16 decode, about 1 us faster
+// than three); six 2-KB steps for int8, whose loop takes steps in pairs.
 #ifndef IFA_GQA_RING_BYTES
-#define IFA_GQA_RING_BYTES 12288
+#define IFA_GQA_RING_BYTES 8192
 #endif
 constexpr int kRingBytesPerWave = IFA_GQA_RING_BYTES;
+constexpr int kRingBytesPerWaveI8 = 12288;
 
 // The value that lane ^ X holds, X in {4, 8, 16, 32}.  The permlane swaps,
 // given one register twice, return it with the partner row's half swapped in
@@ -170,12 +173,12 @@ struct GqaShape {
   static constexpr int STEP_BYTES = 2 * NCH * 1024;  // K and V of one step, whole wave
   // eight heads per workgroup leave one wave per SIMD (registers), so that
   // instantiation gets a deeper ring to keep enough loads in flight
-  static constexpr int RING_WAVE = GH == 8 ? 32768 : kRingBytesPerWave;
+  static constexpr int RING_WAVE = GH == 8 ? 32768 : (KV == kI8 ? kRingBytesPerWaveI8 : kRingBytesPerWave);
   static constexpr int STAGES_FIT = RING_WAVE / STEP_BYTES < 2 ? 2 : RING_WAVE / STEP_BYTES;
   static constexpr int STAGES = (STAGES_FIT - 1) * 2 * NCH > 63 ? 63 / (2 * NCH) + 1 : STAGES_FIT;
   static constexpr int LOADS = 2 * NCH;      // load instructions per step
   static constexpr int RING_BYTES = 4 * STAGES * STEP_BYTES;
-  static constexpr int MERGE_BYTES = 4 * GH * D * 4;
+  static constexpr int MERGE_BYTES = 4 * GH * D * 4 + 2 * 4 * GH * 4;  // [4][GH][D] sums, [4][GH] max and sum
   static constexpr int SMEM = RING_BYTES > MERGE_BYTES ? RING_BYTES : MERGE_BYTES;
   static_assert(STAGES * STEP_BYTES >= kLongestFirstMaxBatch * 4, "rank keys fit a wave's ring");
 };
@@ -197,8 +200,6 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   static_assert(D % 16 == 0 && C >= 4 && STAGES >= 2, "shape");
 
   __shared__ __attribute__((aligned(16))) char smem[S::SMEM];
-  __shared__ float sm_m[4][GH];
-  __shared__ float sm_l[4][GH];
 
   // Work items in dispatch order: consecutive workgroups go round robin to
   // the XCDs, so with the longest-first order every XCD receives an equal
@@ -587,6 +588,8 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   // head (EPL = 16 / TOK), which are consecutive channels.
   __syncthreads();
   float* sm_acc = reinterpret_cast<float*>(smem);  // [4][GH][D]
+  float(*sm_m)[GH] = reinterpret_cast<float(*)[GH]>(sm_acc + 4 * GH * D);  // [4][GH]
+  float(*sm_l)[GH] = sm_m + 4;
   {
     constexpr int EPL = 16 / TOK;  // elements per lane: 2 at D 128, 1 at D 64
     static_assert(EPL == 1 || EPL == 2, "lane groups");
