@@ -107,6 +107,20 @@ def test_c4_int8_antiquant_sink_reduced(seed):
 
 
 # ------------------------------------------------------------ edge cases
+@pytest.mark.parametrize("kv,layout,n_q,d", [("bf16", "paged", 32, 128), ("f16", "bnsd", 32, 128),
+                                              ("bf16", "paged", 64, 128), ("f16", "paged", 32, 64)])
+def test_many_workgroups_ragged(kv, layout, n_q, d):
+    """More items than resident workgroups (64 sequences x 8 KV heads x 4
+    splits, about three rounds of dispatch), with lengths from a small set
+    that includes empty and one-token splits, and eight heads per workgroup
+    (n_q 64)."""
+    lens = [int(x) for x in np.random.default_rng(n_q + d).choice([0, 1, 15, 16, 17, 100, 129, 300, 700], size=64)]
+    kw = dict(block_size=64) if layout == "paged" else dict(s_cap=768)
+    w = make_workload(batch=64, n_q=n_q, n_kv=8, qk_dim=d, kv_dtype=kv, layout=layout, lengths=lens,
+                      seed=n_q + d + 11, **kw)
+    _full_check(w, 4)
+
+
 @pytest.mark.parametrize("batch", [65, 130, 256, 257])
 @pytest.mark.parametrize("kv", ["bf16", "i8"])
 def test_longest_first_batch_sizes(batch, kv):
