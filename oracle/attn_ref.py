@@ -9,7 +9,9 @@ Sources, by page title and section:
         Softmax(Q K^T / sqrt(d)) V, query S fixed to 1, per-batch actual KV
         lengths; "Parameters": numHeads, numKeyValueHeads (0 means equal to
         numHeads), scaleValue, antiquantScale/antiquantOffset (index 0 is K,
-        1 is V, per channel); "Constraints": page attention scenario.
+        1 is V; per channel, or per tensor with shape (2)); "Constraints":
+        page attention scenario (KV cache layouts (blocknum, KV_N,
+        blocksize, D) and (blocknum, blocksize, H)), antiquant modes.
 [RAU]   aclnnRingAttentionUpdate — "功能说明" (function) formula for updating
         an attention output from two (out, softmax_max, softmax_sum) results.
 [SINK]  aclnnFlashAttentionScoreV4 — "计算公式" (formula): learnable sink.
@@ -78,23 +80,28 @@ def gather_kv(cache, layout: str, b: int, g: int, length: int,
     [IFA] "Constraints", page attention scenario: key/value sit in one
     contiguous block pool; token j of batch b lives in block
     blockTable[b][j // blockSize] at slot j % blockSize.  Layouts:
-      "paged": (blocknum, KV_N, blocksize, D)   (the page's recommended one)
-      "bnsd" : (B, KV_N, S, D) padded contiguous
+      "paged"    : (blocknum, KV_N, blocksize, D)   (the page's recommended one)
+      "paged_bsh": (blocknum, blocksize, H), H = KV_N * D, held as the 4-D
+                   (blocknum, blocksize, KV_N, D) with the same memory order
+      "bnsd"     : (B, KV_N, S, D) padded contiguous
+      "bsnd"     : (B, S, KV_N, D) padded contiguous ([IFA] "Parameters",
+                   the BSND / BSH key and value layouts)
     Only the first ``dim`` channels are returned when ``dim`` is given.
     """
     j = np.arange(length, dtype=np.int64)
     if layout == "bnsd":
         rows = cache[b, g, :length]
-    elif layout == "paged":
+    elif layout == "bsnd":
+        rows = cache[b, :length, g]
+    elif layout in ("paged", "paged_bsh"):
         bt = _as_int(block_table)
         blk = bt[b, j // block_size] if length else np.zeros(0, np.int64)
         slot = j % block_size
         if hasattr(cache, "detach"):
             import torch
 
-            rows = cache[torch.from_numpy(blk), g, torch.from_numpy(slot)]
-        else:
-            rows = cache[blk, g, slot]
+            blk, slot = torch.from_numpy(blk), torch.from_numpy(slot)
+        rows = cache[blk, g, slot] if layout == "paged" else cache[blk, slot, g]
     else:
         raise ValueError(f"unknown layout {layout!r}")
     rows = as_f64(rows)
@@ -103,10 +110,12 @@ def gather_kv(cache, layout: str, b: int, g: int, length: int,
     return rows
 
 
-def dequant(x: np.ndarray, scale_c: np.ndarray, offset_c: np.ndarray) -> np.ndarray:
-    """[IFA] antiquantScale / antiquantOffset, per-channel mode; reading R2:
-    x_hat = (x + offset) * scale for every token row x."""
-    return (x + offset_c[None, :]) * scale_c[None, :]
+def dequant(x: np.ndarray, scale_c, offset_c) -> np.ndarray:
+    """[IFA] antiquantScale / antiquantOffset; reading R2: x_hat = (x +
+    offset) * scale for every token row x.  Per-channel mode: scale_c and
+    offset_c are vectors over the channels; per-tensor mode: scalars."""
+    # NumPy broadcasting: a vector applies along the channel axis of every row
+    return (x + np.asarray(offset_c, dtype=np.float64)) * np.asarray(scale_c, dtype=np.float64)
 
 
 # ----------------------------------------------------------------------------
@@ -206,7 +215,10 @@ def _kv_rows(k_cache, v_cache, layout, b, g, L, block_table, block_size,
         V = K[:, :v_dim]  # R17: V is the first v_dim channels of the key row
     else:
         V = gather_kv(v_cache, layout, b, g, L, block_table, block_size, dim=v_dim)
-    if aq_scale is not None:
+    if aq_scale is not None and aq_scale.ndim == 1:  # per tensor, shape (2): [K, V]
+        K = dequant(K, aq_scale[0], aq_offset[0])
+        V = dequant(V, aq_scale[1], aq_offset[1])
+    elif aq_scale is not None:  # per channel, (2, KV_N, D)
         K = dequant(K, aq_scale[0, g, :qk_dim], aq_offset[0, g, :qk_dim])
         V = dequant(V, aq_scale[1, g, :v_dim], aq_offset[1, g, :v_dim])
     return K, V

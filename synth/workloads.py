@@ -28,7 +28,10 @@ DTYPES = {
 }
 
 LAYOUT_BNSD = "bnsd"  # contiguous (B, N_kv, S_cap, D)
+LAYOUT_BSND = "bsnd"  # contiguous (B, S_cap, N_kv, D), i.e. (B, S_cap, H)
 LAYOUT_PAGED = "paged"  # block pool (num_blocks, N_kv, block_size, D)
+LAYOUT_PAGED_BSH = "paged_bsh"  # block pool (num_blocks, block_size, N_kv, D), i.e. (num_blocks, block_size, H)
+PAGED_LAYOUTS = (LAYOUT_PAGED, LAYOUT_PAGED_BSH)
 
 
 @dataclasses.dataclass
@@ -49,8 +52,8 @@ class Workload:
     scale: float
     out_dtype: torch.dtype
     sink: Optional[torch.Tensor] = None  # fp32 (N_q,)
-    antiquant_scale: Optional[torch.Tensor] = None  # fp32 (2, N_kv, D)
-    antiquant_offset: Optional[torch.Tensor] = None  # fp32 (2, N_kv, D)
+    antiquant_scale: Optional[torch.Tensor] = None  # fp32 (2, N_kv, D) per channel, or (2,) per tensor
+    antiquant_offset: Optional[torch.Tensor] = None  # the same shape as antiquant_scale
     num_splits: int = 0
 
     @property
@@ -183,6 +186,7 @@ def make_workload(
     scale: Optional[float] = None,
     sink: bool = False,
     antiquant: bool = False,
+    antiquant_mode: str = "channel",
     v_aliases_k: bool = False,
     seed: int = 0,
     device: Union[str, torch.device] = "cpu",
@@ -194,8 +198,9 @@ def make_workload(
 
     ``v_aliases_k`` builds the MLA form: one cache whose first ``v_dim``
     channels serve as V.  ``poison`` fills every stored slot that the decode
-    must never read (BNSD padding past the length, tail slots of a sequence's
-    last block, unused pool blocks) with NaN (127 for int8).
+    must never read (contiguous padding past the length, tail slots of a
+    sequence's last block, unused pool blocks) with NaN (127 for int8).
+    ``antiquant_mode`` "channel" gives (2, N_kv, D) parameters, "tensor" (2,).
     """
     v_dim = qk_dim if v_dim is None else v_dim
     n_kv_eff = n_q if n_kv == 0 else n_kv
@@ -212,12 +217,13 @@ def make_workload(
 
     q = _randn_as((batch, n_q, qk_dim), DTYPES[q_dtype], vgen, dev)
 
-    if layout == LAYOUT_PAGED:
+    if layout in PAGED_LAYOUTS:
+        bsh = layout == LAYOUT_PAGED_BSH
         if max_blocks_per_seq is None:
             max_blocks_per_seq = max(1, max((L + block_size - 1) // block_size for L in lens))
         table, pool = paged_block_table(lens, block_size, max_blocks_per_seq, sgen, extra_blocks)
-        kshape = (pool, n_kv_eff, block_size, qk_dim)
-        vshape = (pool, n_kv_eff, block_size, v_dim)
+        kshape = (pool, block_size, n_kv_eff, qk_dim) if bsh else (pool, n_kv_eff, block_size, qk_dim)
+        vshape = (pool, block_size, n_kv_eff, v_dim) if bsh else (pool, n_kv_eff, block_size, v_dim)
         k_cache = _randn_as(kshape, kdt, vgen, dev)
         v_cache = k_cache if v_aliases_k else _randn_as(vshape, kdt, vgen, dev)
         if poison:
@@ -229,9 +235,11 @@ def make_workload(
                 used[blks] = True
                 if nb and L % block_size:
                     last = int(blks[-1])
-                    k_cache[last, :, L % block_size:, :] = pv
-                    if not v_aliases_k:
-                        v_cache[last, :, L % block_size:, :] = pv
+                    for c in (k_cache,) if v_aliases_k else (k_cache, v_cache):
+                        if bsh:
+                            c[last, L % block_size:] = pv
+                        else:
+                            c[last, :, L % block_size:] = pv
             unused = (~used).nonzero().flatten().to(dev)
             if unused.numel():
                 k_cache[unused] = pv
@@ -239,18 +247,23 @@ def make_workload(
                     v_cache[unused] = pv
         s_cap_eff = max_blocks_per_seq * block_size
         block_table = table.to(dev)
-    elif layout == LAYOUT_BNSD:
+    elif layout in (LAYOUT_BNSD, LAYOUT_BSND):
+        bsnd = layout == LAYOUT_BSND
         s_cap_eff = s_cap if s_cap is not None else max(1, max(lens))
         if max(lens) > s_cap_eff:
             raise ValueError("length exceeds s_cap")
-        k_cache = _randn_as((batch, n_kv_eff, s_cap_eff, qk_dim), kdt, vgen, dev)
-        v_cache = k_cache if v_aliases_k else _randn_as((batch, n_kv_eff, s_cap_eff, v_dim), kdt, vgen, dev)
+        kshape = (batch, s_cap_eff, n_kv_eff, qk_dim) if bsnd else (batch, n_kv_eff, s_cap_eff, qk_dim)
+        vshape = (batch, s_cap_eff, n_kv_eff, v_dim) if bsnd else (batch, n_kv_eff, s_cap_eff, v_dim)
+        k_cache = _randn_as(kshape, kdt, vgen, dev)
+        v_cache = k_cache if v_aliases_k else _randn_as(vshape, kdt, vgen, dev)
         if poison:
             pv = _poison_value(kdt)
             for b, L in enumerate(lens):
-                k_cache[b, :, L:, :] = pv
-                if not v_aliases_k:
-                    v_cache[b, :, L:, :] = pv
+                for c in (k_cache,) if v_aliases_k else (k_cache, v_cache):
+                    if bsnd:
+                        c[b, L:] = pv
+                    else:
+                        c[b, :, L:] = pv
         block_table = None
         block_size = 0
     else:
@@ -261,8 +274,9 @@ def make_workload(
     sink_t = torch.randn(n_q, generator=vgen, device=dev, dtype=torch.float32) if sink else None
     aq_s = aq_o = None
     if antiquant:
-        aq_s = torch.rand((2, n_kv_eff, qk_dim), generator=vgen, device=dev, dtype=torch.float32) * 0.02 + 0.02
-        aq_o = torch.rand((2, n_kv_eff, qk_dim), generator=vgen, device=dev, dtype=torch.float32) * 2.0 - 1.0
+        ashape = (2,) if antiquant_mode == "tensor" else (2, n_kv_eff, qk_dim)
+        aq_s = torch.rand(ashape, generator=vgen, device=dev, dtype=torch.float32) * 0.02 + 0.02
+        aq_o = torch.rand(ashape, generator=vgen, device=dev, dtype=torch.float32) * 2.0 - 1.0
     return Workload(
         name=name,
         q=q,

@@ -179,6 +179,85 @@ def test_paged_equals_contiguous(bs, lengths):
 
 
 # ---------------------------------------------------------------- P5
+@pytest.mark.parametrize("bs,lengths", [(16, [0, 1, 15, 16, 17, 40]), (32, [31, 32, 33, 100])])
+def test_token_major_layouts_equal_logical_kv(bs, lengths):
+    """aclnnIncreFlashAttentionV3 Constraints, page attention scenario (the
+    KV cache layouts (blocknum, blocksize, H) and (blocknum, KV_N,
+    blocksize, D)) and Parameters (BSND key/value): each token-major layout,
+    filled here element by element from one logical K/V[b][g][j][d] (reading
+    H = KV_N x D with head g in columns g D .. g D + D - 1), gives exactly
+    the attention of that logical K/V taken row by row in brute force."""
+    rng = np.random.default_rng(bs)
+    B, Nq, Nkv, D = len(lengths), 4, 2, 4
+    S = max(lengths) + 2
+    Kl, Vl = _rand(rng, B, Nkv, S, D), _rand(rng, B, Nkv, S, D)
+    q = _rand(rng, B, Nq, D)
+    scale = 0.5
+    # block pool (pool, bs, H) with a seeded permutation of blocks
+    nb = [(L + bs - 1) // bs for L in lengths]
+    pool = sum(nb) + 2
+    perm = rng.permutation(pool)
+    tab = np.full((B, max(max(nb), 1)), -1, dtype=np.int32)
+    kp, vp = np.full((pool, bs, Nkv * D), np.nan), np.full((pool, bs, Nkv * D), np.nan)
+    kc, vc = np.full((B, S, Nkv * D), np.nan), np.full((B, S, Nkv * D), np.nan)
+    used = 0
+    for b, L in enumerate(lengths):
+        for i in range(nb[b]):
+            tab[b, i] = perm[used]
+            used += 1
+        for j in range(L):
+            for g in range(Nkv):
+                for d in range(D):
+                    kp[tab[b, j // bs], j % bs, g * D + d] = Kl[b, g, j, d]
+                    vp[tab[b, j // bs], j % bs, g * D + d] = Vl[b, g, j, d]
+                    kc[b, j, g * D + d] = Kl[b, g, j, d]
+                    vc[b, j, g * D + d] = Vl[b, g, j, d]
+    lens = np.array(lengths)
+    o_p, l_p = oracle.decode(q, kp.reshape(pool, bs, Nkv, D), vp.reshape(pool, bs, Nkv, D), "paged_bsh", lens,
+                             Nkv, scale, block_table=tab, block_size=bs)
+    o_c, l_c = oracle.decode(q, kc.reshape(B, S, Nkv, D), vc.reshape(B, S, Nkv, D), "bsnd", lens, Nkv, scale)
+    for b, L in enumerate(lengths):
+        for h in range(Nq):
+            g = h // (Nq // Nkv)
+            for o, l in ((o_p, l_p), (o_c, l_c)):
+                if L:
+                    ref, ref_lse = _bruteforce_row(q[b, h], Kl[b, g, :L].tolist(), Vl[b, g, :L].tolist(), scale)
+                    np.testing.assert_allclose(o[b, h], ref, rtol=0, atol=1e-12)
+                    assert abs(l[b, h] - ref_lse) < 1e-12
+                else:  # empty sequence: zero output, lse -inf
+                    assert np.all(o[b, h] == 0) and l[b, h] == -np.inf
+
+
+def test_per_tensor_antiquant_is_per_channel_with_constant_vectors():
+    """aclnnIncreFlashAttentionV3 Constraints on antiquantScale and
+    antiquantOffset: per-tensor mode has shape (2), entry 0 for K and entry 1
+    for V, the per-channel mode (2, N, D) otherwise.  A per-tensor pair
+    (s_K, o_K), (s_V, o_V) equals the per-channel parameters that repeat
+    them over every head and channel, and with the V entries set to the
+    identity it changes the output only through K (distinct K and V values,
+    so a swapped index fails)."""
+    w = make_workload(batch=2, n_q=4, n_kv=2, qk_dim=16, kv_dtype="i8", layout="paged",
+                      block_size=32, lengths=[40, 70], seed=19, antiquant_mode="tensor")
+    assert tuple(w.antiquant_scale.shape) == (2,)
+    kw = dict(block_table=w.block_table, block_size=32)
+    sc, off = w.antiquant_scale, w.antiquant_offset
+    full_s = torch.empty((2, 2, 16)); full_o = torch.empty((2, 2, 16))
+    for i in range(2):
+        full_s[i] = float(sc[i]); full_o[i] = float(off[i])
+    o_t, l_t = oracle.decode(w.q, w.k_cache, w.v_cache, "paged", w.seq_lens, 2, w.scale,
+                             antiquant_scale=sc, antiquant_offset=off, **kw)
+    o_c, l_c = oracle.decode(w.q, w.k_cache, w.v_cache, "paged", w.seq_lens, 2, w.scale,
+                             antiquant_scale=full_s, antiquant_offset=full_o, **kw)
+    np.testing.assert_allclose(o_t, o_c, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l_t, l_c, rtol=0, atol=1e-12)
+    # V side identity: out is the attention of dequantised K over the raw V bytes
+    sv = sc.clone(); sv[1] = 1.0
+    ov = off.clone(); ov[1] = 0.0
+    o_k, _ = oracle.decode(w.q, w.k_cache, w.v_cache, "paged", w.seq_lens, 2, w.scale,
+                           antiquant_scale=sv, antiquant_offset=ov, **kw)
+    np.testing.assert_allclose(o_t, float(sc[1]) * (o_k + float(off[1])), rtol=0, atol=1e-10)
+
+
 def test_token_permutation_invariance():
     """Attention is a sum over KV tokens: permuting (K_j, V_j) jointly changes nothing."""
     rng = np.random.default_rng(21)
@@ -416,10 +495,12 @@ def test_planted_mistakes_are_caught(monkeypatch):
         for name, fn in [("bruteforce", lambda: test_bruteforce_tiny(1)),
                          ("split", lambda: test_split_invariance_merge_equals_full(0)),
                          ("sink", lambda: test_sink_closed_form(8.0)),
-                         ("paged", lambda: test_paged_equals_contiguous(16, [1, 15, 16, 17, 40]))]:
+                         ("paged", lambda: test_paged_equals_contiguous(16, [1, 15, 16, 17, 40])),
+                         ("token-major", lambda: test_token_major_layouts_equal_logical_kv(16, [0, 1, 15, 16, 17, 40])),
+                         ("per-tensor", test_per_tensor_antiquant_is_per_channel_with_constant_vectors)]:
             try:
                 fn()
-            except AssertionError:
+            except (AssertionError, IndexError):  # a wrong index may also fall outside the cache
                 failed.append(name)
         return failed
 
@@ -442,12 +523,32 @@ def test_planted_mistakes_are_caught(monkeypatch):
     def wrong_head(cache, layout, b, g, length, block_table=None, block_size=0, dim=None):
         return orig_gather(cache, layout, b, (g + 1) % cache.shape[1], length, block_table, block_size, dim)
 
+    def token_major_read_as_head_major(cache, layout, b, g, length, block_table=None, block_size=0, dim=None):
+        if layout == "paged_bsh":  # the same memory taken as (blocknum, KV_N, blocksize, D)
+            n, bs, nkv, d = cache.shape
+            return orig_gather(cache.reshape(n, nkv, bs, d), "paged", b, g, length, block_table, block_size, dim)
+        if layout == "bsnd":
+            bb, sc, nkv, d = cache.shape
+            return orig_gather(cache.reshape(bb, nkv, sc, d), "bnsd", b, g, length, block_table, block_size, dim)
+        return orig_gather(cache, layout, b, g, length, block_table, block_size, dim)
+
+    orig_kv_rows = attn_ref._kv_rows
+
+    def per_tensor_k_v_swapped(k_cache, v_cache, layout, b, g, L, block_table, block_size, qk_dim, v_dim, v_from_k,
+                               aq_scale, aq_offset):
+        if aq_scale is not None and aq_scale.ndim == 1:
+            aq_scale, aq_offset = aq_scale[::-1].copy(), aq_offset[::-1].copy()
+        return orig_kv_rows(k_cache, v_cache, layout, b, g, L, block_table, block_size, qk_dim, v_dim, v_from_k,
+                            aq_scale, aq_offset)
+
     slips = [("attention_row", no_scale), ("attention_row", sink_in_numerator),
              ("attention_row", transposed), ("merge", unweighted_merge),
-             ("gather_kv", wrong_batch_row), ("gather_kv", wrong_head)]
+             ("gather_kv", wrong_batch_row), ("gather_kv", wrong_head),
+             ("gather_kv", token_major_read_as_head_major), ("_kv_rows", per_tensor_k_v_swapped)]
     for fn_name, bad in slips:
         with monkeypatch.context() as mp:
             mp.setattr(attn_ref, fn_name, bad)
-            mp.setattr(oracle, fn_name, bad)
+            if hasattr(oracle, fn_name):
+                mp.setattr(oracle, fn_name, bad)
             assert run_pins(), f"planted slip {bad.__name__} went unnoticed"
     assert run_pins() == []
