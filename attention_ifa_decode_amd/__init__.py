@@ -13,8 +13,11 @@ call raises.
 
 Layouts: q (B, N_q, D); paged KV pools (num_blocks, N_kv, block_size, D)
 with block_table int32 (B, max_blocks_per_seq); or, with block_table None,
-contiguous padded KV (B, N_kv, S_cap, D).  For the MLA shape pass the same
-tensor as k_cache and v_cache and ``v_dim=512``.
+contiguous padded KV (B, N_kv, S_cap, D).  ``kv_layout="paged_bsh"`` takes
+pools (num_blocks, block_size, N_kv * D) and ``kv_layout="bsnd"`` contiguous
+(B, S_cap, N_kv * D).  Antiquant parameters of shape (2,) are per tensor.
+For the MLA shape pass the same tensor as k_cache and v_cache and
+``v_dim=512``.
 """
 
 from __future__ import annotations
@@ -35,7 +38,9 @@ IFA_ERR_RUNTIME = 361001
 IFA_ERR_PLAN = 561002
 
 IFA_F32, IFA_F16, IFA_BF16, IFA_I8 = 0, 1, 2, 3
-IFA_KV_BNSD, IFA_KV_PAGED = 0, 1
+IFA_KV_BNSD, IFA_KV_PAGED, IFA_KV_PAGED_BSH, IFA_KV_BSND = 0, 1, 2, 3
+IFA_ANTIQUANT_PER_CHANNEL, IFA_ANTIQUANT_PER_TENSOR = 0, 1
+_LAYOUT_CODE = {"bnsd": IFA_KV_BNSD, "paged": IFA_KV_PAGED, "paged_bsh": IFA_KV_PAGED_BSH, "bsnd": IFA_KV_BSND}
 
 _DTYPE_CODE = {torch.float32: IFA_F32, torch.float16: IFA_F16, torch.bfloat16: IFA_BF16, torch.int8: IFA_I8}
 
@@ -86,7 +91,7 @@ class DecodeArgs(ctypes.Structure):
         ("out_dtype", ctypes.c_int32),
         ("kv_layout", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("antiquant_mode", ctypes.c_int32),
     ]
 
 
@@ -159,7 +164,8 @@ class DecodeCall:
     def __init__(self, q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads: int,
                  num_key_value_heads: int, scale_value: float, learnable_sink=None, antiquant_scale=None,
                  antiquant_offset=None, num_splits: int = 0, v_dim: Optional[int] = None,
-                 out_dtype: Optional[torch.dtype] = None, with_lse: bool = True, out=None, lse=None):
+                 out_dtype: Optional[torch.dtype] = None, with_lse: bool = True, out=None, lse=None,
+                 kv_layout: Optional[str] = None):
         lib = load_library()
         _need(q, "q")
         _need(k_cache, "k_cache")
@@ -171,14 +177,22 @@ class DecodeCall:
         alias = v_cache.data_ptr() == k_cache.data_ptr()
         if v_dim is None:
             v_dim = qk_dim if alias else v_cache.shape[-1]
-        paged = block_table is not None
+        # cache shapes: "paged" (blocks, N_kv, block_size, D), "paged_bsh"
+        # (blocks, block_size, N_kv, D) or (blocks, block_size, H), "bnsd"
+        # (B, N_kv, S, D), "bsnd" (B, S, N_kv, D) or (B, S, H)
+        if kv_layout is None:
+            kv_layout = "paged" if block_table is not None else "bnsd"
+        if kv_layout not in _LAYOUT_CODE:
+            raise ValueError(f"unknown kv_layout {kv_layout!r}")
+        paged = kv_layout in ("paged", "paged_bsh")
         if paged:
             _need(block_table, "block_table", torch.int32)
-            num_blocks, _, block_size, _ = k_cache.shape
+            num_blocks = k_cache.shape[0]
+            block_size = k_cache.shape[2] if kv_layout == "paged" else k_cache.shape[1]
             max_blocks = block_table.shape[1]
             s_cap = 0
         else:
-            _, _, s_cap, _ = k_cache.shape
+            s_cap = k_cache.shape[2] if kv_layout == "bnsd" else k_cache.shape[1]
             num_blocks = block_size = max_blocks = 0
         for t, nm in ((learnable_sink, "learnable_sink"), (antiquant_scale, "antiquant_scale"),
                       (antiquant_offset, "antiquant_offset")):
@@ -213,9 +227,10 @@ class DecodeCall:
         a.q_dtype = _DTYPE_CODE[q.dtype]
         a.kv_dtype = _DTYPE_CODE[k_cache.dtype]
         a.out_dtype = _DTYPE_CODE[out_dtype]
-        a.kv_layout = IFA_KV_PAGED if paged else IFA_KV_BNSD
+        a.kv_layout = _LAYOUT_CODE[kv_layout]
         a.num_splits = int(num_splits)
-        a.reserved = 0
+        a.antiquant_mode = (IFA_ANTIQUANT_PER_TENSOR if antiquant_scale is not None and antiquant_scale.dim() == 1
+                            else IFA_ANTIQUANT_PER_CHANNEL)
         self.args = a
         sz = ctypes.c_size_t(0)
         _check(lib.ifa_decode_workspace_size(ctypes.byref(a), ctypes.byref(sz)))
@@ -270,11 +285,14 @@ class DecodeCall:
 def decode(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads: int, num_key_value_heads: int,
            scale_value: float, learnable_sink=None, antiquant_scale=None, antiquant_offset=None,
            num_splits: int = 0, v_dim: Optional[int] = None,
-           out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Decode attention; returns (attention_out (B, N_q, v_dim), softmax_lse (B, N_q) fp32)."""
+           out_dtype: Optional[torch.dtype] = None, kv_layout: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Decode attention; returns (attention_out (B, N_q, v_dim), softmax_lse (B, N_q) fp32).
+    kv_layout: "paged" (default with a block table), "paged_bsh", "bnsd"
+    (default without one) or "bsnd"; antiquant parameters of shape (2,) are
+    per tensor."""
     call = DecodeCall(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads, num_key_value_heads,
                       scale_value, learnable_sink, antiquant_scale, antiquant_offset, num_splits, v_dim,
-                      out_dtype)
+                      out_dtype, kv_layout=kv_layout)
     out, lse = call.run()
     # the workspace must outlive the queued kernels: the caching allocator
     # keeps it reserved for this stream
@@ -322,7 +340,7 @@ def decode_workload(w, num_splits: Optional[int] = None, **kw):
     return decode(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.n_q, w.n_kv, w.scale,
                   learnable_sink=w.sink, antiquant_scale=w.antiquant_scale, antiquant_offset=w.antiquant_offset,
                   num_splits=w.num_splits if num_splits is None else num_splits,
-                  v_dim=w.v_dim, out_dtype=w.out_dtype, **kw)
+                  v_dim=w.v_dim, out_dtype=w.out_dtype, kv_layout=w.layout, **kw)
 
 
 def call_for_workload(w, num_splits: Optional[int] = None, **kw) -> DecodeCall:
@@ -330,4 +348,4 @@ def call_for_workload(w, num_splits: Optional[int] = None, **kw) -> DecodeCall:
                       learnable_sink=w.sink, antiquant_scale=w.antiquant_scale,
                       antiquant_offset=w.antiquant_offset,
                       num_splits=w.num_splits if num_splits is None else num_splits, v_dim=w.v_dim,
-                      out_dtype=w.out_dtype, **kw)
+                      out_dtype=w.out_dtype, kv_layout=w.layout, **kw)

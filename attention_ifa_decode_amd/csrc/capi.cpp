@@ -77,8 +77,12 @@ int auto_splits_gqa(const ifa_decode_args* a, int64_t n_kv, int group, int gh, i
 
 // Fewest splits for which one split of the longest sequence touches at most
 // kMlaMaxTableSlice block-table entries (paged layout).
+bool is_paged(int layout) { return layout == IFA_KV_PAGED || layout == IFA_KV_PAGED_BSH; }
+// token-major layouts: consecutive tokens of one KV head are N_kv rows apart
+bool is_token_major(int layout) { return layout == IFA_KV_PAGED_BSH || layout == IFA_KV_BSND; }
+
 int64_t min_splits_mla(const ifa_decode_args* a, int64_t max_len) {
-  if (a->kv_layout != IFA_KV_PAGED) return 1;
+  if (!is_paged(a->kv_layout)) return 1;
   for (int64_t n = 1; n <= kMaxSplits; ++n)
     if (ifa::split_chunk(max_len, (int)n) <= (int64_t)(ifa::kMlaMaxTableSlice - 2) * a->block_size) return n;
   return kMaxSplits + 1;
@@ -99,7 +103,6 @@ int auto_splits_mla(const ifa_decode_args* a, int64_t max_len) {
 
 ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
   if (!a) return fail(IFA_ERR_PARAM_NULLPTR, "args is NULL");
-  if (a->reserved != 0) return fail(IFA_ERR_PARAM_INVALID, "reserved field must be 0");
   if (a->batch < 0 || a->batch > kMaxBatch)
     return fail(IFA_ERR_PARAM_INVALID, "batch %lld outside [0, %lld]", (long long)a->batch, (long long)kMaxBatch);
   if (a->num_heads < 1 || a->num_heads > kMaxHeads)
@@ -116,6 +119,10 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
   if (a->kv_dtype == IFA_I8) {
     if (a->antiquant_scale == nullptr || a->antiquant_offset == nullptr)
       return fail(IFA_ERR_PARAM_NULLPTR, "int8 KV needs antiquant_scale and antiquant_offset");
+    if (a->antiquant_mode != IFA_ANTIQUANT_PER_CHANNEL && a->antiquant_mode != IFA_ANTIQUANT_PER_TENSOR)
+      return fail(IFA_ERR_PARAM_INVALID, "antiquant_mode %d not supported", a->antiquant_mode);
+  } else if (a->antiquant_mode != 0) {
+    return fail(IFA_ERR_PARAM_INVALID, "antiquant_mode is set for a non-int8 KV cache");
   } else if (!is_float_dtype(a->kv_dtype)) {
     return fail(IFA_ERR_PARAM_INVALID, "kv_dtype %d not supported", a->kv_dtype);
   } else if (a->kv_dtype != a->q_dtype) {
@@ -123,7 +130,8 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
   } else if (a->antiquant_scale || a->antiquant_offset) {
     return fail(IFA_ERR_PARAM_INVALID, "antiquant parameters given for a non-int8 KV cache");
   }
-  if (a->kv_layout != IFA_KV_BNSD && a->kv_layout != IFA_KV_PAGED)
+  if (a->kv_layout != IFA_KV_BNSD && a->kv_layout != IFA_KV_PAGED && a->kv_layout != IFA_KV_PAGED_BSH &&
+      a->kv_layout != IFA_KV_BSND)
     return fail(IFA_ERR_PARAM_INVALID, "kv_layout %d not supported", a->kv_layout);
   if (a->num_splits < 0 || a->num_splits > kMaxSplits)
     return fail(IFA_ERR_PARAM_INVALID, "num_splits %d outside [0, %d]", a->num_splits, kMaxSplits);
@@ -148,7 +156,7 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
   }
 
   int64_t max_len = 0;
-  if (a->kv_layout == IFA_KV_PAGED) {
+  if (is_paged(a->kv_layout)) {
     const int align = a->kv_dtype == IFA_I8 ? 32 : 16;
     if (a->block_size < 16 || a->block_size > 1024 || a->block_size % align)
       return fail(IFA_ERR_PARAM_INVALID, "block_size %lld must be a multiple of %d in [16, 1024]",
@@ -175,7 +183,7 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
     if (!a->value_cache) return fail(IFA_ERR_PARAM_NULLPTR, "value_cache is NULL");
     if (!a->actual_seq_lengths) return fail(IFA_ERR_PARAM_NULLPTR, "actual_seq_lengths is NULL");
     if (!a->attention_out) return fail(IFA_ERR_PARAM_NULLPTR, "attention_out is NULL");
-    if (a->kv_layout == IFA_KV_PAGED && !a->block_table)
+    if (is_paged(a->kv_layout) && !a->block_table)
       return fail(IFA_ERR_PARAM_NULLPTR, "block_table is NULL in the paged layout");
   }
 
@@ -229,7 +237,7 @@ ifa_status runtime(hipError_t e, const char* what) {
 ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStream_t stream,
                        const ifa::LaunchEvents* ev = nullptr) {
   char* w = static_cast<char*>(ws);
-  const int64_t max_len = a->kv_layout == IFA_KV_PAGED ? a->max_blocks_per_seq * a->block_size : a->s_cap;
+  const int64_t max_len = is_paged(a->kv_layout) ? a->max_blocks_per_seq * a->block_size : a->s_cap;
   // Longest-first order for batches of up to 256 sequences.  The int8-KV GQA
   // kernel, with twice the workgroups and each one's start not hidden behind
   // streaming, takes it from a planning kernel launched first; the 16-bit GQA
@@ -267,7 +275,13 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
     L.block_size = (int)a->block_size;
     L.max_blocks = (int)a->max_blocks_per_seq;
     L.num_blocks = (int)a->num_blocks;
-    L.paged = a->kv_layout == IFA_KV_PAGED;
+    L.paged = is_paged(a->kv_layout);
+    L.token_major = is_token_major(a->kv_layout);
+    // antiquant parameter strides (entries; K/V index, KV head, channel)
+    const bool per_tensor = a->antiquant_mode == IFA_ANTIQUANT_PER_TENSOR;
+    L.aq_stride_kv = per_tensor ? 1 : (int)(p.n_kv * a->qk_dim);
+    L.aq_stride_g = per_tensor ? 0 : (int)a->qk_dim;
+    L.aq_stride_d = per_tensor ? 0 : 1;
     L.scale_log2 = scale_log2;
     if (L.paged) ifa::make_divisor((uint32_t)a->block_size, &L.bs_magic, &L.bs_shift);
     L.plan = plan;
@@ -293,11 +307,12 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
   M.max_blocks = (int)a->max_blocks_per_seq;
   M.num_blocks = (int)a->num_blocks;
   M.scale_log2 = scale_log2;
-  if (a->kv_layout == IFA_KV_PAGED) ifa::make_divisor((uint32_t)a->block_size, &M.bs_magic, &M.bs_shift);
+  // one KV head: the token-major layouts address exactly as the head-major ones
+  if (is_paged(a->kv_layout)) ifa::make_divisor((uint32_t)a->block_size, &M.bs_magic, &M.bs_shift);
   M.longest_first = longest_first;
   M.qk_dim = (int)a->qk_dim;
   M.v_dim = (int)a->v_dim;
-  M.paged = a->kv_layout == IFA_KV_PAGED;
+  M.paged = is_paged(a->kv_layout);
   return runtime(ifa::launch_mla_splitkv(M, stream, ev), "MLA split-KV decode launch");
 }
 
@@ -316,7 +331,7 @@ ifa_status run_combine(const ifa_decode_args* a, const Plan& p, const void* ws, 
   C.n_split = p.n_split;
   C.v_dim = (int)a->v_dim;
   C.out_dtype = a->out_dtype;
-  C.s_cap = a->kv_layout == IFA_KV_PAGED ? a->max_blocks_per_seq * a->block_size : a->s_cap;
+  C.s_cap = is_paged(a->kv_layout) ? a->max_blocks_per_seq * a->block_size : a->s_cap;
   return runtime(ifa::launch_combine(C, stream), "combine launch");
 }
 

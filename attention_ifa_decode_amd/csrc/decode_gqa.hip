@@ -269,12 +269,18 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
       const uint32_t k = bi - bi0;
       int blk = k < 64 ? __builtin_amdgcn_readlane(tbl, k) : ld_uniform(a.block_table, (int64_t)b * a.max_blocks + bi);
       blk = blk < 0 ? 0 : (blk >= a.num_blocks ? a.num_blocks - 1 : blk);
-      return ((uint32_t)blk * (uint32_t)a.n_kv + (uint32_t)g) * (uint32_t)a.block_size + (uint32_t)j0 -
-             bi * (uint32_t)a.block_size;
+      const uint32_t slot = (uint32_t)j0 - bi * (uint32_t)a.block_size;
+      if (a.token_major)  // (blocks, block_size, N_kv, D)
+        return ((uint32_t)blk * (uint32_t)a.block_size + slot) * (uint32_t)a.n_kv + (uint32_t)g;
+      return ((uint32_t)blk * (uint32_t)a.n_kv + (uint32_t)g) * (uint32_t)a.block_size + slot;
     } else {
+      if (a.token_major)  // (B, s_cap, N_kv, D)
+        return ((uint32_t)b * (uint32_t)a.s_cap + (uint32_t)j0) * (uint32_t)a.n_kv + (uint32_t)g;
       return ((uint32_t)b * (uint32_t)a.n_kv + (uint32_t)g) * (uint32_t)a.s_cap + (uint32_t)j0;
     }
   };
+  // bytes between consecutive tokens of one KV head
+  const uint32_t tok_bytes = a.token_major ? (uint32_t)a.n_kv * ROWB : (uint32_t)ROWB;
 
   // Queue the direct-to-LDS loads of step `st` (< nsteps) into ring stage
   // `slot`.  Lanes past the split's end read its last valid row: finite data
@@ -282,7 +288,7 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   auto issue = [&](int st, int slot) {
     const uint32_t row0 = step_row(st);
     const int r = min(t, end - 1 - (start + TOK * st));
-    const uint32_t off = (uint32_t)r * ROWB + 16u * c;
+    const uint32_t off = (uint32_t)r * tok_bytes + 16u * c;
     const char* kb = kbase + (uint64_t)row0 * ROWB;
     const char* vb = vbase + (uint64_t)row0 * ROWB;
     const uint32_t dst = ring_lds + slot * S::STEP_BYTES;
@@ -345,15 +351,17 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
           if (e & 1) qp[h][e >> 1] |= bits << 16; else qp[h][e >> 1] = bits;
         } else if constexpr (I8DOT) {
           // x_hat = (x + offset) * scale with x = f - 1152, f = 1024 + (x ^ 0x80)
-          const _Float16 qh = (_Float16)(load_as_f32<QT>(a.q, qrow + d) * a.aq_scale[(int64_t)g * D + d]);
-          part = fmaf((float)qh, a.aq_offset[(int64_t)g * D + d] - 1152.f, part);
+          const int kq = g * a.aq_stride_g + d * a.aq_stride_d;  // K parameters (index 0)
+          const _Float16 qh = (_Float16)(load_as_f32<QT>(a.q, qrow + d) * a.aq_scale[kq]);
+          part = fmaf((float)qh, a.aq_offset[kq] - 1152.f, part);
           const uint32_t bits = __builtin_bit_cast(uint16_t, qh);
           if (e & 1) qp[h][e >> 1] |= bits << 16; else qp[h][e >> 1] = bits;
         } else {
           float qv = load_as_f32<QT>(a.q, qrow + d);
           if constexpr (KV == kI8) {
-            qv *= a.aq_scale[(int64_t)g * D + d];
-            part = fmaf(qv, a.aq_offset[(int64_t)g * D + d] - 128.f, part);
+            const int kq = g * a.aq_stride_g + d * a.aq_stride_d;
+            qv *= a.aq_scale[kq];
+            part = fmaf(qv, a.aq_offset[kq] - 128.f, part);
           }
           qf[h][e] = qv;
         }
@@ -635,10 +643,12 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
     o.x *= inv, o.y *= inv, o.z *= inv, o.w *= inv;
     if constexpr (KV == kI8) {
       // P V ran on (1024 + byte ^ 0x80): x_hat = (byte + offset) * scale
-      const float* vsc = a.aq_scale + ((int64_t)a.n_kv + g) * D + d;  // V parameters (index 1)
-      const float* vof = a.aq_offset + ((int64_t)a.n_kv + g) * D + d;
-      o.x = vsc[0] * (o.x - 1152.f + vof[0]), o.y = vsc[1] * (o.y - 1152.f + vof[1]);
-      o.z = vsc[2] * (o.z - 1152.f + vof[2]), o.w = vsc[3] * (o.w - 1152.f + vof[3]);
+      const int vq = a.aq_stride_kv + g * a.aq_stride_g + d * a.aq_stride_d;  // V parameters (index 1)
+      const int sd = a.aq_stride_d;
+      const float* vsc = a.aq_scale + vq;
+      const float* vof = a.aq_offset + vq;
+      o.x = vsc[0] * (o.x - 1152.f + vof[0]), o.y = vsc[sd] * (o.y - 1152.f + vof[sd]);
+      o.z = vsc[2 * sd] * (o.z - 1152.f + vof[2 * sd]), o.w = vsc[3 * sd] * (o.w - 1152.f + vof[3 * sd]);
     }
     const int64_t row = (int64_t)b * a.n_q + h0 + h;
     *reinterpret_cast<float4*>(a.ws_o + (row * a.n_split + split) * D + d) = o;

@@ -14,8 +14,11 @@ struct GqaLaunch {
   const void* v;
   const int32_t* block_table;
   const int64_t* seq_lens;
-  const float* aq_scale;   // (2, n_kv, D) or null
-  const float* aq_offset;  // (2, n_kv, D) or null
+  const float* aq_scale;   // (2, n_kv, D) or (2), or null
+  const float* aq_offset;  // the shape of aq_scale
+  // entry (i, g, d) of the parameters, i = 0 for K and 1 for V:
+  // i * aq_stride_kv + g * aq_stride_g + d * aq_stride_d
+  int aq_stride_kv, aq_stride_g, aq_stride_d;
   float* ws_o;             // [B][n_q][n_split][D]
   float* ws_m;             // [B][n_q][n_split]
   float* ws_l;             // [B][n_q][n_split]
@@ -26,6 +29,7 @@ struct GqaLaunch {
   float scale_log2;        // scale * log2(e)
   int q_dtype, kv_dtype, head_dim;
   bool paged;
+  bool token_major;        // (blocks, block_size, N_kv, D) / (B, s_cap, N_kv, D) instead of head-major
   const int2* plan;        // [batch] (sequence, clamped length) in longest-first order, or null
   bool longest_first;      // without a plan: each workgroup ranks the lengths itself
 };

@@ -1,14 +1,16 @@
 """Benchmark: paged decode attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
-                    [--num-splits N] [--no-cpu-baseline]
+                    [--num-splits N] [--kv-layout L] [--no-cpu-baseline]
 
 One step = one pass of the whole path over one batch: the split-KV decode
 kernel (block-table gather, QK^T, online softmax, PV, partial triples) and the
 combine kernel (n-way merge, sink, output cast, lse).  Inputs are synthetic,
 seeded and resident in HBM before timing starts.  The default workload is the
 paged bf16 GQA decode: B=64, N_q=32, N_kv=8, D=128, block size 128, lengths
-U[512, 8192], 4 KV splits.
+U[512, 8192], 4 KV splits.  ``--kv-layout`` measures the same workload with
+its cache in another layout (paged_bsh: (blocknum, blocksize, H) pool; bsnd:
+contiguous (B, S, H)).
 
 Prints one JSON line.  ``value`` is KV-cache GB/s: the bytes of K and V that
 belong to valid tokens, per step, divided by the step time.  ``roofline``
@@ -124,6 +126,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--num-splits", type=int, default=None)
+    ap.add_argument("--kv-layout", default=None, choices=["paged", "paged_bsh", "bnsd", "bsnd"],
+                    help="cache layout instead of the config's own (paged <-> paged_bsh, bnsd <-> bsnd)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -150,11 +154,12 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    w = config_workload(args.config, seed=args.seed, device=dev)
+    over = {} if args.kv_layout is None else {"layout": args.kv_layout}
+    w = config_workload(args.config, seed=args.seed, device=dev, **over)
     kv_bytes = w.kv_bytes()
     # enough independent copies that the 256 MB infinity cache never serves KV
     copies = 1 if kv_bytes > 3 * MALL_BYTES else min(4, -(-3 * MALL_BYTES // max(kv_bytes, 1)))
-    works = [w] + [config_workload(args.config, seed=(args.seed or 1000 + args.config) + 17 * i, device=dev)
+    works = [w] + [config_workload(args.config, seed=(args.seed or 1000 + args.config) + 17 * i, device=dev, **over)
                    for i in range(1, copies)]
     for x in works[1:]:  # same lengths and table, fresh values
         x.seq_lens.copy_(w.seq_lens)
@@ -194,7 +199,7 @@ def main():
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     # algorithmic flops: QK^T and PV for every valid token and query head
     flops = sum(w.lengths()) * w.n_q * 2 * (w.qk_dim + w.v_dim)
-    traffic = read_traffic(args.config)
+    traffic = read_traffic(args.config) if args.kv_layout is None else None
     dtype_name = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}
     lens = w.lengths()
     result = {

@@ -78,8 +78,21 @@ typedef enum {
   /* paged pool (num_blocks, N_kv, block_size, D): token j of batch b, KV
    * head g in block blk = block_table[b * max_blocks_per_seq + j / block_size]
    * at ((blk * N_kv + g) * block_size + j % block_size) * D */
-  IFA_KV_PAGED = 1
+  IFA_KV_PAGED = 1,
+  /* paged pool (num_blocks, block_size, H), H = N_kv * D, the other layout of
+   * aclnnIncreFlashAttentionV3 "Constraints" (page attention scenario): head
+   * g holds columns g * D .. g * D + D - 1 of H, so token j of batch b, KV
+   * head g is at ((blk * block_size + j % block_size) * N_kv + g) * D */
+  IFA_KV_PAGED_BSH = 2,
+  /* contiguous, padded (B, s_cap, H), the BSH / BSND key and value layouts
+   * of the same page's "Parameters": ((b * s_cap + j) * N_kv + g) * D */
+  IFA_KV_BSND = 3
 } ifa_kv_layout;
+
+/* Antiquant parameter shapes (aclnnIncreFlashAttentionV3 "Constraints" on
+ * antiquantScale and antiquantOffset): per channel (2, N_kv, qk_dim), or per
+ * tensor (2); index 0 applies to K, 1 to V. */
+typedef enum { IFA_ANTIQUANT_PER_CHANNEL = 0, IFA_ANTIQUANT_PER_TENSOR = 1 } ifa_antiquant_mode;
 
 /* Arguments of one decode call.  Element strides are implied by the shapes;
  * every tensor is dense and row-major as described. */
@@ -88,11 +101,11 @@ typedef struct {
   const void* key_cache;      /* layout per kv_layout, row length qk_dim, kv_dtype */
   const void* value_cache;    /* row length v_dim; MAY EQUAL key_cache, then V is
                                  the first v_dim channels of each key row (MLA) */
-  const int32_t* block_table; /* (B, max_blocks_per_seq), IFA_KV_PAGED only */
+  const int32_t* block_table; /* (B, max_blocks_per_seq), the paged layouts only */
   const int64_t* actual_seq_lengths; /* (B), device; values in [0, s_cap] */
   const float* learnable_sink;       /* (N_q) or NULL */
-  const float* antiquant_scale;      /* (2, N_kv, qk_dim) fp32; required iff kv_dtype is IFA_I8 */
-  const float* antiquant_offset;     /* (2, N_kv, qk_dim) fp32; required iff kv_dtype is IFA_I8 */
+  const float* antiquant_scale;      /* fp32, shape per antiquant_mode; required iff kv_dtype is IFA_I8 */
+  const float* antiquant_offset;     /* fp32, the shape of antiquant_scale; required iff kv_dtype is IFA_I8 */
   void* attention_out;               /* (B, N_q, v_dim), out_dtype */
   float* softmax_lse;                /* (B, N_q) fp32, or NULL */
   int64_t batch;                     /* B >= 0; B == 0 is a no-op */
@@ -100,17 +113,17 @@ typedef struct {
   int64_t num_key_value_heads;       /* N_kv; 0 means N_q; N_q % N_kv == 0 */
   int64_t qk_dim;                    /* 64, 128, or 576 (MLA) */
   int64_t v_dim;                     /* == qk_dim, or 512 with qk_dim 576 (MLA) */
-  int64_t block_size;                /* IFA_KV_PAGED: multiple of 16 (32 for int8), 16..1024 */
-  int64_t max_blocks_per_seq;        /* IFA_KV_PAGED: second dim of block_table */
-  int64_t num_blocks;                /* IFA_KV_PAGED: pool size; block ids are clamped to it */
-  int64_t s_cap;                     /* IFA_KV_BNSD: padded length; lengths are clamped to it */
+  int64_t block_size;                /* paged: multiple of 16 (32 for int8), 16..1024 */
+  int64_t max_blocks_per_seq;        /* paged: second dim of block_table */
+  int64_t num_blocks;                /* paged: pool size; block ids are clamped to it */
+  int64_t s_cap;                     /* contiguous: padded length; lengths are clamped to it */
   double scale_value;                /* usually 1/sqrt(d) */
   int32_t q_dtype;                   /* IFA_F32 / IFA_F16 / IFA_BF16 */
   int32_t kv_dtype;                  /* == q_dtype, or IFA_I8 */
   int32_t out_dtype;                 /* IFA_F32 / IFA_F16 / IFA_BF16 */
   int32_t kv_layout;                 /* ifa_kv_layout */
   int32_t num_splits;                /* KV-axis splits per sequence, 1..256; 0 = auto */
-  int32_t reserved;                  /* must be 0 */
+  int32_t antiquant_mode;            /* ifa_antiquant_mode; 0 unless kv_dtype is IFA_I8 */
 } ifa_decode_args;
 
 /* Phase 1 (aclnnIncreFlashAttentionV3GetWorkspaceSize): validate `args` and

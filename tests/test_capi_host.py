@@ -115,7 +115,7 @@ def test_batch_zero_needs_no_workspace():
     ("kv_layout", 5, ifa.IFA_ERR_PARAM_INVALID),
     ("num_splits", -1, ifa.IFA_ERR_PARAM_INVALID),
     ("num_splits", 300, ifa.IFA_ERR_PARAM_INVALID),
-    ("reserved", 1, ifa.IFA_ERR_PARAM_INVALID),
+    ("antiquant_mode", 1, ifa.IFA_ERR_PARAM_INVALID),          # set for a bf16 cache
     ("scale_value", float("nan"), ifa.IFA_ERR_PARAM_INVALID),
     ("max_blocks_per_seq", 0, ifa.IFA_ERR_PARAM_INVALID),
 ])
@@ -133,6 +133,25 @@ def test_int8_rules():
     assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_NULLPTR  # antiquant parameters missing
     a = base_args(kv_dtype=ifa.IFA_I8, antiquant_scale=FAKE, antiquant_offset=FAKE)
     assert ws_size(a)[0] == ifa.IFA_OK
+    a = base_args(kv_dtype=ifa.IFA_I8, antiquant_scale=FAKE, antiquant_offset=FAKE,
+                  antiquant_mode=ifa.IFA_ANTIQUANT_PER_TENSOR)
+    assert ws_size(a)[0] == ifa.IFA_OK
+    a = base_args(kv_dtype=ifa.IFA_I8, antiquant_scale=FAKE, antiquant_offset=FAKE, antiquant_mode=2)
+    assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_INVALID
+
+
+@pytest.mark.parametrize("layout", [ifa.IFA_KV_PAGED_BSH, ifa.IFA_KV_BSND])
+def test_token_major_layouts_plan_like_head_major(layout):
+    """The token-major layouts take the same arguments as their head-major
+    twins (paged: block table, block size, pool; contiguous: s_cap) and give
+    the same workspace."""
+    twin = ifa.IFA_KV_PAGED if layout == ifa.IFA_KV_PAGED_BSH else ifa.IFA_KV_BNSD
+    extra = {} if twin == ifa.IFA_KV_PAGED else dict(block_table=0, s_cap=4096)
+    a, b = base_args(kv_layout=layout, **extra), base_args(kv_layout=twin, **extra)
+    sa, sb = ws_size(a), ws_size(b)
+    assert sa[0] == ifa.IFA_OK and sa == sb, (sa, sb, ifa.last_error())
+    if twin == ifa.IFA_KV_PAGED:
+        assert ws_size(base_args(kv_layout=layout, block_table=0))[0] == ifa.IFA_ERR_PARAM_NULLPTR
     a = base_args(kv_dtype=ifa.IFA_I8, antiquant_scale=FAKE, antiquant_offset=FAKE, block_size=48)
     assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_INVALID  # int8 needs 32-aligned blocks
     a = base_args(antiquant_scale=FAKE, antiquant_offset=FAKE)

@@ -338,3 +338,48 @@ def test_full_size_sampled_rows(cfg):
     rows = _sampled_rows(w, 12, cfg)
     ref_out, ref_lse = oracle.decode_workload(w, rows=rows)
     _compare(w, out, lse, ref_out, ref_lse, rows=rows)
+
+
+# ------------------------------------------------ token-major layouts, per-tensor antiquant
+@pytest.mark.parametrize("layout", ["paged_bsh", "bsnd"])
+@pytest.mark.parametrize("kv", ["f32", "f16", "bf16", "i8"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_token_major_layouts(layout, kv, d):
+    """The (blocknum, blocksize, H) pool and the contiguous (B, S, H) cache:
+    consecutive tokens of a KV head are N_kv rows apart.  Ragged lengths
+    across block and tile boundaries, NaN-poisoned unused slots."""
+    lens = [0, 1, 15, 16, 17, 31, 127, 128, 129, 300]
+    kw = dict(block_size=32, extra_blocks=2) if layout == "paged_bsh" else dict(s_cap=320)
+    w = make_workload(batch=len(lens), n_q=8, n_kv=2, qk_dim=d, kv_dtype=kv, layout=layout,
+                      lengths=lens, seed=71 + d, sink=(kv == "i8"), **kw)
+    _full_check(w, 3)
+
+
+@pytest.mark.parametrize("layout", ["paged", "paged_bsh", "bsnd"])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_per_tensor_antiquant(layout, splits):
+    """int8 K/V with one scale and offset for K and one for V (shape (2))."""
+    kw = dict(block_size=64) if layout != "bsnd" else dict(s_cap=704)
+    w = make_workload(batch=4, n_q=16, n_kv=4, qk_dim=128, kv_dtype="i8", layout=layout,
+                      lengths=[700, 1, 64, 333], seed=81 + splits, sink=True, antiquant_mode="tensor", **kw)
+    assert tuple(w.antiquant_scale.shape) == (2,)
+    _full_check(w, splits)
+
+
+def test_full_size_token_major_pool_sampled_rows():
+    """The paged bf16 GQA workload at full size (B=64, N_q=32, N_kv=8,
+    lengths U[512, 8192]) with its pool in the (blocknum, blocksize, H)
+    layout; the oracle recomputes a sample of rows."""
+    wg = config_workload(3, device="cuda", layout="paged_bsh")
+    _announce(f"full size config 3 in the paged_bsh layout")
+    out, lse = ifa.decode_workload(wg)
+    torch.cuda.synchronize()
+    out = out.double().cpu().numpy()
+    lse = lse.double().cpu().numpy()
+    assert not np.isnan(out).any()
+    w = wg.to("cpu")
+    del wg
+    torch.cuda.empty_cache()
+    rows = _sampled_rows(w, 12, 33)
+    ref_out, ref_lse = oracle.decode_workload(w, rows=rows)
+    _compare(w, out, lse, ref_out, ref_lse, rows=rows)

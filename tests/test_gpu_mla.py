@@ -145,3 +145,9 @@ def test_mla_wide_offsets_path():
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle.decode_workload(w)
     _compare(w, out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse)
+
+
+def test_mla_token_major_pool():
+    """With one KV head the (blocknum, blocksize, H) pool holds the same bytes
+    as the head-major one."""
+    _full_check(_mla(layout="paged_bsh", lengths=[300, 77], seed=58), 3)
