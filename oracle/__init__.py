@@ -14,7 +14,9 @@ Every function is the plain definition from the pages, in NumPy float64:
   read in its sum-weighted form (see ``merge``);
 * paged gather: aclnnIncreFlashAttentionV3, "Constraints", page attention
   scenario (blockTable, blockSize, KV layout (blocknum, KV_N, blocksize, D));
-* block count: aclnnMlaPrologV3WeightNz, "Constraints", BlockNum row.
+* block count: aclnnMlaPrologV3WeightNz, "Constraints", BlockNum row;
+* paged KV-cache write: aclnnMlaPrologV3WeightNz, "Parameters", kvCacheRef /
+  cacheIndexOptional (``cache_ref.cache_write``).
 
 Parity pins: every function here is pinned by the CPU tests in
 tests/test_oracle_pins.py.  Three readings are not fixed by the pages and are
@@ -39,3 +41,4 @@ from .attn_ref import (  # noqa: F401
     block_count,
     lengths_from_prefix_sums,
 )
+from .cache_ref import cache_write  # noqa: F401,E402
