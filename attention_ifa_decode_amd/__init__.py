@@ -53,6 +53,7 @@ EXPORTED = (
     "ifa_decode_splitkv_timed",
     "ifa_decode_combine",
     "attn_update",
+    "ifa_kv_cache_write",
     "ifa_paged_block_count",
     "ifa_last_error",
 )
@@ -116,12 +117,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ifa_decode_splitkv_timed.argtypes = [args_p, P, SZ, P, P, P]
     lib.ifa_decode_combine.argtypes = [args_p, P, SZ, P]
     lib.attn_update.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I32, I32, P]
+    lib.ifa_kv_cache_write.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, I64, I32, I32, P]
     lib.ifa_paged_block_count.argtypes = [ctypes.POINTER(I64), I64, I64]
     lib.ifa_paged_block_count.restype = I64
     lib.ifa_last_error.argtypes = []
     lib.ifa_last_error.restype = ctypes.c_char_p
     for name in ("ifa_decode_workspace_size", "ifa_decode_num_splits", "ifa_decode", "ifa_decode_splitkv",
-                 "ifa_decode_splitkv_timed", "ifa_decode_combine", "attn_update"):
+                 "ifa_decode_splitkv_timed", "ifa_decode_combine", "attn_update", "ifa_kv_cache_write"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -322,6 +324,31 @@ def attn_update(prev_out, prev_max, prev_sum, cur_out, cur_max, cur_sum, out=Non
                            sum_out.data_ptr(), rows, D, _DTYPE_CODE[prev_out.dtype], stride,
                            _stream_handle()))
     return out, max_out, sum_out
+
+
+def kv_cache_write(src, slot_index, cache, layout: str = "paged_bsh", col_offset: int = 0):
+    """Write new K/V rows into a paged pool in place (the step before a
+    decode step): src (T, N_kv, d) rows go to the slots slot_index (T) int64
+    of ``cache``, "paged_bsh" (num_blocks, block_size, N_kv, W) or "paged"
+    (num_blocks, N_kv, block_size, W), at channels col_offset .. col_offset
+    + d - 1.  Slots outside the pool are skipped.  Returns ``cache``."""
+    lib = load_library()
+    if layout not in ("paged", "paged_bsh"):
+        raise ValueError("layout must be 'paged' or 'paged_bsh'")
+    _need(src, "src", cache.dtype)
+    _need(slot_index, "slot_index", torch.int64)
+    _need(cache, "cache", cache.dtype)
+    T, n_kv, d = src.shape
+    if layout == "paged_bsh":
+        num_blocks, block_size, n_kv_c, w = cache.shape
+    else:
+        num_blocks, n_kv_c, block_size, w = cache.shape
+    if n_kv_c != n_kv or slot_index.numel() != T:
+        raise ValueError("src, slot_index and cache disagree")
+    _check(lib.ifa_kv_cache_write(src.data_ptr(), slot_index.data_ptr(), cache.data_ptr(), T, n_kv, d, w,
+                                  int(col_offset), num_blocks, block_size, _LAYOUT_CODE[layout],
+                                  _DTYPE_CODE[cache.dtype], _stream_handle()))
+    return cache
 
 
 def paged_block_count(lengths, block_size: int) -> int:

@@ -434,6 +434,44 @@ ifa_status attn_update(const void* prev_attn_out, const float* prev_softmax_max,
   return ok();
 }
 
+ifa_status ifa_kv_cache_write(const void* src, const int64_t* slot_index, void* cache, int64_t tokens,
+                              int64_t num_kv_heads, int64_t d, int64_t row_elems, int64_t col_offset,
+                              int64_t num_blocks, int64_t block_size, int32_t layout, int32_t dtype,
+                              hipStream_t stream) {
+  if (tokens < 0) return fail(IFA_ERR_PARAM_INVALID, "tokens must be >= 0");
+  if (num_kv_heads < 1 || num_kv_heads > 256) return fail(IFA_ERR_PARAM_INVALID, "num_kv_heads outside [1, 256]");
+  if (d < 1 || col_offset < 0 || row_elems < col_offset + d || row_elems > 65536)
+    return fail(IFA_ERR_PARAM_INVALID, "need 1 <= d, 0 <= col_offset, col_offset + d <= row_elems <= 65536");
+  if (num_blocks < 1 || block_size < 1 || block_size > 1024)
+    return fail(IFA_ERR_PARAM_INVALID, "num_blocks must be >= 1 and block_size in [1, 1024]");
+  if (layout != IFA_KV_PAGED && layout != IFA_KV_PAGED_BSH)
+    return fail(IFA_ERR_PARAM_INVALID, "layout %d is not a paged layout", layout);
+  if (dtype != IFA_F32 && dtype != IFA_F16 && dtype != IFA_BF16 && dtype != IFA_I8)
+    return fail(IFA_ERR_PARAM_INVALID, "dtype %d not supported", dtype);
+  const int64_t esz = dtype == IFA_F32 ? 4 : (dtype == IFA_I8 ? 1 : 2);
+  if ((d * esz) % 16 || (col_offset * esz) % 16 || (row_elems * esz) % 16)
+    return fail(IFA_ERR_PARAM_INVALID, "d, col_offset and row_elems must each span a multiple of 16 bytes");
+  if (tokens == 0) return ok();
+  if (!src || !slot_index || !cache) return fail(IFA_ERR_PARAM_NULLPTR, "ifa_kv_cache_write: a pointer is NULL");
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(cache)) & 15)
+    return fail(IFA_ERR_PARAM_INVALID, "src and cache must be 16-byte aligned");
+  ifa::CacheWriteLaunch W{};
+  W.src = src;
+  W.slot_index = slot_index;
+  W.cache = cache;
+  W.tokens = tokens;
+  W.n_kv = num_kv_heads;
+  W.row_chunks = d * esz / 16;
+  W.row_bytes = row_elems * esz;
+  W.col_bytes = col_offset * esz;
+  W.num_blocks = num_blocks;
+  W.block_size = block_size;
+  W.token_major = layout == IFA_KV_PAGED_BSH;
+  ifa_status st = runtime(ifa::launch_cache_write(W, stream), "cache write launch");
+  if (st != IFA_OK) return st;
+  return ok();
+}
+
 int64_t ifa_paged_block_count(const int64_t* lengths, int64_t batch, int64_t block_size) {
   if (!lengths || batch < 0 || block_size < 1) return -1;
   int64_t total = 0;

@@ -128,6 +128,17 @@ hipError_t launch_combine(const CombineLaunch& p, hipStream_t stream);
 hipError_t launch_plan(const int64_t* seq_lens, int batch, int64_t cap, int2* plan, hipStream_t stream);
 hipError_t launch_update(const UpdateLaunch& p, hipStream_t stream);
 
+// Paged KV-cache write: source rows (tokens, n_kv, row_chunks * 16 bytes) to
+// the pool rows of their slots, at byte col_bytes of each row_bytes-long row.
+struct CacheWriteLaunch {
+  const void* src;
+  const int64_t* slot_index;  // (tokens)
+  void* cache;
+  int64_t tokens, n_kv, row_chunks, row_bytes, col_bytes, num_blocks, block_size;
+  bool token_major;           // (blocks, block_size, n_kv, W) rather than (blocks, n_kv, block_size, W)
+};
+hipError_t launch_cache_write(const CacheWriteLaunch& p, hipStream_t stream);
+
 // Which (q dtype, kv dtype, head dim, heads per workgroup) the VALU path has
 // kernels for.
 bool gqa_supported(int q_dtype, int kv_dtype, int head_dim, int heads_per_wg);

@@ -194,6 +194,29 @@ ifa_status attn_update(const void* prev_attn_out, const float* prev_softmax_max,
                        int64_t rows, int64_t head_dim, int32_t dtype, int32_t stat_stride,
                        hipStream_t stream);
 
+/* Paged KV-cache write, the step before a decode step
+ * (aclnnMlaPrologV3WeightNz "Parameters": kvCacheRef / krCacheRef updated in
+ * place at cacheIndexOptional, CacheMode PA_BSND).  For every token t and KV
+ * head g, the d elements src[t][g][0 .. d-1] are copied unchanged into
+ * elements col_offset .. col_offset + d - 1 of the cache row of slot
+ * s = slot_index[t], which is position s % block_size of block
+ * s / block_size:
+ *   layout IFA_KV_PAGED_BSH: cache (num_blocks, block_size, N_kv, row_elems)
+ *   layout IFA_KV_PAGED:     cache (num_blocks, N_kv, block_size, row_elems)
+ * (the MLA row [latent 512 | rope 64] takes two calls, col_offset 0 and 512).
+ *   src        (tokens, num_kv_heads, d), device, element type `dtype`
+ *   slot_index (tokens) int64, device; a slot outside
+ *              [0, num_blocks * block_size) is skipped
+ *   cache      device, element type `dtype`, written in place
+ * d, col_offset and row_elems must each span a multiple of 16 bytes, and
+ * src and cache must be 16-byte aligned (IFA_ERR_PARAM_INVALID otherwise).
+ * Two tokens naming the same slot leave one of the two rows there.
+ * tokens == 0 is a no-op.  Asynchronous on `stream`. */
+ifa_status ifa_kv_cache_write(const void* src, const int64_t* slot_index, void* cache, int64_t tokens,
+                              int64_t num_kv_heads, int64_t d, int64_t row_elems, int64_t col_offset,
+                              int64_t num_blocks, int64_t block_size, int32_t layout, int32_t dtype,
+                              hipStream_t stream);
+
 /* Block count of a paged pool (aclnnMlaPrologV3WeightNz "Constraints",
  * BlockNum row): sum over b of ceil(lengths[b] / block_size).  Host pointer;
  * returns -1 for a NULL pointer, a negative batch or length, or a block_size

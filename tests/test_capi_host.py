@@ -234,3 +234,25 @@ def test_block_count_worked_example():
     assert ifa.paged_block_count([], 128) == 0
     with pytest.raises(ValueError):
         ifa.paged_block_count([-1], 128)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tokens=-1), ifa.IFA_ERR_PARAM_INVALID),
+    (dict(n_kv=0), ifa.IFA_ERR_PARAM_INVALID),
+    (dict(d=100), ifa.IFA_ERR_PARAM_INVALID),            # 200 bytes: not a multiple of 16
+    (dict(col_offset=8), ifa.IFA_ERR_PARAM_INVALID),     # 16 bytes, fine, but col_offset + d > row_elems
+    (dict(layout=ifa.IFA_KV_BNSD), ifa.IFA_ERR_PARAM_INVALID),
+    (dict(dtype=9), ifa.IFA_ERR_PARAM_INVALID),
+    (dict(block_size=0), ifa.IFA_ERR_PARAM_INVALID),
+    (dict(src=0), ifa.IFA_ERR_PARAM_NULLPTR),
+    (dict(src=FAKE + 8), ifa.IFA_ERR_PARAM_INVALID),     # not 16-byte aligned
+    (dict(tokens=0, src=0), ifa.IFA_OK),                 # empty: no-op before any pointer check
+])
+def test_cache_write_checks_before_launching(kw, code):
+    a = dict(src=FAKE, slot_index=FAKE + 0x1000, cache=FAKE + 0x2000, tokens=64, n_kv=8, d=128, row_elems=128,
+             col_offset=0, num_blocks=100, block_size=128, layout=ifa.IFA_KV_PAGED_BSH, dtype=ifa.IFA_BF16)
+    a.update(kw)
+    st = lib().ifa_kv_cache_write(a["src"], a["slot_index"], a["cache"], a["tokens"], a["n_kv"], a["d"],
+                                  a["row_elems"], a["col_offset"], a["num_blocks"], a["block_size"], a["layout"],
+                                  a["dtype"], None)
+    assert st == code, (st, ifa.last_error())
