@@ -16,7 +16,9 @@ Every function is the plain definition from the pages, in NumPy float64:
   scenario (blockTable, blockSize, KV layout (blocknum, KV_N, blocksize, D));
 * block count: aclnnMlaPrologV3WeightNz, "Constraints", BlockNum row;
 * paged KV-cache write: aclnnMlaPrologV3WeightNz, "Parameters", kvCacheRef /
-  cacheIndexOptional (``cache_ref.cache_write``).
+  cacheIndexOptional (``cache_ref.cache_write``);
+* multi-token decode with the rightDownCausal and treeMask masks of the
+  FusedInferAttentionScore blog (``spec_ref.decode_multi``).
 
 Parity pins: every function here is pinned by the CPU tests in
 tests/test_oracle_pins.py.  Three readings are not fixed by the pages and are
@@ -42,3 +44,4 @@ from .attn_ref import (  # noqa: F401
     lengths_from_prefix_sums,
 )
 from .cache_ref import cache_write  # noqa: F401,E402
+from .spec_ref import MASK_CAUSAL, MASK_NONE, MASK_TREE, decode_multi, visible_tokens  # noqa: F401,E402
