@@ -40,6 +40,7 @@ IFA_ERR_PLAN = 561002
 IFA_F32, IFA_F16, IFA_BF16, IFA_I8 = 0, 1, 2, 3
 IFA_KV_BNSD, IFA_KV_PAGED, IFA_KV_PAGED_BSH, IFA_KV_BSND = 0, 1, 2, 3
 IFA_ANTIQUANT_PER_CHANNEL, IFA_ANTIQUANT_PER_TENSOR = 0, 1
+IFA_MASK_NONE, IFA_MASK_CAUSAL, IFA_MASK_TREE = 0, 3, 9
 _LAYOUT_CODE = {"bnsd": IFA_KV_BNSD, "paged": IFA_KV_PAGED, "paged_bsh": IFA_KV_PAGED_BSH, "bsnd": IFA_KV_BSND}
 
 _DTYPE_CODE = {torch.float32: IFA_F32, torch.float16: IFA_F16, torch.bfloat16: IFA_BF16, torch.int8: IFA_I8}
@@ -93,6 +94,10 @@ class DecodeArgs(ctypes.Structure):
         ("kv_layout", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
         ("antiquant_mode", ctypes.c_int32),
+        ("q_seq_len", ctypes.c_int64),
+        ("tree_mask", ctypes.c_void_p),
+        ("sparse_mode", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -167,15 +172,19 @@ class DecodeCall:
                  num_key_value_heads: int, scale_value: float, learnable_sink=None, antiquant_scale=None,
                  antiquant_offset=None, num_splits: int = 0, v_dim: Optional[int] = None,
                  out_dtype: Optional[torch.dtype] = None, with_lse: bool = True, out=None, lse=None,
-                 kv_layout: Optional[str] = None):
+                 kv_layout: Optional[str] = None, sparse_mode: int = IFA_MASK_NONE, tree_mask=None):
         lib = load_library()
         _need(q, "q")
         _need(k_cache, "k_cache")
         _need(v_cache, "v_cache")
         _need(actual_seq_lengths, "actual_seq_lengths", torch.int64)
-        B, n_q, qk_dim = q.shape
+        # q (B, N_q, D), or (B, S_q, N_q, D) for S_q query tokens per sequence
+        multi = q.dim() == 4
+        B, q_seq, n_q, qk_dim = q.shape if multi else (q.shape[0], 1, q.shape[1], q.shape[2])
         if n_q != num_heads:
-            raise ValueError("q.shape[1] must equal num_heads")
+            raise ValueError("the query's head dimension must equal num_heads")
+        if tree_mask is not None:
+            _need(tree_mask, "tree_mask", torch.uint8)
         alias = v_cache.data_ptr() == k_cache.data_ptr()
         if v_dim is None:
             v_dim = qk_dim if alias else v_cache.shape[-1]
@@ -202,9 +211,10 @@ class DecodeCall:
                 _need(t, nm, torch.float32)
         out_dtype = out_dtype or q.dtype
         dev = q.device
-        self.out = out if out is not None else torch.empty((B, n_q, v_dim), dtype=out_dtype, device=dev)
+        lead = (B, q_seq) if multi else (B,)
+        self.out = out if out is not None else torch.empty(lead + (n_q, v_dim), dtype=out_dtype, device=dev)
         self.lse = lse if lse is not None else (
-            torch.empty((B, n_q), dtype=torch.float32, device=dev) if with_lse else None)
+            torch.empty(lead + (n_q,), dtype=torch.float32, device=dev) if with_lse else None)
         a = DecodeArgs()
         a.query = _ptr(q)
         a.key_cache = _ptr(k_cache)
@@ -233,6 +243,10 @@ class DecodeCall:
         a.num_splits = int(num_splits)
         a.antiquant_mode = (IFA_ANTIQUANT_PER_TENSOR if antiquant_scale is not None and antiquant_scale.dim() == 1
                             else IFA_ANTIQUANT_PER_CHANNEL)
+        a.q_seq_len = q_seq
+        a.tree_mask = _ptr(tree_mask)
+        a.sparse_mode = int(sparse_mode)
+        a.reserved = 0
         self.args = a
         sz = ctypes.c_size_t(0)
         _check(lib.ifa_decode_workspace_size(ctypes.byref(a), ctypes.byref(sz)))
@@ -243,7 +257,8 @@ class DecodeCall:
         self.workspace = torch.empty(max(1, sz.value), dtype=torch.uint8, device=dev)
         # keep the inputs alive as long as the call object
         self._keep = (q, k_cache, v_cache, block_table, actual_seq_lengths, learnable_sink,
-                      antiquant_scale, antiquant_offset)
+                      antiquant_scale, antiquant_offset, tree_mask)
+        self.q_seq = q_seq
         self._lib = lib
 
     def run(self):
@@ -272,9 +287,10 @@ class DecodeCall:
 
     def partials(self):
         """Views of the workspace after ``splitkv()``: (attn_out, softmax_max,
-        softmax_sum) with shapes (B, N_q, n, v_dim), (B, N_q, n), (B, N_q, n)."""
+        softmax_sum) with shapes (B, N_q, n, v_dim), (B, N_q, n), (B, N_q, n);
+        with S_q query tokens B counts (sequence, query token) pairs."""
         a = self.args
-        B, nq, n, dv = a.batch, a.num_heads, self.num_splits, a.v_dim
+        B, nq, n, dv = a.batch * self.q_seq, a.num_heads, self.num_splits, a.v_dim
         f = self.workspace.view(torch.float32) if self.workspace_bytes else None
         rows = B * nq * n
         al = lambda x: (x + 255) // 256 * 256  # noqa: E731
@@ -287,14 +303,18 @@ class DecodeCall:
 def decode(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads: int, num_key_value_heads: int,
            scale_value: float, learnable_sink=None, antiquant_scale=None, antiquant_offset=None,
            num_splits: int = 0, v_dim: Optional[int] = None,
-           out_dtype: Optional[torch.dtype] = None, kv_layout: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+           out_dtype: Optional[torch.dtype] = None, kv_layout: Optional[str] = None,
+           sparse_mode: int = IFA_MASK_NONE, tree_mask=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Decode attention; returns (attention_out (B, N_q, v_dim), softmax_lse (B, N_q) fp32).
     kv_layout: "paged" (default with a block table), "paged_bsh", "bnsd"
     (default without one) or "bsnd"; antiquant parameters of shape (2,) are
-    per tensor."""
+    per tensor.  A query of shape (B, S_q, N_q, D) decodes S_q tokens per
+    sequence (the last S_q of its length) under ``sparse_mode`` (IFA_MASK_NONE,
+    IFA_MASK_CAUSAL, or IFA_MASK_TREE with ``tree_mask`` uint8 (B, S_q, S_q));
+    then out is (B, S_q, N_q, v_dim) and lse (B, S_q, N_q)."""
     call = DecodeCall(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads, num_key_value_heads,
                       scale_value, learnable_sink, antiquant_scale, antiquant_offset, num_splits, v_dim,
-                      out_dtype, kv_layout=kv_layout)
+                      out_dtype, kv_layout=kv_layout, sparse_mode=sparse_mode, tree_mask=tree_mask)
     out, lse = call.run()
     # the workspace must outlive the queued kernels: the caching allocator
     # keeps it reserved for this stream

@@ -46,7 +46,8 @@ struct Plan {
   Path path;
   int64_t n_kv;
   int group;
-  int heads_per_wg;
+  int heads_per_wg;  // query rows per workgroup (GQA)
+  int q_seq;         // query tokens per sequence
   int n_split;
   size_t off_o, off_m, off_l, off_plan, bytes;
 };
@@ -64,8 +65,8 @@ bool is_float_dtype(int32_t d) { return d == IFA_F32 || d == IFA_F16 || d == IFA
 // does more arithmetic per byte, at about 2048 (B=32, 16K tokens: 345 us at
 // 4 splits, 434 us at 1).  A split also keeps at least ~1024 tokens of the
 // longest sequence.
-int auto_splits_gqa(const ifa_decode_args* a, int64_t n_kv, int group, int gh, int64_t max_len) {
-  const int64_t per_split = a->batch * n_kv * (group / gh);  // workgroups per split index
+int auto_splits_gqa(const ifa_decode_args* a, int64_t n_kv, int rows_kv, int gh, int64_t max_len) {
+  const int64_t per_split = a->batch * n_kv * (rows_kv / gh);  // workgroups per split index
   const int64_t target = a->kv_dtype == IFA_I8 ? 8LL * kTargetCUs : 2LL * kTargetCUs;
   int64_t n = (target + per_split - 1) / per_split;
   const int64_t by_len = (max_len + 1023) / 1024;
@@ -133,6 +134,12 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
   if (a->kv_layout != IFA_KV_BNSD && a->kv_layout != IFA_KV_PAGED && a->kv_layout != IFA_KV_PAGED_BSH &&
       a->kv_layout != IFA_KV_BSND)
     return fail(IFA_ERR_PARAM_INVALID, "kv_layout %d not supported", a->kv_layout);
+  if (a->reserved != 0) return fail(IFA_ERR_PARAM_INVALID, "reserved field must be 0");
+  if (a->q_seq_len < 0 || a->q_seq_len > 16)
+    return fail(IFA_ERR_PARAM_INVALID, "q_seq_len %lld outside [0, 16]", (long long)a->q_seq_len);
+  const int q_seq = a->q_seq_len == 0 ? 1 : (int)a->q_seq_len;
+  if (a->sparse_mode != IFA_MASK_NONE && a->sparse_mode != IFA_MASK_CAUSAL && a->sparse_mode != IFA_MASK_TREE)
+    return fail(IFA_ERR_PARAM_INVALID, "sparse_mode %d not supported (0, 3 or 9)", a->sparse_mode);
   if (a->num_splits < 0 || a->num_splits > kMaxSplits)
     return fail(IFA_ERR_PARAM_INVALID, "num_splits %d outside [0, %d]", a->num_splits, kMaxSplits);
 
@@ -146,6 +153,8 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
     if (n_kv != 1) return fail(IFA_ERR_PARAM_INVALID, "the MLA shape needs num_key_value_heads 1");
     if (!ifa::mla_supported((int)a->num_heads))
       return fail(IFA_ERR_PARAM_INVALID, "the MLA shape needs num_heads to be a multiple of 32");
+    if (q_seq != 1 || a->sparse_mode != IFA_MASK_NONE)
+      return fail(IFA_ERR_PARAM_INVALID, "multi-token decode and masks are supported on the GQA shapes only");
     path = Path::kMla;
   } else if ((a->qk_dim == 64 || a->qk_dim == 128) && a->v_dim == a->qk_dim) {
     if (alias) return fail(IFA_ERR_PARAM_INVALID, "value_cache may equal key_cache only for the MLA shape");
@@ -185,21 +194,26 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
     if (!a->attention_out) return fail(IFA_ERR_PARAM_NULLPTR, "attention_out is NULL");
     if (is_paged(a->kv_layout) && !a->block_table)
       return fail(IFA_ERR_PARAM_NULLPTR, "block_table is NULL in the paged layout");
+    if (a->sparse_mode == IFA_MASK_TREE && !a->tree_mask)
+      return fail(IFA_ERR_PARAM_NULLPTR, "tree_mask is NULL with IFA_MASK_TREE");
   }
 
   Plan p{};
   p.path = path;
   p.n_kv = n_kv;
   p.group = (int)(a->num_heads / n_kv);
+  p.q_seq = q_seq;
   if (path == Path::kGqa) {
+    // a workgroup takes gh of the q_seq * group query rows of a KV head
+    const int rows_kv = q_seq * p.group;
     const int gh_max = ifa::gqa_max_heads_per_wg(a->kv_dtype, (int)a->qk_dim);
     int gh = 1;
     for (int c = gh_max; c >= 1; c >>= 1)
-      if (p.group % c == 0) { gh = c; break; }
+      if (rows_kv % c == 0) { gh = c; break; }
     p.heads_per_wg = gh;
     if (!ifa::gqa_supported(a->q_dtype, a->kv_dtype, (int)a->qk_dim, gh))
       return fail(IFA_ERR_PARAM_INVALID, "dtype combination (q %d, kv %d) not supported", a->q_dtype, a->kv_dtype);
-    p.n_split = a->num_splits ? a->num_splits : auto_splits_gqa(a, n_kv, p.group, gh, max_len);
+    p.n_split = a->num_splits ? a->num_splits : auto_splits_gqa(a, n_kv, rows_kv, gh, max_len);
   } else {
     p.heads_per_wg = (int)a->num_heads;
     p.n_split = a->num_splits ? a->num_splits : auto_splits_mla(a, max_len);
@@ -208,7 +222,7 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
                   "the MLA shape needs num_splits >= %lld so that a split spans at most %d cache blocks",
                   (long long)min_splits_mla(a, max_len), ifa::kMlaMaxTableSlice - 2);
   }
-  const size_t rows = (size_t)a->batch * (size_t)a->num_heads * (size_t)p.n_split;
+  const size_t rows = (size_t)a->batch * (size_t)q_seq * (size_t)a->num_heads * (size_t)p.n_split;
   p.off_o = 0;
   p.off_m = align256(rows * (size_t)a->v_dim * sizeof(float));
   p.off_l = p.off_m + align256(rows * sizeof(float));
@@ -270,6 +284,10 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
     L.n_kv = (int)p.n_kv;
     L.group = p.group;
     L.heads_per_wg = p.heads_per_wg;
+    L.q_seq = p.q_seq;
+    L.rows_kv = p.q_seq * p.group;
+    L.mask_mode = a->sparse_mode;
+    L.tree_mask = a->tree_mask;
     L.n_split = p.n_split;
     L.s_cap = max_len;
     L.block_size = (int)a->block_size;
@@ -326,7 +344,8 @@ ifa_status run_combine(const ifa_decode_args* a, const Plan& p, const void* ws, 
   C.sink = a->learnable_sink;
   C.out = a->attention_out;
   C.lse = a->softmax_lse;
-  C.batch = (int)a->batch;
+  C.batch = (int)a->batch * p.q_seq;  // rows are (sequence, query token, head)
+  C.q_seq = p.q_seq;
   C.n_q = (int)a->num_heads;
   C.n_split = p.n_split;
   C.v_dim = (int)a->v_dim;

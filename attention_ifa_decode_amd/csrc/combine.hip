@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
   if (lane < a.n_split) m0 = m[lane], l0 = l[lane];
   const float sink = a.sink ? a.sink[h] : kNegInf;
 
-  int64_t L64 = a.seq_lens[b];
+  int64_t L64 = a.seq_lens[b / a.q_seq];
   const int L = (int)(L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64));
   const int per = ((L + a.n_split - 1) / a.n_split + 15) & ~15;  // split_chunk, in 32 bits
   const int nvalid = L == 0 ? 0 : (L + per - 1) / per;
@@ -125,7 +125,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
   float part_tot = 0.f;
   for (int c0 = 0; c0 < nvalid; c0 += 64) {
     const int s = c0 + lane;
-    const float w = s < nvalid ? sm_w[wave][s] * fast_exp2((sm_m[wave][s] - M) * kLog2e) : 0.f;
+    // a partial whose max is -inf (a masked query row) has weight 0, even when every one is
+    const float w = s < nvalid && sm_m[wave][s] != kNegInf ? sm_w[wave][s] * fast_exp2((sm_m[wave][s] - M) * kLog2e) : 0.f;
     sm_w[wave][s] = w;
     part_tot += w;
   }

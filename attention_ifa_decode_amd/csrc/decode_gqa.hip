@@ -208,7 +208,7 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   // robin to the 8 XCDs, so the head groups of an item are placed 8 ids
   // apart: they run on the same XCD at about the same time and the later
   // reads hit its L2 instead of HBM.
-  const int HG = a.group / GH;
+  const int HG = a.rows_kv / GH;
   const int span = 8 * HG;
   const int hg = (blockIdx.x % span) / 8;
   int rem = (blockIdx.x / span) * 8 + blockIdx.x % 8;  // item without the head group
@@ -240,7 +240,34 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = lane / C, c = lane % C;
-  const int h0 = g * a.group + hg * GH;
+  // Query row x of this workgroup: row hg * GH + x of the KV head's q_seq *
+  // group rows, query token major; its index in (B, q_seq, N_q).  With one
+  // query token this is head g * group + hg * GH + x of sequence b.
+  auto qrow_of = [&](int x) -> int64_t {
+    const int rr = hg * GH + x;
+    const int i = rr / a.group;
+    return ((int64_t)b * a.q_seq + i) * a.n_q + g * a.group + (rr - i * a.group);
+  };
+  // Multi-token masks: bit k of vis[x] is set when row x attends to draft
+  // token k, the token at position draft0 + k (rows attend to every token
+  // before draft0).  Wave-uniform.
+  const bool masked = a.mask_mode != 0;
+  const int draft0 = L - a.q_seq;
+  uint32_t vis[GH];
+#pragma unroll
+  for (int x = 0; x < GH; ++x) {
+    vis[x] = ~0u;
+    if (masked) {
+      const int i = (hg * GH + x) / a.group;
+      if (a.mask_mode == 3) {
+        vis[x] = (2u << i) - 1u;  // rightDownCausal: draft tokens k <= i
+      } else {
+        const int k = threadIdx.x & 63;
+        const uint8_t m = k < a.q_seq ? a.tree_mask[((int64_t)b * a.q_seq + i) * a.q_seq + k] : 1;
+        vis[x] = (uint32_t)__builtin_amdgcn_ballot_w64(m == 0);
+      }
+    }
+  }
   const int nsteps = (end - start + TOK - 1) / TOK;
 
   const char* kbase = static_cast<const char*>(a.k);
@@ -328,7 +355,7 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
     if (q16) {
 #pragma unroll
       for (int h = 0; h < GH; ++h) {
-        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.n_q + h0 + h) * D;
+        const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + qrow_of(h) * D;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const u32x4 v = *reinterpret_cast<const u32x4*>(qrow + 8 * (c + C * i));
@@ -340,7 +367,7 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
     }
 #pragma unroll
     for (int h = 0; h < GH && !q16; ++h) {
-      const int64_t qrow = ((int64_t)b * a.n_q + h0 + h) * D;
+      const int64_t qrow = qrow_of(h) * D;
       float part = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -435,6 +462,17 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
           d1 = group_sum<C>(d1) + kconst[h];
           s0[h] = valid0 ? d0 * a.scale_log2 : kNegInf;
           s1[h] = valid1 ? d1 * a.scale_log2 : kNegInf;
+        }
+        if (masked && start + TOK * (st + (two ? 5 : 1)) > draft0) {  // the steps reach the draft tokens
+          const int k0 = start + TOK * st + t - draft0, k1 = k0 + 4 * TOK;
+#pragma unroll
+          for (int h = 0; h < GH; ++h) {
+            if (k0 >= 0 && k0 < 32 && !((vis[h] >> k0) & 1u)) s0[h] = kNegInf;
+            if (k1 >= 0 && k1 < 32 && !((vis[h] >> k1) & 1u)) s1[h] = kNegInf;
+          }
+        }
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
           const float sm = fmaxf(s0[h], s1[h]);
           mtrue[h] = fmaxf(mtrue[h], sm);
           need |= sm > mref[h] + kRescale;
@@ -539,6 +577,15 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
           float dot = group_sum<C>(part);
           if constexpr (KV == kI8) dot += kconst[h];
           s[h] = valid ? dot * a.scale_log2 : kNegInf;
+        }
+        if (masked && start + TOK * (st + 1) > draft0) {  // the step reaches the draft tokens
+          const int k = start + TOK * st + t - draft0;
+#pragma unroll
+          for (int h = 0; h < GH; ++h)
+            if (k >= 0 && k < 32 && !((vis[h] >> k) & 1u)) s[h] = kNegInf;  // k < q_seq for valid tokens
+        }
+#pragma unroll
+        for (int h = 0; h < GH; ++h) {
           mtrue[h] = fmaxf(mtrue[h], s[h]);
           need |= s[h] > mref[h] + kRescale;
         }
@@ -639,7 +686,7 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
         o.x = fmaf(x.x, f, o.x), o.y = fmaf(x.y, f, o.y), o.z = fmaf(x.z, f, o.z), o.w = fmaf(x.w, f, o.w);
       }
     }
-    const float inv = 1.f / tot;
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;  // 0: every token of the split masked for this row
     o.x *= inv, o.y *= inv, o.z *= inv, o.w *= inv;
     if constexpr (KV == kI8) {
       // P V ran on (1024 + byte ^ 0x80): x_hat = (byte + offset) * scale
@@ -650,7 +697,7 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
       o.x = vsc[0] * (o.x - 1152.f + vof[0]), o.y = vsc[sd] * (o.y - 1152.f + vof[sd]);
       o.z = vsc[2 * sd] * (o.z - 1152.f + vof[2 * sd]), o.w = vsc[3 * sd] * (o.w - 1152.f + vof[3 * sd]);
     }
-    const int64_t row = (int64_t)b * a.n_q + h0 + h;
+    const int64_t row = qrow_of(h);
     *reinterpret_cast<float4*>(a.ws_o + (row * a.n_split + split) * D + d) = o;
     if (d == 0) {
       a.ws_m[row * a.n_split + split] = M * kLn2;
@@ -661,11 +708,11 @@ __global__ void __launch_bounds__(256) gqa_splitkv_kernel(const GqaLaunch a, int
 
 template <int QT, int KV, int D, int GH>
 hipError_t launch_typed(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
-  const int items = p.batch * p.n_kv * (p.group / GH) * p.n_split;
+  const int items = p.batch * p.n_kv * (p.rows_kv / GH) * p.n_split;
   if (items == 0) return hipSuccess;
   // head-group interleave (see the kernel): items without the head group,
   // rounded up to a multiple of 8, times the head groups
-  const int padded = (items / (p.group / GH) + 7) / 8 * 8 * (p.group / GH);
+  const int padded = (items / (p.rows_kv / GH) + 7) / 8 * 8 * (p.rows_kv / GH);
   if (p.paged)
     launch_kernel(gqa_splitkv_kernel<QT, KV, D, GH, true>, dim3(padded), dim3(256), stream, ev, p, items);
   else

@@ -19,10 +19,16 @@ struct GqaLaunch {
   // entry (i, g, d) of the parameters, i = 0 for K and 1 for V:
   // i * aq_stride_kv + g * aq_stride_g + d * aq_stride_d
   int aq_stride_kv, aq_stride_g, aq_stride_d;
-  float* ws_o;             // [B][n_q][n_split][D]
-  float* ws_m;             // [B][n_q][n_split]
-  float* ws_l;             // [B][n_q][n_split]
+  float* ws_o;             // [B][q_seq][n_q][n_split][D]
+  float* ws_m;             // [B][q_seq][n_q][n_split]
+  float* ws_l;             // [B][q_seq][n_q][n_split]
   int batch, n_q, n_kv, group, heads_per_wg, n_split;
+  // multi-token decode: q_seq query tokens per sequence; the rows_kv =
+  // q_seq * group query rows of a KV head (query token major) are split into
+  // workgroups of heads_per_wg rows
+  int q_seq, rows_kv;
+  int mask_mode;               // 0 none, 3 rightDownCausal, 9 tree
+  const uint8_t* tree_mask;    // (B, q_seq, q_seq), 1 removes a draft token
   int64_t s_cap;           // lengths are clamped to this
   int block_size, max_blocks, num_blocks;
   uint32_t bs_magic, bs_shift;  // n / block_size == (umulhi(n, magic) + n) >> shift
@@ -59,9 +65,10 @@ struct CombineLaunch {
   const float* ws_l;
   const int64_t* seq_lens;
   const float* sink;  // (n_q) or null
-  void* out;          // (B, n_q, v_dim)
-  float* lse;         // (B, n_q) or null
-  int batch, n_q, n_split, v_dim, out_dtype;
+  void* out;          // (batch, n_q, v_dim)
+  float* lse;         // (batch, n_q) or null
+  int batch, n_q, n_split, v_dim, out_dtype;  // batch counts (sequence, query token) pairs
+  int q_seq;          // query tokens per sequence: row r belongs to sequence r / n_q / q_seq
   int64_t s_cap;
 };
 

@@ -1,7 +1,8 @@
 """Benchmark: paged decode attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
-                    [--num-splits N] [--kv-layout L] [--no-cpu-baseline]
+                    [--num-splits N] [--kv-layout L] [--q-seq S --mask M]
+                    [--no-cpu-baseline]
 
 One step = one pass of the whole path over one batch: the split-KV decode
 kernel (block-table gather, QK^T, online softmax, PV, partial triples) and the
@@ -10,7 +11,9 @@ seeded and resident in HBM before timing starts.  The default workload is the
 paged bf16 GQA decode: B=64, N_q=32, N_kv=8, D=128, block size 128, lengths
 U[512, 8192], 4 KV splits.  ``--kv-layout`` measures the same workload with
 its cache in another layout (paged_bsh: (blocknum, blocksize, H) pool; bsnd:
-contiguous (B, S, H)).
+contiguous (B, S, H)).  ``--q-seq S`` decodes S query tokens per sequence
+(speculative verification) under ``--mask`` none / causal / tree (a seeded
+random tree over the S draft tokens); ``value`` still counts each KV byte once.
 
 Prints one JSON line.  ``value`` is KV-cache GB/s: the bytes of K and V that
 belong to valid tokens, per step, divided by the step time.  ``roofline``
@@ -128,6 +131,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=None)
     ap.add_argument("--kv-layout", default=None, choices=["paged", "paged_bsh", "bnsd", "bsnd"],
                     help="cache layout instead of the config's own (paged <-> paged_bsh, bnsd <-> bsnd)")
+    ap.add_argument("--q-seq", type=int, default=1, help="query tokens per sequence (1..16)")
+    ap.add_argument("--mask", default="causal", choices=["none", "causal", "tree"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -165,7 +170,26 @@ def main():
         x.seq_lens.copy_(w.seq_lens)
         if x.block_table is not None:
             x.block_table.copy_(w.block_table)
-    calls = [ifa.call_for_workload(x, num_splits=args.num_splits) for x in works]
+    modes = {"none": ifa.IFA_MASK_NONE, "causal": ifa.IFA_MASK_CAUSAL, "tree": ifa.IFA_MASK_TREE}
+
+    def make_call(x, i):
+        if args.q_seq == 1:
+            return ifa.call_for_workload(x, num_splits=args.num_splits)
+        # S_q query tokens per sequence; the tree keeps each draft token's own position
+        g = torch.Generator(device=dev).manual_seed(7000 + i)
+        q4 = torch.randn((x.batch, args.q_seq, x.n_q, x.qk_dim), generator=g, device=dev).to(x.q.dtype)
+        tm = None
+        if args.mask == "tree":
+            tm = (torch.rand((x.batch, args.q_seq, args.q_seq), generator=g, device=dev) < 0.5).to(torch.uint8)
+            tm *= 1 - torch.eye(args.q_seq, dtype=torch.uint8, device=dev)
+        return ifa.DecodeCall(q4, x.k_cache, x.v_cache, x.block_table, x.seq_lens, x.n_q, x.n_kv, x.scale,
+                              learnable_sink=x.sink, antiquant_scale=x.antiquant_scale,
+                              antiquant_offset=x.antiquant_offset,
+                              num_splits=x.num_splits if args.num_splits is None else args.num_splits,
+                              v_dim=x.v_dim, out_dtype=x.out_dtype, kv_layout=x.layout,
+                              sparse_mode=modes[args.mask], tree_mask=tm)
+
+    calls = [make_call(x, i) for i, x in enumerate(works)]
 
     for i in range(args.warmup):
         calls[i % copies].run()
@@ -198,8 +222,8 @@ def main():
     achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     # algorithmic flops: QK^T and PV for every valid token and query head
-    flops = sum(w.lengths()) * w.n_q * 2 * (w.qk_dim + w.v_dim)
-    traffic = read_traffic(args.config) if args.kv_layout is None else None
+    flops = sum(w.lengths()) * w.n_q * args.q_seq * 2 * (w.qk_dim + w.v_dim)  # masked tokens counted too
+    traffic = read_traffic(args.config) if args.kv_layout is None and args.q_seq == 1 else None
     dtype_name = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}
     lens = w.lengths()
     result = {
@@ -215,7 +239,7 @@ def main():
         "vs_baseline": None,
         "dtype": dtype_name[w.kv_dtype],
         "data": "synthetic",
-        "qtok_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "qtok_per_s": round(w.batch * args.q_seq / (ms_step * 1e-3), 1),
         "config": {
             "workload": w.name,
             "batch": w.batch,
@@ -228,6 +252,8 @@ def main():
             "seq_len_mean": round(sum(lens) / len(lens), 1),
             "seq_len_range": [min(lens), max(lens)],
             "num_splits": calls[0].num_splits,
+            "q_seq_len": args.q_seq,
+            "mask": args.mask if args.q_seq > 1 else "none",
             "kv_bytes_per_step": kv_bytes,
             "input_copies": copies,
             "parallelism": "none (1 GPU)",
@@ -251,7 +277,7 @@ def main():
         },
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.q_seq == 1:
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)
 

@@ -94,6 +94,17 @@ typedef enum {
  * tensor (2); index 0 applies to K, 1 to V. */
 typedef enum { IFA_ANTIQUANT_PER_CHANNEL = 0, IFA_ANTIQUANT_PER_TENSOR = 1 } ifa_antiquant_mode;
 
+/* Masks of a multi-token decode (the sparseMode values of the
+ * FusedInferAttentionScore pages).  With S_q query tokens per sequence of
+ * actual length L, query i is the token at position L - S_q + i:
+ *   IFA_MASK_NONE   every query attends to all L tokens;
+ *   IFA_MASK_CAUSAL rightDownCausal: query i attends to tokens j <= L - S_q + i;
+ *   IFA_MASK_TREE   treeMask of speculative decoding: every query attends to
+ *                   the tokens before the last S_q, and to the last-S_q token k
+ *                   iff tree_mask[b][i][k] == 0 (1 removes it).
+ * A query left with no token gives attention_out 0 and softmax_lse -inf. */
+typedef enum { IFA_MASK_NONE = 0, IFA_MASK_CAUSAL = 3, IFA_MASK_TREE = 9 } ifa_sparse_mode;
+
 /* Arguments of one decode call.  Element strides are implied by the shapes;
  * every tensor is dense and row-major as described. */
 typedef struct {
@@ -124,6 +135,14 @@ typedef struct {
   int32_t kv_layout;                 /* ifa_kv_layout */
   int32_t num_splits;                /* KV-axis splits per sequence, 1..256; 0 = auto */
   int32_t antiquant_mode;            /* ifa_antiquant_mode; 0 unless kv_dtype is IFA_I8 */
+  /* multi-token decode (speculative verification), GQA shapes only: S_q =
+   * q_seq_len query tokens per sequence (0 means 1; at most 16).  Then query
+   * is (B, S_q, N_q, qk_dim), attention_out (B, S_q, N_q, v_dim) and
+   * softmax_lse (B, S_q, N_q); with S_q == 1 these are the shapes above. */
+  int64_t q_seq_len;
+  const uint8_t* tree_mask;          /* (B, S_q, S_q) device, IFA_MASK_TREE only */
+  int32_t sparse_mode;               /* ifa_sparse_mode */
+  int32_t reserved;                  /* must be 0 */
 } ifa_decode_args;
 
 /* Phase 1 (aclnnIncreFlashAttentionV3GetWorkspaceSize): validate `args` and

@@ -116,6 +116,11 @@ def test_batch_zero_needs_no_workspace():
     ("num_splits", -1, ifa.IFA_ERR_PARAM_INVALID),
     ("num_splits", 300, ifa.IFA_ERR_PARAM_INVALID),
     ("antiquant_mode", 1, ifa.IFA_ERR_PARAM_INVALID),          # set for a bf16 cache
+    ("q_seq_len", 17, ifa.IFA_ERR_PARAM_INVALID),
+    ("q_seq_len", -1, ifa.IFA_ERR_PARAM_INVALID),
+    ("sparse_mode", 5, ifa.IFA_ERR_PARAM_INVALID),
+    ("sparse_mode", ifa.IFA_MASK_TREE, ifa.IFA_ERR_PARAM_NULLPTR),  # no tree_mask
+    ("reserved", 1, ifa.IFA_ERR_PARAM_INVALID),
     ("scale_value", float("nan"), ifa.IFA_ERR_PARAM_INVALID),
     ("max_blocks_per_seq", 0, ifa.IFA_ERR_PARAM_INVALID),
 ])
@@ -256,3 +261,17 @@ def test_cache_write_checks_before_launching(kw, code):
                                   a["row_elems"], a["col_offset"], a["num_blocks"], a["block_size"], a["layout"],
                                   a["dtype"], None)
     assert st == code, (st, ifa.last_error())
+
+
+def test_multi_token_decode_plans_rows_per_query_token():
+    """S_q query tokens per sequence: the workspace holds S_q times the rows;
+    the MLA shape takes one query token and no mask."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    st, sz = ws_size(base_args(q_seq_len=4, sparse_mode=ifa.IFA_MASK_CAUSAL, batch=64))
+    assert st == ifa.IFA_OK, ifa.last_error()
+    rows = 64 * 4 * 32 * 4
+    assert sz == al(rows * 128 * 4) + 2 * al(rows * 4) + al(64 * 8)
+    mla = dict(qk_dim=576, v_dim=512, num_heads=128, num_key_value_heads=1, value_cache=FAKE, num_splits=16)
+    assert ws_size(base_args(**mla))[0] == ifa.IFA_OK, ifa.last_error()
+    assert ws_size(base_args(q_seq_len=2, **mla))[0] == ifa.IFA_ERR_PARAM_INVALID
+    assert ws_size(base_args(sparse_mode=ifa.IFA_MASK_CAUSAL, **mla))[0] == ifa.IFA_ERR_PARAM_INVALID
