@@ -48,6 +48,7 @@ struct Plan {
   int group;
   int heads_per_wg;  // query rows per workgroup (GQA)
   int q_seq;         // query tokens per sequence
+  bool mfma;         // GQA rows on the matrix cores (multi-token decode)
   int n_split;
   size_t off_o, off_m, off_l, off_plan, bytes;
 };
@@ -70,6 +71,18 @@ int auto_splits_gqa(const ifa_decode_args* a, int64_t n_kv, int rows_kv, int gh,
   const int64_t target = a->kv_dtype == IFA_I8 ? 8LL * kTargetCUs : 2LL * kTargetCUs;
   int64_t n = (target + per_split - 1) / per_split;
   const int64_t by_len = (max_len + 1023) / 1024;
+  if (n > by_len) n = by_len;
+  if (n < 1) n = 1;
+  if (n > 64) n = 64;
+  return (int)n;
+}
+
+// One-wave workgroups of the multi-token MFMA path: about 2048 of them, each
+// split at least 512 tokens long.
+int auto_splits_mfma(const ifa_decode_args* a, int64_t n_kv, int rows_kv, int64_t max_len) {
+  const int64_t per_split = a->batch * n_kv * ((rows_kv + 31) / 32);
+  int64_t n = (8LL * kTargetCUs + per_split - 1) / per_split;
+  const int64_t by_len = (max_len + 511) / 512;
   if (n > by_len) n = by_len;
   if (n < 1) n = 1;
   if (n > 64) n = 64;
@@ -213,7 +226,15 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
     p.heads_per_wg = gh;
     if (!ifa::gqa_supported(a->q_dtype, a->kv_dtype, (int)a->qk_dim, gh))
       return fail(IFA_ERR_PARAM_INVALID, "dtype combination (q %d, kv %d) not supported", a->q_dtype, a->kv_dtype);
-    p.n_split = a->num_splits ? a->num_splits : auto_splits_gqa(a, n_kv, rows_kv, gh, max_len);
+    // several query tokens: the rows of a KV head go to the matrix cores in
+    // groups of 32, one wave each
+    p.mfma = q_seq > 1 && ifa::gqa_mfma_supported(a->q_dtype, a->kv_dtype, (int)a->qk_dim);
+    if (p.mfma) {
+      p.heads_per_wg = 32;
+      p.n_split = a->num_splits ? a->num_splits : auto_splits_mfma(a, n_kv, rows_kv, max_len);
+    } else {
+      p.n_split = a->num_splits ? a->num_splits : auto_splits_gqa(a, n_kv, rows_kv, gh, max_len);
+    }
   } else {
     p.heads_per_wg = (int)a->num_heads;
     p.n_split = a->num_splits ? a->num_splits : auto_splits_mla(a, max_len);
@@ -307,6 +328,7 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
     L.q_dtype = a->q_dtype;
     L.kv_dtype = a->kv_dtype;
     L.head_dim = (int)a->qk_dim;
+    if (p.mfma) return runtime(ifa::launch_gqa_mfma(L, stream, ev), "multi-token split-KV decode launch");
     return runtime(ifa::launch_gqa_splitkv(L, stream, ev), "split-KV decode launch");
   }
   ifa::MlaLaunch M{};

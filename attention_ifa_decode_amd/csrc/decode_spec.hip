@@ -1,0 +1,387 @@
+// Multi-token GQA split-KV decode on the matrix cores (gfx950).
+//
+// Speculative verification decodes S_q query tokens per sequence (the last
+// S_q of its length) under the masks of the FusedInferAttentionScore pages
+// (sparseMode 3 rightDownCausal, 9 treeMask).  A KV head then serves S_q * G
+// query rows, and every cached token meets all of them: QK^T and PV become
+// dense contractions with M = rows, which this kernel runs on
+// v_mfma_f32_32x32x16_{bf16,f16} and writes the split partial triples
+// (aclnnRingAttentionUpdate, "功能说明") that the combine kernel merges.
+//
+// Work decomposition.  One workgroup = one wave = one (sequence, KV head,
+// group of up to 32 rows, split); rows are query token major.  The split's
+// tokens stream in tiles of 32 through a private LDS ring of STAGES slots,
+// each slot the tile's K rows (8 KB) then its V rows (8 KB), loaded straight
+// from HBM with global_load_lds_dwordx4.  Per tile:
+//   S^T (32 tokens x 32 rows) = K (32 x 128) . Q^T (128 x 32): 8 MFMAs, K from
+//       LDS (ds_read_b128), Q^T in registers for the item;
+//   online softmax per row (a lane holds one row column and 16 tokens), the
+//       tail of the split and the masks' removed draft tokens at -inf, with
+//       the lazy rescale of the other kernels;
+//   O^T (128 x 32) += V^T (128 x 32 tokens) . P^T: 8 MFMAs, V^T through the
+//       transposing read ds_read_b64_tr_b16, P^T from the S^T accumulator
+//       rounded to the K/V dtype (normalised by the sum of the rounded
+//       weights; the partial's sum uses the fp32 weights).
+// The operand and accumulator layouts are those of the MLA kernel, on
+// 256-byte rows: row t keeps its 16-byte chunk c at position c ^ swz(t).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ifa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kD = 128;
+constexpr int kRowB = kD * 2;            // bytes of one token row of one KV head
+constexpr int kTile = 32;                // tokens per tile
+constexpr int kTileB = kTile * kRowB;    // 8 KB of K (and of V) per tile
+constexpr int kLoads = kTileB / 1024;    // DMA instructions per K (and per V) tile
+constexpr int kKSteps = kD / 16;         // MFMA k-steps of S^T
+constexpr int kMTiles = kD / 32;         // row tiles of O^T
+constexpr int kStages = 3;               // tiles in the ring
+constexpr int kSlotB = 2 * kTileB;       // K then V
+constexpr float kRescale = 8.f;
+constexpr float kMrefInit = -1e30f;
+static_assert(2 * kLoads * (kStages - 1) <= 63, "vmcnt");
+
+__device__ __forceinline__ int swz(int t) { return (2 * (t & 3) + ((t >> 2) & 1)) ^ (2 * ((t >> 3) & 1)); }
+
+__device__ __forceinline__ void dma16_lane(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, off offset:0 nt" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <typename T>
+__device__ __forceinline__ void settle(const T& x) {
+  asm volatile("" ::"v"(x));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+__device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)addr;
+}
+
+__device__ __forceinline__ s16x4_t lds_read_tr16(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(uintptr_t)addr);
+}
+
+// 32x32x16 MFMA on 16-bit operands held as raw 16-byte vectors
+template <int KV>
+__device__ __forceinline__ f32x16_t mfma(const u32x4& x, const u32x4& y, const f32x16_t& c) {
+  if constexpr (KV == kBF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, x), __builtin_bit_cast(bf16x8_t, y), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, x), __builtin_bit_cast(f16x8_t, y), c,
+                                                  0, 0, 0);
+}
+
+// the 16-bit pattern of `v` rounded to the K/V dtype
+template <int KV>
+__device__ __forceinline__ uint16_t round16(float v) {
+  if constexpr (KV == kBF16) return __builtin_bit_cast(uint16_t, (__bf16)v);
+  else return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// In-place scale of one accumulator tile, kept in accumulator registers (a
+// plain multiply would make the allocator copy the tiles to VGPRs).
+__device__ __forceinline__ void scale_acc(f32x16_t& v, float s) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = v[r];
+    float tmp;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(tmp)
+                 : "v"(s));
+    v[r] = x;
+  }
+}
+
+template <int KV, bool PAGED>
+__global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int work_items) {
+  __shared__ __attribute__((aligned(16))) char ring[kStages * kSlotB];
+
+  const int lane = threadIdx.x;
+  const int h = lane >> 5;  // which half of an MFMA k-range this lane feeds
+  const int col = lane & 31;
+
+  // ---- work item: (row group, split, KV head, sequence rank) ----
+  const int HG = (a.rows_kv + 31) / 32;
+  int rem = blockIdx.x;
+  if (rem >= work_items) return;
+  const int hg = rem % HG;
+  rem /= HG;
+  const int split = rem % a.n_split;
+  rem /= a.n_split;
+  const int g = rem % a.n_kv;
+  rem /= a.n_kv;
+  int b = rem, L;
+  if (a.longest_first) {  // the keys use the ring, which no load has reached yet
+    const BatchPick pick = batch_of_rank(rem, a.seq_lens, a.batch, a.s_cap, reinterpret_cast<uint32_t*>(ring));
+    b = pick.b;
+    L = pick.len;
+  } else {
+    const int64_t L64 = a.seq_lens[b];
+    L = (int)(L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64));
+  }
+  const int per = (int)split_chunk(L, a.n_split);
+  const int start = split * per;
+  const int end = min(L, start + per);
+  if (start >= end) return;  // empty split: nothing is written for it
+  const int ntiles = (end - start + kTile - 1) / kTile;
+
+  // ---- this lane's row (the MFMA column it holds), its mask over the drafts ----
+  const int rr = hg * 32 + col;  // row of the KV head's q_seq * group rows
+  const bool row_ok = rr < a.rows_kv;
+  const int qi = row_ok ? rr / a.group : 0;
+  const int64_t qrow = ((int64_t)b * a.q_seq + qi) * a.n_q + g * a.group + (row_ok ? rr - qi * a.group : 0);
+  const int draft0 = L - a.q_seq;  // position of draft token 0
+  uint32_t vis = ~0u;              // bit k: the row attends to draft token k
+  if (a.mask_mode == 3) {
+    vis = (2u << qi) - 1u;
+  } else if (a.mask_mode == 9) {
+    vis = 0;
+    const uint8_t* m = a.tree_mask + ((int64_t)b * a.q_seq + qi) * a.q_seq;
+    for (int k = 0; k < a.q_seq; ++k) vis |= (m[k] == 0 ? 1u : 0u) << k;
+  }
+
+  // ---- Q^T operand: 8 channels per lane per k-step (zero for padding rows) ----
+  u32x4 qreg[kKSteps];
+  {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + qrow * kRowB) + h;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = row_ok ? qp[2 * ks] : u32x4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int ks = 0; ks < kKSteps; ++ks) settle(qreg[ks]);
+
+  // ---- block-table slice of the split: lane k holds its k-th block id ----
+  const uint32_t bi_first = PAGED ? fast_div((uint32_t)start, a.bs_magic, a.bs_shift) : 0;
+  int tbl = 0;
+  if constexpr (PAGED) {
+    const int nblk = (int)fast_div((uint32_t)(end - 1), a.bs_magic, a.bs_shift) - (int)bi_first + 1;
+    tbl = lanes_from_scalar_loads(a.block_table + (int64_t)b * a.max_blocks + bi_first, nblk < 64 ? nblk : 64, 0);
+  }
+  auto block_id = [&](uint32_t bi) -> uint32_t {  // wave-uniform
+    const uint32_t k = bi - bi_first;
+    int v = k < 64 ? __builtin_amdgcn_readlane(tbl, k) : ld_uniform(a.block_table, (int64_t)b * a.max_blocks + bi);
+    return (uint32_t)(v < 0 ? 0 : (v >= a.num_blocks ? a.num_blocks - 1 : v));
+  };
+
+  const char* kbase = static_cast<const char*>(a.k);
+  const char* vbase = static_cast<const char*>(a.v);
+  const uint32_t ring_lds = lds_addr(ring);
+
+  // Queue tile j into ring slot `slot`: LDS chunk position P of the K (or V)
+  // tile holds row t = P / 16, chunk (P % 16) ^ swz(t) of token tstart + t
+  // (rows past the split's end repeat its last row).  Load i covers rows
+  // 4 i .. 4 i + 3; a tile's 32 tokens lie in at most 3 cache blocks.
+  auto queue_tile = [&](int j, int slot) {
+    const int tstart = start + kTile * j;
+    uint32_t tok0 = 0, adj0 = 0, adj1 = 0, adj2 = 0;
+    if constexpr (PAGED) {
+      const uint32_t bi0 = fast_div((uint32_t)tstart, a.bs_magic, a.bs_shift);
+      const uint32_t bil = fast_div((uint32_t)(end - 1), a.bs_magic, a.bs_shift);
+      tok0 = bi0 * (uint32_t)a.block_size;
+      adj0 = block_id(bi0);
+      adj1 = block_id(bi0 + 1 <= bil ? bi0 + 1 : bil);
+      adj2 = block_id(bi0 + 2 <= bil ? bi0 + 2 : bil);
+    }
+    const uint32_t dst = ring_lds + slot * kSlotB;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int t = 4 * i + (lane >> 4);
+      const int c = (lane & 15) ^ swz(t);
+      const uint32_t tok = (uint32_t)min(tstart + t, end - 1);
+      uint64_t row;
+      if constexpr (PAGED) {
+        const uint32_t bs = (uint32_t)a.block_size;
+        const uint32_t u = tok - tok0;
+        const uint32_t blk = u >= 2 * bs ? adj2 : (u >= bs ? adj1 : adj0);
+        const uint32_t slot_in = u - (u >= 2 * bs ? 2 * bs : (u >= bs ? bs : 0));
+        row = a.token_major ? ((uint64_t)blk * bs + slot_in) * (uint32_t)a.n_kv + (uint32_t)g
+                            : ((uint64_t)blk * (uint32_t)a.n_kv + (uint32_t)g) * bs + slot_in;
+      } else {
+        row = a.token_major ? ((uint64_t)b * (uint64_t)a.s_cap + tok) * (uint32_t)a.n_kv + (uint32_t)g
+                            : ((uint64_t)b * (uint32_t)a.n_kv + (uint32_t)g) * (uint64_t)a.s_cap + tok;
+      }
+      const uint64_t off = row * kRowB + 16u * (uint32_t)c;
+      dma16_lane(kbase + off, dst + 1024 * i);
+      dma16_lane(vbase + off, dst + kTileB + 1024 * i);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s)
+    if (s < ntiles) queue_tile(s, s);
+
+  // ---- per-lane LDS offsets within a slot ----
+  // S^T A operand: token t = lane % 32, chunk 2 ks + h of the K row
+  uint32_t offS[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) offS[j] = col * kRowB + 16 * ((2 * j + h) ^ swz(col));
+  // V^T A operand (transposing read): in 16-lane group gq, source lane s reads
+  // 4 channels of row 8 rd + 4 (gq >> 1) + s / 4 at chunk 4 odd + 2 (gq & 1) +
+  // (s % 4) / 2, half (s % 2); the read hands each lane 4 tokens of one channel
+  uint32_t offV[2][2];
+  {
+    const int s = lane & 15, gq = lane >> 4;
+    const int r = s >> 2, q = s & 3;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int t = 8 * rd + 4 * (gq >> 1) + r;
+#pragma unroll
+      for (int odd = 0; odd < 2; ++odd) {
+        const int x = 4 * odd + 2 * (gq & 1) + (q >> 1);
+        offV[odd][rd] = kTileB + t * kRowB + 16 * (x ^ swz(t)) + 8 * (q & 1);
+      }
+    }
+  }
+
+  float mref = kMrefInit, mtrue = kNegInf, lsum = 0.f, lsum_r = 0.f;
+  f32x16_t acc[kMTiles];
+#pragma unroll
+  for (int mt = 0; mt < kMTiles; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+
+  for (int i = 0; i < ntiles; ++i) {
+    // tile i has landed once only the loads of tiles queued after it remain
+    // (vmcnt retires in order)
+    if (i + 1 < ntiles) wait_vmem<2 * kLoads>();
+    else wait_vmem<0>();
+    // the slot of tile i - 1 is free: its operands were read during the last
+    // iteration, by this wave, before their MFMAs
+    if (i + kStages - 1 < ntiles) queue_tile(i + kStages - 1, (i + kStages - 1) % kStages);
+    const uint32_t slot = ring_lds + (i % kStages) * kSlotB;
+    const int tstart = start + kTile * i;
+
+    // ---- S^T = K . Q^T ----
+    f32x16_t sacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+    u32x4 kb[kKSteps];
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) kb[ks] = lds_read_b128(slot + offS[ks & 3] + 128 * (ks >> 2));
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) sacc = mfma<KV>(kb[ks], qreg[ks], sacc);
+
+    // ---- online softmax over this lane's row (column) ----
+    // accumulator register r holds token 8 (r / 4) + 4 h + r % 4 of the tile
+    float sv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sv[r] = sacc[r] * a.scale_log2;
+    if (tstart + kTile > end || tstart + kTile > draft0) {  // the split's tail, or draft tokens
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tok = tstart + 8 * (r >> 2) + 4 * h + (r & 3);
+        const uint32_t k = (uint32_t)(tok - draft0);  // draft index; huge for tokens before the drafts
+        const uint32_t kept = k < 32u ? (vis >> k) & 1u : 1u;
+        const uint32_t keep = (uint32_t)(tok < end) & kept;
+        sv[r] = keep ? sv[r] : kNegInf;  // a select, not a branch
+      }
+    }
+    float smax = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sv[r]);
+    smax = xor32_max(smax);  // the other 16 tokens of the column sit in lane ^ 32
+    mtrue = fmaxf(mtrue, smax);
+    if (__builtin_amdgcn_ballot_w64(smax > mref + kRescale)) {
+      const float mnew = smax > mref + kRescale ? smax : mref;
+      const float alpha = fast_exp2(mref - mnew);  // 0 on the first scores
+      lsum *= alpha;
+      lsum_r *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < kMTiles; ++mt) scale_acc(acc[mt], alpha);
+      mref = mnew;
+    }
+    // P^T operand: k-slot j of lane half h is accumulator register j (k-step
+    // 0) or 8 + j (k-step 1), rounded to the K/V dtype
+    u32x4 pb[2];
+    float pr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pf = fast_exp2(sv[r] - mref);  // <= 2^8; 0 for removed tokens
+      lsum += pf;
+      const uint16_t bits = round16<KV>(pf);
+      pr[r] = KV == kBF16 ? (float)__builtin_bit_cast(__bf16, bits) : (float)__builtin_bit_cast(_Float16, bits);
+      if (r & 1) pb[r >> 3][(r & 7) >> 1] |= (uint32_t)bits << 16;
+      else pb[r >> 3][(r & 7) >> 1] = bits;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lsum_r += pr[r];
+
+    // ---- O^T += V^T . P^T (MFMA n: k-step n / 4, row tile n % 4) ----
+    const uint32_t bV[2][2] = {{slot + offV[0][0], slot + offV[0][1]}, {slot + offV[1][0], slot + offV[1][1]}};
+    u32x4 vb[2 * kMTiles];
+#pragma unroll
+    for (int n = 0; n < 2 * kMTiles; ++n) {
+      const int kk = n / kMTiles, mt = n % kMTiles;
+      const uint32_t imm = kRowB * 16 * kk + 128 * (mt >> 1);
+      const s16x4_t lo = lds_read_tr16(bV[mt & 1][0] + imm);
+      const s16x4_t hi = lds_read_tr16(bV[mt & 1][1] + imm);
+      vb[n] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int n = 0; n < 2 * kMTiles; ++n) acc[n % kMTiles] = mfma<KV>(vb[n], pb[n / kMTiles], acc[n % kMTiles]);
+  }
+
+  // ---- partial triple: normalised out, true max, sum relative to it ----
+  const float ltot = xor32_sum(lsum);
+  const float lr = xor32_sum(lsum_r);
+  const float inv = lr > 0.f ? 1.f / lr : 0.f;  // 0: every token of the split removed for this row
+#pragma unroll
+  for (int mt = 0; mt < kMTiles; ++mt) scale_acc(acc[mt], inv);
+  if (row_ok) {
+    float* o = a.ws_o + (qrow * a.n_split + split) * kD;
+#pragma unroll
+    for (int mt = 0; mt < kMTiles; ++mt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4_t v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = acc[mt][4 * r4 + e];
+        *reinterpret_cast<f32x4_t*>(o + 32 * mt + 8 * r4 + 4 * h) = v;
+      }
+    if (h == 0) {
+      a.ws_m[qrow * a.n_split + split] = mtrue * kLn2;
+      a.ws_l[qrow * a.n_split + split] = ltot > 0.f ? ltot * fast_exp2(mref - mtrue) : 0.f;
+    }
+  }
+}
+
+template <int KV>
+hipError_t launch_kv(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
+  const int items = p.batch * p.n_kv * ((p.rows_kv + 31) / 32) * p.n_split;
+  if (items == 0) return hipSuccess;
+  if (p.paged)
+    launch_kernel(gqa_mfma_kernel<KV, true>, dim3(items), dim3(64), stream, ev, p, items);
+  else
+    launch_kernel(gqa_mfma_kernel<KV, false>, dim3(items), dim3(64), stream, ev, p, items);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim) {
+  return head_dim == kD && q_dtype == kv_dtype && (kv_dtype == kF16 || kv_dtype == kBF16);
+}
+
+hipError_t launch_gqa_mfma(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
+  if (!gqa_mfma_supported(p.q_dtype, p.kv_dtype, p.head_dim)) return hipErrorInvalidValue;
+  return p.kv_dtype == kBF16 ? launch_kv<kBF16>(p, stream, ev) : launch_kv<kF16>(p, stream, ev);
+}
+
+}  // namespace ifa

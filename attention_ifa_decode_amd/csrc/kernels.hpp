@@ -128,6 +128,10 @@ inline void launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, c
 }
 
 hipError_t launch_gqa_splitkv(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev = nullptr);
+// Multi-token decode on MFMA: one wave per (sequence, KV head, 32 query rows,
+// split); 16-bit K/V with head dim 128.
+bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim);
+hipError_t launch_gqa_mfma(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev = nullptr);
 hipError_t launch_mla_splitkv(const MlaLaunch& p, hipStream_t stream, const LaunchEvents* ev = nullptr);
 hipError_t launch_combine(const CombineLaunch& p, hipStream_t stream);
 // One workgroup: plan[r] = (sequence, clamped length) of the r-th longest
