@@ -77,15 +77,15 @@ int auto_splits_gqa(const ifa_decode_args* a, int64_t n_kv, int rows_kv, int gh,
   return (int)n;
 }
 
-// One-wave workgroups of the multi-token MFMA path: about 2048 of them, each
-// split at least 512 tokens long.
+// One-wave workgroups of the MFMA path: about 2048 of them, each split at
+// least 384 tokens long (measured over batch 1 to 64 and lengths 512 to 32768).
 int auto_splits_mfma(const ifa_decode_args* a, int64_t n_kv, int rows_kv, int64_t max_len) {
   const int64_t per_split = a->batch * n_kv * ((rows_kv + 31) / 32);
   int64_t n = (8LL * kTargetCUs + per_split - 1) / per_split;
-  const int64_t by_len = (max_len + 511) / 512;
+  const int64_t by_len = (max_len + 383) / 384;
   if (n > by_len) n = by_len;
   if (n < 1) n = 1;
-  if (n > 64) n = 64;
+  if (n > 128) n = 128;
   return (int)n;
 }
 
@@ -226,9 +226,9 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
     p.heads_per_wg = gh;
     if (!ifa::gqa_supported(a->q_dtype, a->kv_dtype, (int)a->qk_dim, gh))
       return fail(IFA_ERR_PARAM_INVALID, "dtype combination (q %d, kv %d) not supported", a->q_dtype, a->kv_dtype);
-    // several query tokens: the rows of a KV head go to the matrix cores in
-    // groups of 32, one wave each
-    p.mfma = q_seq > 1 && ifa::gqa_mfma_supported(a->q_dtype, a->kv_dtype, (int)a->qk_dim);
+    // 16-bit K/V with head dim 128: the rows of a KV head (any number of
+    // query tokens) go to the matrix cores in groups of 32, one wave each
+    p.mfma = ifa::gqa_mfma_supported(a->q_dtype, a->kv_dtype, (int)a->qk_dim);
     if (p.mfma) {
       p.heads_per_wg = 32;
       p.n_split = a->num_splits ? a->num_splits : auto_splits_mfma(a, n_kv, rows_kv, max_len);

@@ -43,11 +43,11 @@ constexpr int kTileB = kTile * kRowB;    // 8 KB of K (and of V) per tile
 constexpr int kLoads = kTileB / 1024;    // DMA instructions per K (and per V) tile
 constexpr int kKSteps = kD / 16;         // MFMA k-steps of S^T
 constexpr int kMTiles = kD / 32;         // row tiles of O^T
-constexpr int kStages = 3;               // tiles in the ring
+constexpr int kStages = 2;               // tiles in the ring
 constexpr int kSlotB = 2 * kTileB;       // K then V
 constexpr float kRescale = 8.f;
 constexpr float kMrefInit = -1e30f;
-static_assert(2 * kLoads * (kStages - 1) <= 63, "vmcnt");
+static_assert(2 * kLoads * (kStages - 1) <= 63 && kStages >= 2 && kStages <= 3, "vmcnt, ring");
 
 __device__ __forceinline__ int swz(int t) { return (2 * (t & 3) + ((t >> 2) & 1)) ^ (2 * ((t >> 3) & 1)); }
 
@@ -159,10 +159,17 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
 
   // ---- Q^T operand: 8 channels per lane per k-step (zero for padding rows) ----
   u32x4 qreg[kKSteps];
-  {
+  if ((reinterpret_cast<uintptr_t>(a.q) & 15) == 0) {  // 16-byte loads
     const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + qrow * kRowB) + h;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = row_ok ? qp[2 * ks] : u32x4{0u, 0u, 0u, 0u};
+  } else {  // a query buffer aligned to its element only
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.q) + qrow * kRowB) + 8 * h;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        qreg[ks][w] = row_ok ? (uint32_t)qp[16 * ks + 2 * w] | ((uint32_t)qp[16 * ks + 2 * w + 1] << 16) : 0u;
   }
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) settle(qreg[ks]);
@@ -258,12 +265,20 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
 
   for (int i = 0; i < ntiles; ++i) {
-    // tile i has landed once only the loads of tiles queued after it remain
-    // (vmcnt retires in order)
-    if (i + 1 < ntiles) wait_vmem<2 * kLoads>();
-    else wait_vmem<0>();
-    // the slot of tile i - 1 is free: its operands were read during the last
-    // iteration, by this wave, before their MFMAs
+    // tile i has landed once only the loads of the tiles queued after it
+    // (at most kStages - 2) remain (vmcnt retires in order)
+    const int after = min(kStages - 2, ntiles - 1 - i);
+    if constexpr (kStages == 3) {
+      if (after >= 1) wait_vmem<2 * kLoads>();
+      else wait_vmem<0>();
+    } else {
+      wait_vmem<0>();
+    }
+    // tile i + kStages - 1 goes into the slot of tile i - 1, whose operands
+    // this wave read during the last iteration, before their MFMAs.  Queued
+    // after the wait: with two slots one tile is in flight while this one is
+    // computed, which measured faster than queueing it before the wait (two
+    // in flight) or a third slot.
     if (i + kStages - 1 < ntiles) queue_tile(i + kStages - 1, (i + kStages - 1) % kStages);
     const uint32_t slot = ring_lds + (i % kStages) * kSlotB;
     const int tstart = start + kTile * i;
