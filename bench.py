@@ -39,8 +39,9 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 MALL_BYTES = 256 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_splitkv_c3_bf16_paged_traffic.txt")
-KERNEL_SOURCES = ["attention_ifa_decode_amd/csrc/decode_gqa.hip", "attention_ifa_decode_amd/csrc/common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_mfma_c3_bf16_paged_traffic.txt")
+# the kernel of the paged bf16 GQA workload (16-bit K/V, head dim 128: the MFMA path)
+KERNEL_SOURCES = ["attention_ifa_decode_amd/csrc/decode_spec.hip", "attention_ifa_decode_amd/csrc/common.hpp"]
 
 
 def kernel_source_hash() -> str:
@@ -57,6 +58,18 @@ def kernel_source_hash() -> str:
         text = re.sub(r"//[^\n]*", "", text)
         h.update(re.sub(r"\s+", "", text).encode())
     return h.hexdigest()[:16]
+
+
+def kernel_name(w) -> str:
+    """The split-KV kernel a workload runs: MLA shape on MFMA, 16-bit K/V
+    with head dim 128 on the MFMA GQA kernel, the rest on the VALU kernel."""
+    import torch
+
+    if w.qk_dim == 576:
+        return "mla_splitkv_kernel"
+    if w.qk_dim == 128 and w.kv_dtype in (torch.float16, torch.bfloat16):
+        return "gqa_mfma_kernel"
+    return "gqa_splitkv_kernel"
 
 
 def read_traffic(config_idx: int):
@@ -260,7 +273,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gqa_splitkv_kernel" if w.qk_dim != 576 else "mla_splitkv_kernel",
+            "kernel": kernel_name(w),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
