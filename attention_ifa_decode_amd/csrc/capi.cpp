@@ -279,7 +279,7 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
   // and MLA workgroups rank the lengths themselves, which costs less than the
   // extra launch there.
   const bool longest_first = a->batch <= ifa::kLongestFirstMaxBatch;
-  const bool use_plan = longest_first && p.path == Path::kGqa && a->kv_dtype == IFA_I8;
+  const bool use_plan = longest_first && p.path == Path::kGqa && a->kv_dtype == IFA_I8 && !p.mfma;
   int2* plan = nullptr;
   if (use_plan) {
     plan = reinterpret_cast<int2*>(w + p.off_plan);

@@ -10,9 +10,9 @@
 //
 // Work decomposition.  One workgroup = one wave = one (sequence, KV head,
 // group of up to 32 rows, split); rows are query token major.  The split's
-// tokens stream in tiles of 32 through a private LDS ring of STAGES slots,
-// each slot the tile's K rows (8 KB) then its V rows (8 KB), loaded straight
-// from HBM with global_load_lds_dwordx4.  Per tile:
+// tokens stream in tiles of 32 through a private LDS ring of 2 slots,
+// each slot the tile's K rows then its V rows (8 KB each for 16-bit K/V, 4 KB
+// for int8), loaded straight from HBM with global_load_lds_dwordx4.  Per tile:
 //   S^T (32 tokens x 32 rows) = K (32 x 128) . Q^T (128 x 32): 8 MFMAs, K from
 //       LDS (ds_read_b128), Q^T in registers for the item;
 //   online softmax per row (a lane holds one row column and 16 tokens), the
@@ -24,6 +24,14 @@
 //       weights; the partial's sum uses the fp32 weights).
 // The operand and accumulator layouts are those of the MLA kernel, on
 // 256-byte rows: row t keeps its 16-byte chunk c at position c ^ swz(t).
+//
+// int8 K/V (antiquant x_hat = (x + offset) * scale, per channel or per
+// tensor): the stored bytes become the exact fp16 values 1152 + x with one
+// byte permute (fp16 has unit spacing in [1024, 2048)), so both products run
+// on fp16 MFMAs.  The K scale is folded into q (q' = q * scale_K, rounded to
+// fp16) and the K offset into a per-row constant sum_d q'_d (offset_d - 1152);
+// each V tile is widened into an fp16 copy in LDS for the transposing read,
+// and the V scale and offset are applied to the normalised output.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -37,17 +45,29 @@ typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kD = 128;
-constexpr int kRowB = kD * 2;            // bytes of one token row of one KV head
 constexpr int kTile = 32;                // tokens per tile
-constexpr int kTileB = kTile * kRowB;    // 8 KB of K (and of V) per tile
-constexpr int kLoads = kTileB / 1024;    // DMA instructions per K (and per V) tile
 constexpr int kKSteps = kD / 16;         // MFMA k-steps of S^T
 constexpr int kMTiles = kD / 32;         // row tiles of O^T
-constexpr int kStages = 2;               // tiles in the ring
-constexpr int kSlotB = 2 * kTileB;       // K then V
+constexpr int kRowB16 = kD * 2;          // bytes of a 16-bit row (and of the int8 V tile's fp16 copy)
 constexpr float kRescale = 8.f;
 constexpr float kMrefInit = -1e30f;
-static_assert(2 * kLoads * (kStages - 1) <= 63 && kStages >= 2 && kStages <= 3, "vmcnt, ring");
+
+template <int KV>
+struct SpecShape {
+  static constexpr int ESZ = KV == kI8 ? 1 : 2;
+  // tiles in the ring: one tile is computed while the next one loads (a
+  // third slot, two tiles in flight, measured slower for both widths)
+  static constexpr int STAGES = 2;
+  static constexpr int RB = kD * ESZ;       // bytes of one token row of one KV head
+  static constexpr int CPR = RB / 16;       // 16-byte chunks per row
+  static constexpr int TB = kTile * RB;     // bytes of the K (and of the V) tile
+  static constexpr int LT = TB / 1024;      // DMA instructions per K (and per V) tile
+  static constexpr int SLOT = 2 * TB;       // K then V
+  static constexpr int CONV = KV == kI8 ? kTile * kRowB16 : 0;  // fp16 copy of the int8 V tile
+  static constexpr int SMEM = STAGES * SLOT + CONV;
+  static constexpr int MK = KV == kBF16 ? kBF16 : kF16;  // MFMA operand type
+  static_assert(2 * LT * (STAGES - 1) <= 63 && STAGES >= 2 && STAGES <= 3, "vmcnt, ring");
+};
 
 __device__ __forceinline__ int swz(int t) { return (2 * (t & 3) + ((t >> 2) & 1)) ^ (2 * ((t >> 3) & 1)); }
 
@@ -71,6 +91,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 __device__ __forceinline__ u32x4 lds_read_b128(uint32_t addr) {
   return *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)addr;
+}
+
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+__device__ __forceinline__ u32x2 lds_read_b64(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) u32x2*)(uintptr_t)addr;
+}
+
+__device__ __forceinline__ void lds_write_b128(uint32_t addr, const u32x4& v) {
+  *(__attribute__((address_space(3))) u32x4*)(uintptr_t)addr = v;
 }
 
 __device__ __forceinline__ s16x4_t lds_read_tr16(uint32_t addr) {
@@ -109,9 +139,19 @@ __device__ __forceinline__ void scale_acc(f32x16_t& v, float s) {
   }
 }
 
-template <int KV, bool PAGED>
+// int8 bytes of one dword -> the fp16 pairs 1152 + x of bytes (0, 1) and (2, 3)
+__device__ __forceinline__ u32x2 widen_i8(uint32_t w) {
+  const uint32_t b = w ^ 0x80808080u;
+  return u32x2{__builtin_amdgcn_perm(0x64646464u, b, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u)};
+}
+
+template <int QT, int KV, bool PAGED>
 __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int work_items) {
-  __shared__ __attribute__((aligned(16))) char ring[kStages * kSlotB];
+  using S = SpecShape<KV>;
+  constexpr int RB = S::RB, CPR = S::CPR, TB = S::TB, LT = S::LT, SLOT = S::SLOT, MK = S::MK;
+  constexpr int kStages = S::STAGES;
+  constexpr bool I8 = KV == kI8;
+  __shared__ __attribute__((aligned(16))) char ring[S::SMEM];
 
   const int lane = threadIdx.x;
   const int h = lane >> 5;  // which half of an MFMA k-range this lane feeds
@@ -157,14 +197,34 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     for (int k = 0; k < a.q_seq; ++k) vis |= (m[k] == 0 ? 1u : 0u) << k;
   }
 
-  // ---- Q^T operand: 8 channels per lane per k-step (zero for padding rows) ----
+  // ---- Q^T operand: channels 16 ks + 8 h .. + 7 per k-step (zero for padding rows) ----
   u32x4 qreg[kKSteps];
-  if ((reinterpret_cast<uintptr_t>(a.q) & 15) == 0) {  // 16-byte loads
-    const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + qrow * kRowB) + h;
+  float kconst = 0.f;  // int8: sum_d q'_d (offset_d - 1152) over the row
+  if constexpr (I8) {
+    // q' = q * scale_K rounded to fp16, and this lane's half of the constant
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t pair = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int d = 16 * ks + 8 * h + 2 * w + e;
+          const int kq = g * a.aq_stride_g + d * a.aq_stride_d;  // K parameters (index 0)
+          const _Float16 qh = row_ok ? (_Float16)(load_as_f32<QT>(a.q, qrow * kD + d) * a.aq_scale[kq]) : (_Float16)0.f;
+          part = fmaf((float)qh, a.aq_offset[kq] - 1152.f, part);
+          pair |= (uint32_t)__builtin_bit_cast(uint16_t, qh) << (16 * e);
+        }
+        qreg[ks][w] = pair;
+      }
+    kconst = xor32_sum(part);  // lanes l and l ^ 32 hold the two halves of the channels
+  } else if ((reinterpret_cast<uintptr_t>(a.q) & 15) == 0) {  // 16-byte loads
+    const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + qrow * RB) + h;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = row_ok ? qp[2 * ks] : u32x4{0u, 0u, 0u, 0u};
   } else {  // a query buffer aligned to its element only
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.q) + qrow * kRowB) + 8 * h;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.q) + qrow * RB) + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks)
 #pragma unroll
@@ -173,6 +233,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
   }
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) settle(qreg[ks]);
+  settle(kconst);
 
   // ---- block-table slice of the split: lane k holds its k-th block id ----
   const uint32_t bi_first = PAGED ? fast_div((uint32_t)start, a.bs_magic, a.bs_shift) : 0;
@@ -190,11 +251,12 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
   const char* kbase = static_cast<const char*>(a.k);
   const char* vbase = static_cast<const char*>(a.v);
   const uint32_t ring_lds = lds_addr(ring);
+  const uint32_t conv_lds = ring_lds + kStages * SLOT;  // int8: fp16 copy of the current V tile
 
   // Queue tile j into ring slot `slot`: LDS chunk position P of the K (or V)
-  // tile holds row t = P / 16, chunk (P % 16) ^ swz(t) of token tstart + t
-  // (rows past the split's end repeat its last row).  Load i covers rows
-  // 4 i .. 4 i + 3; a tile's 32 tokens lie in at most 3 cache blocks.
+  // tile holds row t = P / CPR, chunk (P % CPR) ^ swz(t) of token tstart + t
+  // (rows past the split's end repeat its last row).  A tile's 32 tokens lie
+  // in at most 3 cache blocks.
   auto queue_tile = [&](int j, int slot) {
     const int tstart = start + kTile * j;
     uint32_t tok0 = 0, adj0 = 0, adj1 = 0, adj2 = 0;
@@ -206,11 +268,12 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
       adj1 = block_id(bi0 + 1 <= bil ? bi0 + 1 : bil);
       adj2 = block_id(bi0 + 2 <= bil ? bi0 + 2 : bil);
     }
-    const uint32_t dst = ring_lds + slot * kSlotB;
+    const uint32_t dst = ring_lds + slot * SLOT;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int t = 4 * i + (lane >> 4);
-      const int c = (lane & 15) ^ swz(t);
+    for (int i = 0; i < LT; ++i) {
+      const int P = 64 * i + lane;
+      const int t = P / CPR;
+      const int c = (P % CPR) ^ swz(t);
       const uint32_t tok = (uint32_t)min(tstart + t, end - 1);
       uint64_t row;
       if constexpr (PAGED) {
@@ -224,9 +287,9 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
         row = a.token_major ? ((uint64_t)b * (uint64_t)a.s_cap + tok) * (uint32_t)a.n_kv + (uint32_t)g
                             : ((uint64_t)b * (uint32_t)a.n_kv + (uint32_t)g) * (uint64_t)a.s_cap + tok;
       }
-      const uint64_t off = row * kRowB + 16u * (uint32_t)c;
+      const uint64_t off = row * RB + 16u * (uint32_t)c;
       dma16_lane(kbase + off, dst + 1024 * i);
-      dma16_lane(vbase + off, dst + kTileB + 1024 * i);
+      dma16_lane(vbase + off, dst + TB + 1024 * i);
     }
   };
 
@@ -235,13 +298,16 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     if (s < ntiles) queue_tile(s, s);
 
   // ---- per-lane LDS offsets within a slot ----
-  // S^T A operand: token t = lane % 32, chunk 2 ks + h of the K row
-  uint32_t offS[4];
+  // S^T A operand: token t = lane % 32, channels 16 ks + 8 h .. + 7: chunk
+  // 2 ks + h of a 16-bit row, or the half h of chunk ks of an int8 row
+  uint32_t offS[kKSteps];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) offS[j] = col * kRowB + 16 * ((2 * j + h) ^ swz(col));
-  // V^T A operand (transposing read): in 16-lane group gq, source lane s reads
-  // 4 channels of row 8 rd + 4 (gq >> 1) + s / 4 at chunk 4 odd + 2 (gq & 1) +
-  // (s % 4) / 2, half (s % 2); the read hands each lane 4 tokens of one channel
+  for (int ks = 0; ks < kKSteps; ++ks)
+    offS[ks] = I8 ? col * RB + 16 * (ks ^ swz(col)) + 8 * h : col * RB + 16 * ((2 * ks + h) ^ swz(col));
+  // V^T A operand (transposing read) on 16-bit rows (the int8 V tile's fp16
+  // copy): in 16-lane group gq, source lane s reads 4 channels of row
+  // 8 rd + 4 (gq >> 1) + s / 4 at chunk 4 odd + 2 (gq & 1) + (s % 4) / 2, half
+  // (s % 2); the read hands each lane 4 tokens of one channel
   uint32_t offV[2][2];
   {
     const int s = lane & 15, gq = lane >> 4;
@@ -252,7 +318,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
 #pragma unroll
       for (int odd = 0; odd < 2; ++odd) {
         const int x = 4 * odd + 2 * (gq & 1) + (q >> 1);
-        offV[odd][rd] = kTileB + t * kRowB + 16 * (x ^ swz(t)) + 8 * (q & 1);
+        offV[odd][rd] = t * kRowB16 + 16 * (x ^ swz(t)) + 8 * (q & 1);
       }
     }
   }
@@ -269,7 +335,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     // (at most kStages - 2) remain (vmcnt retires in order)
     const int after = min(kStages - 2, ntiles - 1 - i);
     if constexpr (kStages == 3) {
-      if (after >= 1) wait_vmem<2 * kLoads>();
+      if (after >= 1) wait_vmem<2 * LT>();
       else wait_vmem<0>();
     } else {
       wait_vmem<0>();
@@ -280,7 +346,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     // computed, which measured faster than queueing it before the wait (two
     // in flight) or a third slot.
     if (i + kStages - 1 < ntiles) queue_tile(i + kStages - 1, (i + kStages - 1) % kStages);
-    const uint32_t slot = ring_lds + (i % kStages) * kSlotB;
+    const uint32_t slot = ring_lds + (i % kStages) * SLOT;
     const int tstart = start + kTile * i;
 
     // ---- S^T = K . Q^T ----
@@ -289,15 +355,45 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
     u32x4 kb[kKSteps];
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) kb[ks] = lds_read_b128(slot + offS[ks & 3] + 128 * (ks >> 2));
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      if constexpr (I8) {
+        const u32x2 x = lds_read_b64(slot + offS[ks]);
+        const u32x2 w0 = widen_i8(x[0]), w1 = widen_i8(x[1]);
+        kb[ks] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+      } else {
+        kb[ks] = lds_read_b128(slot + offS[ks]);
+      }
+    }
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) sacc = mfma<KV>(kb[ks], qreg[ks], sacc);
+    for (int ks = 0; ks < kKSteps; ++ks) sacc = mfma<MK>(kb[ks], qreg[ks], sacc);
+
+    // int8: widen this V tile into its fp16 copy (16-bit row layout): lane
+    // takes positions P = lane + 64 k of the int8 tile, row t = P / 8, chunk
+    // c = (P % 8) ^ swz(t) = channels 16 c .. 16 c + 15, which become fp16
+    // chunks 2 c and 2 c + 1 of row t
+    if constexpr (I8) {
+#pragma unroll
+      for (int k = 0; k < TB / 1024; ++k) {
+        const int P = lane + 64 * k;
+        const int t = P >> 3;
+        const int c = (P & 7) ^ swz(t);
+        const u32x4 x = lds_read_b128(slot + TB + 16 * P);
+        const u32x2 w0 = widen_i8(x[0]), w1 = widen_i8(x[1]), w2 = widen_i8(x[2]), w3 = widen_i8(x[3]);
+        const u32x4 lo = {w0[0], w0[1], w1[0], w1[1]}, hi = {w2[0], w2[1], w3[0], w3[1]};
+        lds_write_b128(conv_lds + t * kRowB16 + 16 * ((2 * c) ^ swz(t)), lo);
+        lds_write_b128(conv_lds + t * kRowB16 + 16 * ((2 * c + 1) ^ swz(t)), hi);
+      }
+      // the reads below see this wave's writes (LDS operations of a wave
+      // complete in order)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    }
 
     // ---- online softmax over this lane's row (column) ----
     // accumulator register r holds token 8 (r / 4) + 4 h + r % 4 of the tile
     float sv[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sv[r] = sacc[r] * a.scale_log2;
+    for (int r = 0; r < 16; ++r) sv[r] = (sacc[r] + kconst) * a.scale_log2;
     if (tstart + kTile > end || tstart + kTile > draft0) {  // the split's tail, or draft tokens
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -323,15 +419,15 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
       mref = mnew;
     }
     // P^T operand: k-slot j of lane half h is accumulator register j (k-step
-    // 0) or 8 + j (k-step 1), rounded to the K/V dtype
+    // 0) or 8 + j (k-step 1), rounded to the MFMA operand type
     u32x4 pb[2];
     float pr[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float pf = fast_exp2(sv[r] - mref);  // <= 2^8; 0 for removed tokens
       lsum += pf;
-      const uint16_t bits = round16<KV>(pf);
-      pr[r] = KV == kBF16 ? (float)__builtin_bit_cast(__bf16, bits) : (float)__builtin_bit_cast(_Float16, bits);
+      const uint16_t bits = round16<MK>(pf);
+      pr[r] = MK == kBF16 ? (float)__builtin_bit_cast(__bf16, bits) : (float)__builtin_bit_cast(_Float16, bits);
       if (r & 1) pb[r >> 3][(r & 7) >> 1] |= (uint32_t)bits << 16;
       else pb[r >> 3][(r & 7) >> 1] = bits;
     }
@@ -339,18 +435,19 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     for (int r = 0; r < 16; ++r) lsum_r += pr[r];
 
     // ---- O^T += V^T . P^T (MFMA n: k-step n / 4, row tile n % 4) ----
-    const uint32_t bV[2][2] = {{slot + offV[0][0], slot + offV[0][1]}, {slot + offV[1][0], slot + offV[1][1]}};
+    const uint32_t vt = I8 ? conv_lds : slot + TB;
+    const uint32_t bV[2][2] = {{vt + offV[0][0], vt + offV[0][1]}, {vt + offV[1][0], vt + offV[1][1]}};
     u32x4 vb[2 * kMTiles];
 #pragma unroll
     for (int n = 0; n < 2 * kMTiles; ++n) {
       const int kk = n / kMTiles, mt = n % kMTiles;
-      const uint32_t imm = kRowB * 16 * kk + 128 * (mt >> 1);
+      const uint32_t imm = kRowB16 * 16 * kk + 128 * (mt >> 1);
       const s16x4_t lo = lds_read_tr16(bV[mt & 1][0] + imm);
       const s16x4_t hi = lds_read_tr16(bV[mt & 1][1] + imm);
       vb[n] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
-    for (int n = 0; n < 2 * kMTiles; ++n) acc[n % kMTiles] = mfma<KV>(vb[n], pb[n / kMTiles], acc[n % kMTiles]);
+    for (int n = 0; n < 2 * kMTiles; ++n) acc[n % kMTiles] = mfma<MK>(vb[n], pb[n / kMTiles], acc[n % kMTiles]);
   }
 
   // ---- partial triple: normalised out, true max, sum relative to it ----
@@ -365,10 +462,19 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     for (int mt = 0; mt < kMTiles; ++mt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * mt + 8 * r4 + 4 * h;
         f32x4_t v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[mt][4 * r4 + e];
-        *reinterpret_cast<f32x4_t*>(o + 32 * mt + 8 * r4 + 4 * h) = v;
+        if constexpr (I8) {
+          // P V ran on 1152 + x: x_hat = (x + offset) * scale per channel (index 1)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int vq = a.aq_stride_kv + g * a.aq_stride_g + (d + e) * a.aq_stride_d;
+            v[e] = a.aq_scale[vq] * (v[e] - 1152.f + a.aq_offset[vq]);
+          }
+        }
+        *reinterpret_cast<f32x4_t*>(o + d) = v;
       }
     if (h == 0) {
       a.ws_m[qrow * a.n_split + split] = mtrue * kLn2;
@@ -377,26 +483,35 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
   }
 }
 
-template <int KV>
+template <int QT, int KV>
 hipError_t launch_kv(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
   const int items = p.batch * p.n_kv * ((p.rows_kv + 31) / 32) * p.n_split;
   if (items == 0) return hipSuccess;
   if (p.paged)
-    launch_kernel(gqa_mfma_kernel<KV, true>, dim3(items), dim3(64), stream, ev, p, items);
+    launch_kernel(gqa_mfma_kernel<QT, KV, true>, dim3(items), dim3(64), stream, ev, p, items);
   else
-    launch_kernel(gqa_mfma_kernel<KV, false>, dim3(items), dim3(64), stream, ev, p, items);
+    launch_kernel(gqa_mfma_kernel<QT, KV, false>, dim3(items), dim3(64), stream, ev, p, items);
   return hipGetLastError();
 }
 
 }  // namespace
 
 bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim) {
-  return head_dim == kD && q_dtype == kv_dtype && (kv_dtype == kF16 || kv_dtype == kBF16);
+  if (head_dim != kD) return false;
+  if (kv_dtype == kI8) return q_dtype == kF32 || q_dtype == kF16 || q_dtype == kBF16;
+  return q_dtype == kv_dtype && (kv_dtype == kF16 || kv_dtype == kBF16);
 }
 
 hipError_t launch_gqa_mfma(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
   if (!gqa_mfma_supported(p.q_dtype, p.kv_dtype, p.head_dim)) return hipErrorInvalidValue;
-  return p.kv_dtype == kBF16 ? launch_kv<kBF16>(p, stream, ev) : launch_kv<kF16>(p, stream, ev);
+  if (p.kv_dtype == kI8) {
+    switch (p.q_dtype) {
+      case kF32: return launch_kv<kF32, kI8>(p, stream, ev);
+      case kF16: return launch_kv<kF16, kI8>(p, stream, ev);
+      default: return launch_kv<kBF16, kI8>(p, stream, ev);
+    }
+  }
+  return p.kv_dtype == kBF16 ? launch_kv<kBF16, kBF16>(p, stream, ev) : launch_kv<kF16, kF16>(p, stream, ev);
 }
 
 }  // namespace ifa
