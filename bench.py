@@ -61,13 +61,13 @@ def kernel_source_hash() -> str:
 
 
 def kernel_name(w) -> str:
-    """The split-KV kernel a workload runs: MLA shape on MFMA, 16-bit K/V
-    with head dim 128 on the MFMA GQA kernel, the rest on the VALU kernel."""
+    """The split-KV kernel a workload runs: MLA shape on MFMA, 16-bit or int8
+    K/V with head dim 128 on the MFMA GQA kernel, the rest on the VALU kernel."""
     import torch
 
     if w.qk_dim == 576:
         return "mla_splitkv_kernel"
-    if w.qk_dim == 128 and w.kv_dtype in (torch.float16, torch.bfloat16):
+    if w.qk_dim == 128 and w.kv_dtype in (torch.float16, torch.bfloat16, torch.int8):
         return "gqa_mfma_kernel"
     return "gqa_splitkv_kernel"
 
