@@ -63,8 +63,7 @@ struct SpecShape {
   static constexpr int TB = kTile * RB;     // bytes of the K (and of the V) tile
   static constexpr int LT = TB / 1024;      // DMA instructions per K (and per V) tile
   static constexpr int SLOT = 2 * TB;       // K then V
-  static constexpr int CONV = KV == kI8 ? kTile * kRowB16 : 0;  // fp16 copy of the int8 V tile
-  static constexpr int SMEM = STAGES * SLOT + CONV;
+  static constexpr int SMEM = STAGES * SLOT;
   static constexpr int MK = KV == kBF16 ? kBF16 : kF16;  // MFMA operand type
   static_assert(2 * LT * (STAGES - 1) <= 63 && STAGES >= 2 && STAGES <= 3, "vmcnt, ring");
 };
@@ -251,7 +250,6 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
   const char* kbase = static_cast<const char*>(a.k);
   const char* vbase = static_cast<const char*>(a.v);
   const uint32_t ring_lds = lds_addr(ring);
-  const uint32_t conv_lds = ring_lds + kStages * SLOT;  // int8: fp16 copy of the current V tile
 
   // Queue tile j into ring slot `slot`: LDS chunk position P of the K (or V)
   // tile holds row t = P / CPR, chunk (P % CPR) ^ swz(t) of token tstart + t
@@ -367,24 +365,27 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) sacc = mfma<MK>(kb[ks], qreg[ks], sacc);
 
-    // int8: widen this V tile into its fp16 copy (16-bit row layout): lane
-    // takes positions P = lane + 64 k of the int8 tile, row t = P / 8, chunk
-    // c = (P % 8) ^ swz(t) = channels 16 c .. 16 c + 15, which become fp16
-    // chunks 2 c and 2 c + 1 of row t
+    // int8: widen this V tile into an fp16 copy in 16-bit row layout, written
+    // over the whole slot (K and V, 2 x 4 KB), whose K operands are in
+    // registers by now.  All int8 chunks are read before any write (a wave's
+    // LDS operations complete in order).  Lane takes positions P = lane + 64 k
+    // of the int8 V tile: row t = P / 8, chunk c = (P % 8) ^ swz(t) = channels
+    // 16 c .. 16 c + 15, which become fp16 chunks 2 c and 2 c + 1 of row t.
     if constexpr (I8) {
+      u32x4 x[TB / 1024];
+#pragma unroll
+      for (int k = 0; k < TB / 1024; ++k) x[k] = lds_read_b128(slot + TB + 16 * (lane + 64 * k));
 #pragma unroll
       for (int k = 0; k < TB / 1024; ++k) {
         const int P = lane + 64 * k;
         const int t = P >> 3;
         const int c = (P & 7) ^ swz(t);
-        const u32x4 x = lds_read_b128(slot + TB + 16 * P);
-        const u32x2 w0 = widen_i8(x[0]), w1 = widen_i8(x[1]), w2 = widen_i8(x[2]), w3 = widen_i8(x[3]);
+        const u32x2 w0 = widen_i8(x[k][0]), w1 = widen_i8(x[k][1]), w2 = widen_i8(x[k][2]), w3 = widen_i8(x[k][3]);
         const u32x4 lo = {w0[0], w0[1], w1[0], w1[1]}, hi = {w2[0], w2[1], w3[0], w3[1]};
-        lds_write_b128(conv_lds + t * kRowB16 + 16 * ((2 * c) ^ swz(t)), lo);
-        lds_write_b128(conv_lds + t * kRowB16 + 16 * ((2 * c + 1) ^ swz(t)), hi);
+        lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c) ^ swz(t)), lo);
+        lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c + 1) ^ swz(t)), hi);
       }
-      // the reads below see this wave's writes (LDS operations of a wave
-      // complete in order)
+      // the reads below see this wave's writes
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
     }
@@ -435,7 +436,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     for (int r = 0; r < 16; ++r) lsum_r += pr[r];
 
     // ---- O^T += V^T . P^T (MFMA n: k-step n / 4, row tile n % 4) ----
-    const uint32_t vt = I8 ? conv_lds : slot + TB;
+    const uint32_t vt = I8 ? slot : slot + TB;
     const uint32_t bV[2][2] = {{vt + offV[0][0], vt + offV[0][1]}, {vt + offV[1][0], vt + offV[1][1]}};
     u32x4 vb[2 * kMTiles];
 #pragma unroll
