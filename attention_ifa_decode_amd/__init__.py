@@ -49,6 +49,7 @@ _DTYPE_CODE = {torch.float32: IFA_F32, torch.float16: IFA_F16, torch.bfloat16: I
 EXPORTED = (
     "ifa_decode_workspace_size",
     "ifa_decode_num_splits",
+    "ifa_decode_split_mode",
     "ifa_decode",
     "ifa_decode_splitkv",
     "ifa_decode_splitkv_timed",
@@ -117,6 +118,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     args_p = ctypes.POINTER(DecodeArgs)
     lib.ifa_decode_workspace_size.argtypes = [args_p, ctypes.POINTER(SZ)]
     lib.ifa_decode_num_splits.argtypes = [args_p, ctypes.POINTER(I32)]
+    lib.ifa_decode_split_mode.argtypes = [args_p, ctypes.POINTER(I32)]
     for fn in (lib.ifa_decode, lib.ifa_decode_splitkv):
         fn.argtypes = [args_p, P, SZ, P]
     lib.ifa_decode_splitkv_timed.argtypes = [args_p, P, SZ, P, P, P]
@@ -127,7 +129,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ifa_paged_block_count.restype = I64
     lib.ifa_last_error.argtypes = []
     lib.ifa_last_error.restype = ctypes.c_char_p
-    for name in ("ifa_decode_workspace_size", "ifa_decode_num_splits", "ifa_decode", "ifa_decode_splitkv",
+    for name in ("ifa_decode_workspace_size", "ifa_decode_num_splits", "ifa_decode_split_mode", "ifa_decode",
+                 "ifa_decode_splitkv",
                  "ifa_decode_splitkv_timed", "ifa_decode_combine", "attn_update", "ifa_kv_cache_write"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
@@ -253,6 +256,9 @@ class DecodeCall:
         ns = ctypes.c_int32(0)
         _check(lib.ifa_decode_num_splits(ctypes.byref(a), ctypes.byref(ns)))
         self.num_splits = ns.value
+        bal = ctypes.c_int32(0)
+        _check(lib.ifa_decode_split_mode(ctypes.byref(a), ctypes.byref(bal)))
+        self.balanced = bool(bal.value)
         self.workspace_bytes = sz.value
         self.workspace = torch.empty(max(1, sz.value), dtype=torch.uint8, device=dev)
         # keep the inputs alive as long as the call object
@@ -288,7 +294,10 @@ class DecodeCall:
     def partials(self):
         """Views of the workspace after ``splitkv()``: (attn_out, softmax_max,
         softmax_sum) with shapes (B, N_q, n, v_dim), (B, N_q, n), (B, N_q, n);
-        with S_q query tokens B counts (sequence, query token) pairs."""
+        with S_q query tokens B counts (sequence, query token) pairs.  The
+        per-sequence split only; see ``partial_slots`` for the balanced one."""
+        if self.balanced:
+            raise ValueError("this call uses the balanced split: read its partials with partial_slots()")
         a = self.args
         B, nq, n, dv = a.batch * self.q_seq, a.num_heads, self.num_splits, a.v_dim
         f = self.workspace.view(torch.float32) if self.workspace_bytes else None
@@ -298,6 +307,26 @@ class DecodeCall:
         off_l = off_m + al(rows * 4) // 4
         return (f[:rows * dv].view(B, nq, n, dv), f[off_m:off_m + rows].view(B, nq, n),
                 f[off_l:off_l + rows].view(B, nq, n))
+
+    def partial_slots(self):
+        """Views of the workspace after ``splitkv()`` with the balanced split:
+        (attn_out (n + B, N_q, v_dim), softmax_max (n + B, N_q), softmax_sum
+        (n + B, N_q), (first slot, slot count) int32 (B, 2)); run r's piece of
+        sequence b is slot r + b."""
+        if not self.balanced:
+            raise ValueError("this call splits per sequence: read its partials with partials()")
+        a = self.args
+        B, nq, dv = a.batch, a.num_heads, a.v_dim
+        slots = self.num_splits + B
+        f = self.workspace.view(torch.float32)
+        rows = slots * nq
+        al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+        off_m = al(rows * dv * 4) // 4
+        off_l = off_m + al(rows * 4) // 4
+        off_p = off_l + al(rows * 4) // 4
+        desc = self.workspace.view(torch.int32)[off_p:off_p + 2 * B].view(B, 2)
+        return (f[:rows * dv].view(slots, nq, dv), f[off_m:off_m + rows].view(slots, nq),
+                f[off_l:off_l + rows].view(slots, nq), desc)
 
 
 def decode(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads: int, num_key_value_heads: int,

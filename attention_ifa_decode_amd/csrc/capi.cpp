@@ -49,6 +49,7 @@ struct Plan {
   int heads_per_wg;  // query rows per workgroup (GQA)
   int q_seq;         // query tokens per sequence
   bool mfma;         // GQA rows on the matrix cores (multi-token decode)
+  bool balanced;     // MLA: equal runs of the whole batch's tiles (n_split runs)
   int n_split;
   size_t off_o, off_m, off_l, off_plan, bytes;
 };
@@ -100,6 +101,32 @@ int64_t min_splits_mla(const ifa_decode_args* a, int64_t max_len) {
   for (int64_t n = 1; n <= kMaxSplits; ++n)
     if (ifa::split_chunk(max_len, (int)n) <= (int64_t)(ifa::kMlaMaxTableSlice - 2) * a->block_size) return n;
   return kMaxSplits + 1;
+}
+
+// Balanced split of the MLA path: runs of the batch's 32-token tiles, one
+// workgroup each, about one workgroup per compute unit whatever the number
+// of head groups (each workgroup holds up to 128 heads), at most 256 (the
+// combine's slots per sequence).
+int balanced_runs(const ifa_decode_args* a) {
+  const int64_t r = kTargetCUs * 128LL / a->num_heads;
+  return (int)(r < 1 ? 1 : (r > kMaxSplits ? kMaxSplits : r));
+}
+
+// The automatic choice for the MLA shape when the batch allows it: the plan
+// region holds one (first slot, count) pair per sequence (batch <= 256), tile
+// counts stay in 32 bits, and a run spans at most kMlaMaxTableSlice - 2 cache
+// blocks.  Measured on the MLA config (B 32, lengths 1K..32K): about 20 us per
+// workgroup item goes to loading Q, filling the ring and writing 256 KB of
+// partials, and 16 splits per sequence left CUs idle for about 25 us of the
+// tail; equal runs pay the start once per piece and finish together (a
+// run's extra pieces are paid for by its weight: kMlaPieceCost).
+bool use_balanced_mla(const ifa_decode_args* a, int64_t max_len) {
+  if (a->num_splits != 0 || a->batch > ifa::kLongestFirstMaxBatch) return false;
+  const int64_t tiles = a->batch * ((max_len + 31) / 32 + ifa::kMlaPieceCost);
+  if (tiles >= (int64_t)1 << 31) return false;
+  const int64_t runs = balanced_runs(a);
+  const int64_t run_tokens = 32 * ((tiles + runs - 1) / runs);
+  return !is_paged(a->kv_layout) || run_tokens <= (int64_t)(ifa::kMlaMaxTableSlice - 2) * a->block_size;
 }
 
 int auto_splits_mla(const ifa_decode_args* a, int64_t max_len) {
@@ -237,18 +264,23 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
     }
   } else {
     p.heads_per_wg = (int)a->num_heads;
-    p.n_split = a->num_splits ? a->num_splits : auto_splits_mla(a, max_len);
-    if (p.n_split > kMaxSplits || p.n_split < min_splits_mla(a, max_len))
+    p.balanced = use_balanced_mla(a, max_len);
+    p.n_split = p.balanced ? balanced_runs(a) : (a->num_splits ? a->num_splits : auto_splits_mla(a, max_len));
+    if (!p.balanced && (p.n_split > kMaxSplits || p.n_split < min_splits_mla(a, max_len)))
       return fail(IFA_ERR_PARAM_INVALID,
                   "the MLA shape needs num_splits >= %lld so that a split spans at most %d cache blocks",
                   (long long)min_splits_mla(a, max_len), ifa::kMlaMaxTableSlice - 2);
   }
-  const size_t rows = (size_t)a->batch * (size_t)q_seq * (size_t)a->num_heads * (size_t)p.n_split;
+  // partial rows: (sequence, query token, head, split), or (slot, head) with
+  // runs + batch slots in the balanced split
+  const size_t rows = p.balanced ? ((size_t)p.n_split + (size_t)a->batch) * (size_t)a->num_heads
+                                 : (size_t)a->batch * (size_t)q_seq * (size_t)a->num_heads * (size_t)p.n_split;
   p.off_o = 0;
   p.off_m = align256(rows * (size_t)a->v_dim * sizeof(float));
   p.off_l = p.off_m + align256(rows * sizeof(float));
   p.off_plan = p.off_l + align256(rows * sizeof(float));
-  // longest-first plan: (sequence, clamped length) per rank, int32 pairs
+  // longest-first plan: (sequence, clamped length) per rank, int32 pairs; in
+  // the balanced split, (first slot, slot count) per sequence
   p.bytes = p.off_plan + (a->batch <= ifa::kLongestFirstMaxBatch ? align256((size_t)a->batch * 8) : 0);
   if (rows == 0) p.bytes = 0;
   *plan = p;
@@ -353,6 +385,8 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
   M.qk_dim = (int)a->qk_dim;
   M.v_dim = (int)a->v_dim;
   M.paged = is_paged(a->kv_layout);
+  M.balanced = p.balanced;
+  M.seg_desc = p.balanced ? reinterpret_cast<int2*>(w + p.off_plan) : nullptr;
   return runtime(ifa::launch_mla_splitkv(M, stream, ev), "MLA split-KV decode launch");
 }
 
@@ -373,6 +407,7 @@ ifa_status run_combine(const ifa_decode_args* a, const Plan& p, const void* ws, 
   C.v_dim = (int)a->v_dim;
   C.out_dtype = a->out_dtype;
   C.s_cap = is_paged(a->kv_layout) ? a->max_blocks_per_seq * a->block_size : a->s_cap;
+  C.seg_desc = p.balanced ? reinterpret_cast<const int2*>(w + p.off_plan) : nullptr;
   return runtime(ifa::launch_combine(C, stream), "combine launch");
 }
 
@@ -395,6 +430,15 @@ ifa_status ifa_decode_num_splits(const ifa_decode_args* args, int32_t* num_split
   ifa_status st = validate_and_plan(args, &p);
   if (st != IFA_OK) return st;
   *num_splits = p.n_split;
+  return ok();
+}
+
+ifa_status ifa_decode_split_mode(const ifa_decode_args* args, int32_t* balanced) {
+  if (!balanced) return fail(IFA_ERR_PARAM_NULLPTR, "balanced is NULL");
+  Plan p;
+  ifa_status st = validate_and_plan(args, &p);
+  if (st != IFA_OK) return st;
+  *balanced = p.balanced ? 1 : 0;
   return ok();
 }
 

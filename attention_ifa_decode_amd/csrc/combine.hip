@@ -82,10 +82,32 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
   const int b = row / a.n_q, h = row - b * a.n_q;
   const int part = lane / kLanesPerSplit, col = lane % kLanesPerSplit;
 
-  // Every load of the row is issued before the length arrives: partial
-  // vectors and statistics of all n_split slots (in bounds of the workspace
-  // row), of which only the first nvalid were written by this call.
-  const float4* o = reinterpret_cast<const float4*>(a.ws_o + (int64_t)row * a.n_split * VD);
+  // Partial s of the row: vector o[s * ostep], statistics m[s * mstep],
+  // l[s * mstep]; slots [0, nload) lie in the workspace, of which the first
+  // nvalid were written by this call.  In the per-sequence layout every load
+  // of the row is issued before the length arrives; the balanced layout
+  // reads the sequence's slot range first.
+  int64_t L64 = a.seq_lens[b / a.q_seq];
+  const int L = (int)(L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64));
+  const float4* o;
+  const float *m, *l;
+  int ostep, mstep, nload, nvalid = 0;
+  if (a.seg_desc) {
+    const int2 d = a.seg_desc[b / a.q_seq];
+    const int slots = a.n_split + a.batch / a.q_seq;
+    int s0 = 0;
+    if (L > 0 && d.x >= 0 && d.x < slots) s0 = d.x, nvalid = min(d.y, min(slots - d.x, kMaxSplitsPerRow));
+    nvalid = max(nvalid, 0);
+    o = reinterpret_cast<const float4*>(a.ws_o + ((int64_t)s0 * a.n_q + h) * VD);
+    m = a.ws_m + (int64_t)s0 * a.n_q + h;
+    l = a.ws_l + (int64_t)s0 * a.n_q + h;
+    ostep = a.n_q * kQuads, mstep = a.n_q, nload = nvalid;
+  } else {
+    o = reinterpret_cast<const float4*>(a.ws_o + (int64_t)row * a.n_split * VD);
+    m = a.ws_m + (int64_t)row * a.n_split;
+    l = a.ws_l + (int64_t)row * a.n_split;
+    ostep = kQuads, mstep = 1, nload = a.n_split;
+  }
   float4 v[kSteps][kCols];
   auto load_batch = [&](int s0) {
 #pragma unroll
@@ -93,20 +115,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
       const int s = s0 + j * kParts + part;
 #pragma unroll
       for (int c = 0; c < kCols; ++c)
-        v[j][c] = s < a.n_split ? o[s * kQuads + c * kLanesPerSplit + col] : float4{0.f, 0.f, 0.f, 0.f};
+        v[j][c] = s < nload ? o[(int64_t)s * ostep + c * kLanesPerSplit + col] : float4{0.f, 0.f, 0.f, 0.f};
     }
   };
   load_batch(0);
-  const float* m = a.ws_m + (int64_t)row * a.n_split;
-  const float* l = a.ws_l + (int64_t)row * a.n_split;
   float m0 = 0.f, l0 = 0.f;
-  if (lane < a.n_split) m0 = m[lane], l0 = l[lane];
+  if (lane < nload) m0 = m[lane * mstep], l0 = l[lane * mstep];
   const float sink = a.sink ? a.sink[h] : kNegInf;
 
-  int64_t L64 = a.seq_lens[b / a.q_seq];
-  const int L = (int)(L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64));
-  const int per = ((L + a.n_split - 1) / a.n_split + 15) & ~15;  // split_chunk, in 32 bits
-  const int nvalid = L == 0 ? 0 : (L + per - 1) / per;
+  if (!a.seg_desc) {
+    const int per = ((L + a.n_split - 1) / a.n_split + 15) & ~15;  // split_chunk, in 32 bits
+    nvalid = L == 0 ? 0 : (L + per - 1) / per;
+  }
 
   // statistics: lane s holds split s (in chunks of 64)
   float M = sink;
@@ -116,7 +136,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
     if (c0 == 0) {
       if (s < nvalid) mv = m0, lv = l0;
     } else if (s < nvalid) {
-      mv = m[s], lv = l[s];
+      mv = m[s * mstep], lv = l[s * mstep];
     }
     sm_m[wave][s] = mv;
     sm_w[wave][s] = lv;

@@ -57,6 +57,13 @@ struct MlaLaunch {
   int qk_dim, v_dim;
   bool paged;
   bool longest_first;      // each workgroup ranks the lengths and takes its rank's sequence
+  // Balanced split (batch <= kLongestFirstMaxBatch): the batch's 32-token
+  // tiles, sequence after sequence, each sequence's first one weighted
+  // kMlaPieceCost more, are cut into n_split runs of equal weight; run r's
+  // piece of sequence b writes partial slot r + b ([slot][n_q] statistics,
+  // [slot][n_q][v_dim] outputs), and seg_desc[b] = (first slot, slot count).
+  bool balanced;
+  int2* seg_desc;
 };
 
 struct CombineLaunch {
@@ -70,6 +77,10 @@ struct CombineLaunch {
   int batch, n_q, n_split, v_dim, out_dtype;  // batch counts (sequence, query token) pairs
   int q_seq;          // query tokens per sequence: row r belongs to sequence r / n_q / q_seq
   int64_t s_cap;
+  // balanced split of the MLA path: sequence b's partials are slots
+  // seg_desc[b].x .. + seg_desc[b].y - 1 of a [slot][n_q] layout; null for
+  // the per-sequence [row][n_split] layout
+  const int2* seg_desc;
 };
 
 struct UpdateLaunch {
@@ -112,6 +123,9 @@ constexpr int kLongestFirstMaxBatch = 256;
 
 // Most block-table entries one split of the MLA path may touch (staged in LDS).
 constexpr int kMlaMaxTableSlice = 1024;
+// Balanced split of the MLA path: the cost, in tiles, charged to a sequence
+// for the start of a piece on it.
+constexpr int kMlaPieceCost = 7;
 
 // Optional events that a launch records around the kernel itself
 // (hipExtLaunchKernel), for measuring the kernel's own duration.

@@ -154,8 +154,23 @@ ifa_status ifa_decode_workspace_size(const ifa_decode_args* args, size_t* worksp
 /* The number of KV-axis splits per sequence that a call with `args` uses
  * (args->num_splits, or the automatic choice when it is 0).  Split i of a
  * sequence of length L covers tokens [i*c, min(L, (i+1)*c)) with
- * c = 16 * ceil(ceil(L / n) / 16); splits past the end are empty. */
+ * c = 16 * ceil(ceil(L / n) / 16); splits past the end are empty.
+ * With the balanced split (ifa_decode_split_mode) it is instead the number
+ * of runs n the whole batch is cut into. */
 ifa_status ifa_decode_num_splits(const ifa_decode_args* args, int32_t* num_splits);
+
+/* Whether a call with `args` splits per sequence (*balanced = 0) or
+ * balanced (1).  The balanced split is the automatic choice (num_splits 0)
+ * of the MLA shape for batch <= 256 (when a run spans at most 1022 cache
+ * blocks).  Every sequence with L > 0 tokens is cut into t = ceil(L / 32)
+ * tiles (the last one ragged) and weighs 7 + t units: 7 for starting a piece
+ * on it, then one per tile.  The V units of the batch, sequence after
+ * sequence, are cut into R = min(n, V) runs, run r the units
+ * [floor(r V / R), floor((r + 1) V / R)) (n = ifa_decode_num_splits); a run
+ * takes the tiles whose units it holds.  Each run is one workgroup, so the
+ * work per compute unit is about the same whatever the mix of lengths; a
+ * run's piece of sequence b is one partial, in slot r + b. */
+ifa_status ifa_decode_split_mode(const ifa_decode_args* args, int32_t* balanced);
 
 /* Phase 2 (aclnnIncreFlashAttentionV3): split-KV decode followed by the
  * combine, queued on `stream`.  `workspace` must hold at least the bytes
@@ -176,7 +191,11 @@ ifa_status ifa_decode(const ifa_decode_args* args, void* workspace, size_t works
  * On the int8-KV path a small planning kernel writes it first and the
  * split-KV kernel dispatches its work by it (longest sequences first); the
  * other paths rank the lengths inside the split-KV kernel and leave it
- * unused. */
+ * unused.
+ * The balanced split lays the partials out by slot instead: attn_out fp32
+ * [n + B][N_q][v_dim], softmax_max and softmax_sum fp32 [n + B][N_q], and the
+ * fourth array holds, for each sequence with at least one token, the int32
+ * pair (first slot, number of slots) of its pieces, in token order. */
 ifa_status ifa_decode_splitkv(const ifa_decode_args* args, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 

@@ -275,3 +275,38 @@ def test_multi_token_decode_plans_rows_per_query_token():
     assert ws_size(base_args(**mla))[0] == ifa.IFA_OK, ifa.last_error()
     assert ws_size(base_args(q_seq_len=2, **mla))[0] == ifa.IFA_ERR_PARAM_INVALID
     assert ws_size(base_args(sparse_mode=ifa.IFA_MASK_CAUSAL, **mla))[0] == ifa.IFA_ERR_PARAM_INVALID
+
+
+def split_mode(a):
+    m = ctypes.c_int32(-1)
+    st = lib().ifa_decode_split_mode(ctypes.byref(a), ctypes.byref(m))
+    assert st == ifa.IFA_OK, ifa.last_error()
+    return m.value
+
+
+def test_mla_balanced_split_plan():
+    """The MLA shape's automatic split is balanced (runs of the whole batch's
+    tiles) for batch <= 256: n = 256 * 128 / N_q runs (at most 256), n + B
+    partial slots, and the (first slot, count) pairs in the plan region.
+    Explicit split counts, bigger batches and GQA split per sequence."""
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    mla = dict(qk_dim=576, v_dim=512, num_heads=128, num_key_value_heads=1, value_cache=FAKE, batch=32,
+               max_blocks_per_seq=256)
+    a = base_args(num_splits=0, **mla)
+    assert split_mode(a) == 1
+    n = ctypes.c_int32()
+    assert lib().ifa_decode_num_splits(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == 256
+    st, sz = ws_size(a)
+    assert st == ifa.IFA_OK, ifa.last_error()
+    rows = (256 + 32) * 128
+    assert sz == al(rows * 512 * 4) + 2 * al(rows * 4) + al(32 * 8)
+    for nq, runs in ((256, 128), (64, 256), (32, 256), (96, 256), (224, 146)):
+        a = base_args(num_splits=0, **dict(mla, num_heads=nq))
+        assert split_mode(a) == 1
+        assert lib().ifa_decode_num_splits(ctypes.byref(a), ctypes.byref(n)) == 0 and n.value == runs, nq
+    assert split_mode(base_args(num_splits=16, **mla)) == 0
+    assert split_mode(base_args(num_splits=0, **dict(mla, batch=257))) == 0
+    assert split_mode(base_args(num_splits=0)) == 0  # GQA
+    # a run longer than 1022 blocks of 16 tokens falls back to the per-sequence split
+    big = dict(mla, batch=256, block_size=16, max_blocks_per_seq=1 << 14)
+    assert split_mode(base_args(num_splits=0, **big)) == 0

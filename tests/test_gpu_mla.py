@@ -151,3 +151,81 @@ def test_mla_token_major_pool():
     """With one KV head the (blocknum, blocksize, H) pool holds the same bytes
     as the head-major one."""
     _full_check(_mla(layout="paged_bsh", lengths=[300, 77], seed=58), 3)
+
+
+PIECE_COST = 7  # units a sequence weighs for the start of a piece on it
+
+
+def _balanced_runs(lengths, n):
+    """Host model of the balanced split: per sequence, its first unit (its
+    first tile's unit is PIECE_COST later), and the runs
+    [floor(r V / R), floor((r + 1) V / R)) of the batch's units."""
+    cost = [(L + 31) // 32 + PIECE_COST if L > 0 else 0 for L in lengths]
+    pref = np.concatenate([[0], np.cumsum(cost)]).astype(np.int64)
+    V = int(pref[-1])
+    R = min(n, V)
+    bounds = [(r * V // R, (r + 1) * V // R) for r in range(R)]
+    return pref, bounds
+
+
+@pytest.mark.parametrize("n_q,lengths", [(128, [20000, 33, 0, 1, 9000, 700]), (256, [1, 0, 4100, 31, 32, 65])])
+def test_mla_balanced_partials_match_oracle_triples(n_q, lengths):
+    """The balanced split: every run is a workgroup of consecutive units of
+    the whole batch (a sequence's tiles, after PIECE_COST units for its
+    start); run r's piece of sequence b is slot r + b, and (first slot,
+    count) per sequence names them.  Each piece's triple is the oracle's
+    over exactly its tokens."""
+    w = _mla(n_q=n_q, batch=len(lengths), lengths=lengths, seed=59)
+    wg = w.to("cuda")
+    call = ifa.call_for_workload(wg)
+    assert call.balanced
+    call.splitkv()
+    torch.cuda.synchronize()
+    po, pm, ps, desc = (x.cpu().numpy() for x in call.partial_slots())
+    po, pm, ps = po.astype(np.float64), pm.astype(np.float64), ps.astype(np.float64)
+    pref, bounds = _balanced_runs(lengths, call.num_splits)
+    qf = w.q.double().numpy()
+    checked = 0
+    for b, L in enumerate(lengths):
+        if L == 0:
+            continue
+        z = pref[b] + PIECE_COST  # unit of the sequence's first tile
+        runs = [r for r, (t0, t1) in enumerate(bounds) if t0 < pref[b + 1] and t1 > z]
+        assert tuple(desc[b]) == (runs[0] + b, len(runs)), (b, desc[b], runs[0], len(runs))
+        K = oracle.gather_kv(w.k_cache, "paged", b, 0, L, w.block_table, w.block_size)
+        for r in runs:
+            t0, t1 = bounds[r]
+            a = (max(t0, z) - z) * 32
+            e = min(L, (min(t1, pref[b + 1]) - z) * 32)
+            for h in range(r % 5, n_q, 9):
+                o, m, s = oracle.partial_triple(qf[b, h], K[a:e], K[a:e, :512], w.scale)
+                slot = r + b
+                assert np.max(np.abs(po[slot, h] - o)) < 1e-2, (b, r, h)
+                assert abs(pm[slot, h] - m) < 1e-3 * max(1, abs(m)), (b, r, h)
+                assert abs(ps[slot, h] - s) < 1e-2 * s, (b, r, h)
+                checked += 1
+    assert checked > 100
+
+
+@pytest.mark.parametrize("n_q,bs,layout", [(128, 16, "paged"), (64, 128, "paged"), (256, 64, "paged_bsh"),
+                                           (128, 128, "bnsd")])
+def test_mla_balanced_decode(n_q, bs, layout):
+    """The automatic (balanced) split end to end: runs that cover several
+    short sequences, empty sequences, head groups, two waves per workgroup,
+    small cache blocks and the contiguous layout."""
+    lens = [3000, 0, 1, 31, 33, 700, 0, 1500]
+    w = _mla(n_q=n_q, batch=len(lens), lengths=lens, block_size=bs, layout=layout, seed=60 + n_q + bs)
+    _full_check(w)
+
+
+def test_mla_balanced_wide_offsets_path():
+    """The balanced split on the 64-bit addressing path."""
+    w = _mla(lengths=[2600, 97, 1], batch=3, seed=61)
+    wg = w.to("cuda")
+    call = ifa.call_for_workload(wg)
+    assert call.balanced
+    call.args.num_blocks = 1 << 22
+    out, lse = call.run()
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle.decode_workload(w)
+    _compare(w, out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse)
