@@ -178,6 +178,12 @@ mla_splitkv_kernel(const MlaLaunch a) {
   // ones and the start of another; one piece per sequence it touches.
   const int HGM = a.n_q / (32 * NW);
   int id = blockIdx.x;
+  // Workgroups go to the 8 XCDs round-robin (workgroup i to XCD i % 8), each
+  // with its own L2.  In the balanced split, XCD x takes the consecutive ids
+  // x G/8 .. (x + 1) G/8 - 1, so the runs of one sequence (which read the
+  // same Q rows) and the head groups of one run (which read the same KV
+  // tiles) mostly share an L2.
+  if (a.balanced && (gridDim.x & 7) == 0) id = (id & 7) * (int)(gridDim.x >> 3) + (id >> 3);
   const int hg = id % HGM;
   id /= HGM;
   int b = 0, L = 0, start = 0, end = 0;
