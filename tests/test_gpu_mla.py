@@ -229,3 +229,18 @@ def test_mla_balanced_wide_offsets_path():
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle.decode_workload(w)
     _compare(w, out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse)
+
+
+def test_mla_balanced_batch_limit():
+    """The balanced split at its batch limit (256 sequences): many empty and
+    one-token sequences, so that runs hold many pieces and many sequences
+    start inside a run; a few long ones span several runs."""
+    rng = np.random.default_rng(62)
+    lens = [int(x) for x in rng.choice([0, 1, 33, 70], size=256)]
+    for i in (3, 100, 201):
+        lens[i] = 4000 + 37 * i
+    w = _mla(n_q=32, batch=256, lengths=lens, seed=62)
+    wg = w.to("cuda")
+    call = ifa.call_for_workload(wg)
+    assert call.balanced
+    _full_check(w)
