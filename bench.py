@@ -39,19 +39,26 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak of MI355X
 MALL_BYTES = 256 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gqa_mfma_c3_bf16_paged_traffic.txt")
-# the kernel of the paged bf16 GQA workload (16-bit K/V, head dim 128: the MFMA path)
-KERNEL_SOURCES = ["attention_ifa_decode_amd/csrc/decode_spec.hip", "attention_ifa_decode_amd/csrc/common.hpp"]
+# kernel sources of each split-KV kernel, hashed so that stored counter
+# readings are used only while the kernel code they were taken on is unchanged
+GQA_MFMA_SOURCES = ["attention_ifa_decode_amd/csrc/decode_spec.hip", "attention_ifa_decode_amd/csrc/common.hpp"]
+MLA_SOURCES = ["attention_ifa_decode_amd/csrc/decode_mla.hip", "attention_ifa_decode_amd/csrc/common.hpp"]
+# HBM counter summaries per workload (in its own layout and query length)
+TRAFFIC_FILES = {
+    3: ("gqa_mfma_c3_bf16_paged_traffic.txt", GQA_MFMA_SOURCES),
+    4: ("gqa_mfma_c4_i8_paged_sink_traffic.txt", GQA_MFMA_SOURCES),
+    5: ("mla_splitkv_c5_bf16_paged_traffic.txt", MLA_SOURCES),
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=GQA_MFMA_SOURCES) -> str:
     """Hash of the split-KV kernel's source with comments and whitespace
     removed, so that only a change to the code itself invalidates the stored
     counter readings."""
     import re
 
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -75,14 +82,18 @@ def kernel_name(w) -> str:
 def read_traffic(config_idx: int):
     """HBM bytes per launch of the split-KV kernel from the committed counter
     summary, or None if absent or taken on a different kernel source."""
-    if config_idx != 3 or not os.path.exists(TRAFFIC_FILE):
+    if config_idx not in TRAFFIC_FILES:
+        return None
+    name, sources = TRAFFIC_FILES[config_idx]
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
         return None
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line:
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -113,7 +124,7 @@ def cpu_baseline(w, budget_s: float = 20.0):
     t1 = time.perf_counter() - t0
     rate = max(lens[0], 1) / max(t1, 1e-6)  # tokens (all heads) per second
     sample, tok = [], 0
-    for b in range(1, wc.batch):
+    for b in range(wc.batch):
         if tok / rate > budget_s:
             break
         sample.append(b)
