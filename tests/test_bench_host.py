@@ -1,0 +1,56 @@
+"""Host-side logic of bench.py: the stored HBM counter summaries and the
+kernel-source hash that decides whether a summary still applies.  No GPU."""
+import os
+import re
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def _fields(path):
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip().split()[0]
+    return kv
+
+
+def test_every_traffic_summary_is_consistent():
+    for cfg, (name, sources) in bench.TRAFFIC_FILES.items():
+        path = os.path.join(ROOT, "profiles", name)
+        assert os.path.exists(path), name
+        kv = _fields(path)
+        # read and write bytes are the counter readings times the copy-calibrated scale
+        rd = float(kv["fetch_size_kib_per_dispatch"]) * 1024 * float(kv["fetch_scale"])
+        wr = float(kv["write_size_kib_per_dispatch"]) * 1024 * float(kv["write_scale"])
+        assert abs(rd - float(kv["hbm_read_bytes_per_launch"])) < 1e-4 * rd, name
+        assert abs(rd + wr - float(kv["traffic_bytes_per_launch"])) < 1e-4 * (rd + wr), name
+        # a kernel cannot read less than the K/V bytes it attends over
+        assert float(kv["hbm_read_bytes_per_launch"]) >= 0.999 * float(kv["algorithmic_kv_bytes_per_launch"]), name
+        assert re.fullmatch(r"[0-9a-f]{16}", kv["kernel_source_sha256_16"]), name
+        got = bench.read_traffic(cfg)
+        if kv["kernel_source_sha256_16"] == bench.kernel_source_hash(sources):
+            assert got == float(kv["traffic_bytes_per_launch"])
+        else:  # taken on other kernel code: reported as unknown
+            assert got is None
+
+
+def test_configs_without_a_summary_report_no_traffic():
+    for cfg in (1, 2):
+        assert cfg not in bench.TRAFFIC_FILES
+        assert bench.read_traffic(cfg) is None
+
+
+def test_source_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
+    a = tmp_path / "a.hip"
+    a.write_text("int f(int x) { return x + 1; }  // one\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash(["a.hip"])
+    a.write_text("/* doc */\nint f(int x)\n{\n  return x + 1;  // another comment\n}\n")
+    assert bench.kernel_source_hash(["a.hip"]) == h0
+    a.write_text("int f(int x) { return x + 2; }\n")
+    assert bench.kernel_source_hash(["a.hip"]) != h0
