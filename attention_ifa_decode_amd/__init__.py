@@ -28,6 +28,8 @@ from typing import Optional, Tuple
 
 import torch
 
+from ._checks import check_decode, check_update
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libifa_decode.so")
 
@@ -43,6 +45,8 @@ IFA_ANTIQUANT_PER_CHANNEL, IFA_ANTIQUANT_PER_TENSOR = 0, 1
 IFA_MASK_NONE, IFA_MASK_CAUSAL, IFA_MASK_TREE = 0, 3, 9
 _LAYOUT_CODE = {"bnsd": IFA_KV_BNSD, "paged": IFA_KV_PAGED, "paged_bsh": IFA_KV_PAGED_BSH, "bsnd": IFA_KV_BSND}
 
+_AQ_CODE = {"": 0, "channel": 0, "tensor": 1}
+
 _DTYPE_CODE = {torch.float32: IFA_F32, torch.float16: IFA_F16, torch.bfloat16: IFA_BF16, torch.int8: IFA_I8}
 
 # Every function the header declares.
@@ -57,6 +61,7 @@ EXPORTED = (
     "attn_update",
     "ifa_kv_cache_write",
     "ifa_paged_block_count",
+    "ifa_read_bandwidth_probe",
     "ifa_last_error",
 )
 
@@ -127,11 +132,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ifa_kv_cache_write.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, I64, I32, I32, P]
     lib.ifa_paged_block_count.argtypes = [ctypes.POINTER(I64), I64, I64]
     lib.ifa_paged_block_count.restype = I64
+    lib.ifa_read_bandwidth_probe.argtypes = [P, SZ, P, I32, P]
     lib.ifa_last_error.argtypes = []
     lib.ifa_last_error.restype = ctypes.c_char_p
     for name in ("ifa_decode_workspace_size", "ifa_decode_num_splits", "ifa_decode_split_mode", "ifa_decode",
                  "ifa_decode_splitkv",
-                 "ifa_decode_splitkv_timed", "ifa_decode_combine", "attn_update", "ifa_kv_cache_write"):
+                 "ifa_decode_splitkv_timed", "ifa_decode_combine", "attn_update", "ifa_kv_cache_write",
+                 "ifa_read_bandwidth_probe"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -177,47 +184,16 @@ class DecodeCall:
                  out_dtype: Optional[torch.dtype] = None, with_lse: bool = True, out=None, lse=None,
                  kv_layout: Optional[str] = None, sparse_mode: int = IFA_MASK_NONE, tree_mask=None):
         lib = load_library()
-        _need(q, "q")
-        _need(k_cache, "k_cache")
-        _need(v_cache, "v_cache")
-        _need(actual_seq_lengths, "actual_seq_lengths", torch.int64)
-        # q (B, N_q, D), or (B, S_q, N_q, D) for S_q query tokens per sequence
-        multi = q.dim() == 4
-        B, q_seq, n_q, qk_dim = q.shape if multi else (q.shape[0], 1, q.shape[1], q.shape[2])
-        if n_q != num_heads:
-            raise ValueError("the query's head dimension must equal num_heads")
-        if tree_mask is not None:
-            _need(tree_mask, "tree_mask", torch.uint8)
-        alias = v_cache.data_ptr() == k_cache.data_ptr()
-        if v_dim is None:
-            v_dim = qk_dim if alias else v_cache.shape[-1]
-        # cache shapes: "paged" (blocks, N_kv, block_size, D), "paged_bsh"
-        # (blocks, block_size, N_kv, D) or (blocks, block_size, H), "bnsd"
-        # (B, N_kv, S, D), "bsnd" (B, S, N_kv, D) or (B, S, H)
-        if kv_layout is None:
-            kv_layout = "paged" if block_table is not None else "bnsd"
-        if kv_layout not in _LAYOUT_CODE:
-            raise ValueError(f"unknown kv_layout {kv_layout!r}")
-        paged = kv_layout in ("paged", "paged_bsh")
-        if paged:
-            _need(block_table, "block_table", torch.int32)
-            num_blocks = k_cache.shape[0]
-            block_size = k_cache.shape[2] if kv_layout == "paged" else k_cache.shape[1]
-            max_blocks = block_table.shape[1]
-            s_cap = 0
-        else:
-            s_cap = k_cache.shape[2] if kv_layout == "bnsd" else k_cache.shape[1]
-            num_blocks = block_size = max_blocks = 0
-        for t, nm in ((learnable_sink, "learnable_sink"), (antiquant_scale, "antiquant_scale"),
-                      (antiquant_offset, "antiquant_offset")):
-            if t is not None:
-                _need(t, nm, torch.float32)
-        out_dtype = out_dtype or q.dtype
+        sh = check_decode(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads, num_key_value_heads,
+                          learnable_sink, antiquant_scale, antiquant_offset, v_dim, out_dtype, out, lse, kv_layout,
+                          sparse_mode, tree_mask)
+        B, q_seq, n_q, qk_dim, v_dim = sh.batch, sh.q_seq, sh.n_q, sh.qk_dim, sh.v_dim
+        kv_layout, out_dtype = sh.layout, sh.out_dtype
+        num_blocks, block_size, max_blocks, s_cap = sh.num_blocks, sh.block_size, sh.max_blocks, sh.s_cap
         dev = q.device
-        lead = (B, q_seq) if multi else (B,)
-        self.out = out if out is not None else torch.empty(lead + (n_q, v_dim), dtype=out_dtype, device=dev)
+        self.out = out if out is not None else torch.empty(sh.lead + (n_q, v_dim), dtype=out_dtype, device=dev)
         self.lse = lse if lse is not None else (
-            torch.empty(lead + (n_q,), dtype=torch.float32, device=dev) if with_lse else None)
+            torch.empty(sh.lead + (n_q,), dtype=torch.float32, device=dev) if with_lse else None)
         a = DecodeArgs()
         a.query = _ptr(q)
         a.key_cache = _ptr(k_cache)
@@ -244,8 +220,7 @@ class DecodeCall:
         a.out_dtype = _DTYPE_CODE[out_dtype]
         a.kv_layout = _LAYOUT_CODE[kv_layout]
         a.num_splits = int(num_splits)
-        a.antiquant_mode = (IFA_ANTIQUANT_PER_TENSOR if antiquant_scale is not None and antiquant_scale.dim() == 1
-                            else IFA_ANTIQUANT_PER_CHANNEL)
+        a.antiquant_mode = _AQ_CODE[sh.antiquant_mode]
         a.q_seq_len = q_seq
         a.tree_mask = _ptr(tree_mask)
         a.sparse_mode = int(sparse_mode)
@@ -272,9 +247,12 @@ class DecodeCall:
                                     _stream_handle()))
         return self.out, self.lse
 
+    def _ws(self) -> int:
+        return self.workspace.data_ptr()
+
     def splitkv(self):
-        _check(self._lib.ifa_decode_splitkv(ctypes.byref(self.args), self.workspace.data_ptr(),
-                                            self.workspace_bytes, _stream_handle()))
+        _check(self._lib.ifa_decode_splitkv(ctypes.byref(self.args), self._ws(), self.workspace_bytes,
+                                            _stream_handle()))
 
     def splitkv_timed(self, start: "torch.cuda.Event", stop: "torch.cuda.Event"):
         """splitkv() with `start` / `stop` (timing events of this device)
@@ -282,13 +260,12 @@ class DecodeCall:
         for e in (start, stop):
             if not e.cuda_event:  # torch creates the event at its first record
                 e.record()
-        _check(self._lib.ifa_decode_splitkv_timed(ctypes.byref(self.args), self.workspace.data_ptr(),
-                                                  self.workspace_bytes, _stream_handle(), start.cuda_event,
-                                                  stop.cuda_event))
+        _check(self._lib.ifa_decode_splitkv_timed(ctypes.byref(self.args), self._ws(), self.workspace_bytes,
+                                                  _stream_handle(), start.cuda_event, stop.cuda_event))
 
     def combine(self):
-        _check(self._lib.ifa_decode_combine(ctypes.byref(self.args), self.workspace.data_ptr(),
-                                            self.workspace_bytes, _stream_handle()))
+        _check(self._lib.ifa_decode_combine(ctypes.byref(self.args), self._ws(), self.workspace_bytes,
+                                            _stream_handle()))
         return self.out, self.lse
 
     def partials(self):
@@ -358,13 +335,7 @@ def attn_update(prev_out, prev_max, prev_sum, cur_out, cur_max, cur_sum, out=Non
     a trailing dimension of size 8.  Returns (attn_out, softmax_max,
     softmax_sum); outputs may alias inputs."""
     lib = load_library()
-    D = prev_out.shape[-1]
-    rows = prev_out.numel() // D if D else 0
-    for t, nm in ((prev_out, "prev_out"), (cur_out, "cur_out")):
-        _need(t, nm, prev_out.dtype)
-    for t, nm in ((prev_max, "prev_max"), (prev_sum, "prev_sum"), (cur_max, "cur_max"), (cur_sum, "cur_sum")):
-        _need(t, nm, torch.float32)
-    stride = prev_max.numel() // rows if rows else 1
+    rows, D, stride = check_update(prev_out, prev_max, prev_sum, cur_out, cur_max, cur_sum, out, max_out, sum_out)
     out = out if out is not None else torch.empty_like(prev_out)
     max_out = max_out if max_out is not None else torch.empty_like(prev_max)
     sum_out = sum_out if sum_out is not None else torch.empty_like(prev_sum)
@@ -398,6 +369,19 @@ def kv_cache_write(src, slot_index, cache, layout: str = "paged_bsh", col_offset
                                   int(col_offset), num_blocks, block_size, _LAYOUT_CODE[layout],
                                   _DTYPE_CODE[cache.dtype], _stream_handle()))
     return cache
+
+
+def read_bandwidth_probe(buf: torch.Tensor, workgroups: int = 4096) -> torch.Tensor:
+    """Queue one read of every byte of ``buf`` (a contiguous GPU tensor of
+    16-byte aligned size) on the current stream; returns the per-workgroup
+    words the probe writes.  For measuring the device's read rate."""
+    lib = load_library()
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    out = torch.empty(workgroups, dtype=torch.int32, device=buf.device)
+    _check(lib.ifa_read_bandwidth_probe(buf.data_ptr(), nbytes, out.data_ptr(), int(workgroups), _stream_handle()))
+    return out
 
 
 def paged_block_count(lengths, block_size: int) -> int:

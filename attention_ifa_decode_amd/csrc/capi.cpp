@@ -567,6 +567,18 @@ int64_t ifa_paged_block_count(const int64_t* lengths, int64_t batch, int64_t blo
   return total;
 }
 
+ifa_status ifa_read_bandwidth_probe(const void* buf, size_t bytes, uint32_t* out, int32_t workgroups,
+                                    hipStream_t stream) {
+  if (workgroups < 1 || workgroups > (1 << 20)) return fail(IFA_ERR_PARAM_INVALID, "workgroups outside [1, 2^20]");
+  if (bytes % 16) return fail(IFA_ERR_PARAM_INVALID, "bytes must be a multiple of 16");
+  if (bytes == 0) return ok();
+  if (!buf || !out) return fail(IFA_ERR_PARAM_NULLPTR, "ifa_read_bandwidth_probe: a pointer is NULL");
+  if (reinterpret_cast<uintptr_t>(buf) & 15) return fail(IFA_ERR_PARAM_INVALID, "buf must be 16-byte aligned");
+  ifa_status st = runtime(ifa::launch_read_probe(buf, bytes, out, workgroups, stream), "read probe launch");
+  if (st != IFA_OK) return st;
+  return ok();
+}
+
 const char* ifa_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

@@ -152,6 +152,9 @@ hipError_t launch_combine(const CombineLaunch& p, hipStream_t stream);
 // sequence, for the longest-first dispatch of the split-KV kernels.
 hipError_t launch_plan(const int64_t* seq_lens, int batch, int64_t cap, int2* plan, hipStream_t stream);
 hipError_t launch_update(const UpdateLaunch& p, hipStream_t stream);
+// Read-stream probe: reads bytes / 16 chunks of buf once, writes one word per
+// workgroup to out.
+hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* out, int workgroups, hipStream_t stream);
 
 // Paged KV-cache write: source rows (tokens, n_kv, row_chunks * 16 bytes) to
 // the pool rows of their slots, at byte col_bytes of each row_bytes-long row.

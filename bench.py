@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
                     [--num-splits N] [--kv-layout L] [--q-seq S --mask M]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-read-ceiling] [--reps R]
 
 One step = one pass of the whole path over one batch: the split-KV decode
 kernel (block-table gather, QK^T, online softmax, PV, partial triples) and the
@@ -16,12 +16,15 @@ contiguous (B, S, H)).  ``--q-seq S`` decodes S query tokens per sequence
 random tree over the S draft tokens); ``value`` still counts each KV byte once.
 
 Prints one JSON line.  ``value`` is KV-cache GB/s: the bytes of K and V that
-belong to valid tokens, per step, divided by the step time.  ``roofline``
-relates the split-KV kernel's own average duration (HIP timing events that
-the runtime records at the start and end of every split-KV launch in the timed
-region, on its stream) to the 8 TB/s HBM peak.
-``cpu_baseline`` times the float64 oracle on a bounded sample of the same
-workload on the host cores.
+belong to valid tokens, per step, divided by the mean step time of the timed
+region (K plain ifa_decode calls, events only around the loop).  ``step_us``
+adds the median, p10 and p90 of 100 steps timed one by one.  ``roofline``
+relates the split-KV kernel's own average duration (HIP events that the
+runtime records at the start and end of the kernel, hipExtLaunchKernel, over
+100 launches in a loop after the timed region) to the 8 TB/s HBM peak and to
+the read rate of this device measured in the same run (a probe kernel reading
+a 4 GiB buffer).  ``cpu_baseline`` times the float64 oracle on a bounded
+sample of the same workload on the host cores.
 """
 
 from __future__ import annotations
@@ -101,49 +104,103 @@ def read_traffic(config_idx: int):
         return None
 
 
-def cpu_baseline(w, budget_s: float = 20.0):
-    """The float64 oracle on the host: batches are added to the sample until
-    the estimated work reaches the time budget."""
-    import numpy as np
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, budget_s: float = 15.0):
+    """The float64 oracle on the host cores: whole sequences (all heads),
+    from the first one on, spread over one worker thread per core this
+    process may run on (os.sched_getaffinity, at most OMP_NUM_THREADS or 16)
+    with single-threaded BLAS, so
+    that the core count reported is the number of threads that computed.  The
+    oracle's array operations release the interpreter lock; the sample is
+    sized so that the run takes about ``budget_s`` seconds."""
+    import concurrent.futures as cf
 
     import oracle
 
+    # one thread per core this process may run on, within the host share the
+    # run is given (OMP_NUM_THREADS, else 16)
+    cores = max(1, min(len(os.sched_getaffinity(0)), int(os.environ.get("OMP_NUM_THREADS", "16") or 16)))
     try:
-        from threadpoolctl import threadpool_info
-
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
     except Exception:  # pragma: no cover
-        threads = 1
+        threadpool_limits = None
     wc = w.to("cpu")
     lens = wc.lengths()
     esz = wc.k_cache.element_size()
     per_tok = wc.n_kv * wc.qk_dim * esz + (0 if wc.v_aliases_k else wc.n_kv * wc.v_dim * esz)
-    # calibrate on one batch
-    t0 = time.perf_counter()
-    oracle.decode_workload(wc, rows=[(0, h) for h in range(wc.n_q)])
-    t1 = time.perf_counter() - t0
-    rate = max(lens[0], 1) / max(t1, 1e-6)  # tokens (all heads) per second
-    sample, tok = [], 0
-    for b in range(wc.batch):
-        if tok / rate > budget_s:
-            break
-        sample.append(b)
-        tok += lens[b]
-    if not sample:
-        sample, tok = [0], lens[0]
-    rows = [(b, h) for b in sample for h in range(wc.n_q)]
-    t0 = time.perf_counter()
-    oracle.decode_workload(wc, rows=rows)
-    dt = time.perf_counter() - t0
+
+    def one(b):
+        return oracle.decode_workload(wc, rows=[(b, h) for h in range(wc.n_q)])
+
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx is not None:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()  # calibration: the first sequence on one thread
+        one(0)
+        t1 = time.perf_counter() - t0
+        rate = max(lens[0], 1) / max(t1, 1e-6)  # tokens (all heads) per second and thread
+        sample, tok = [], 0
+        for b in range(wc.batch):
+            if tok / (rate * cores * 0.7) > budget_s:
+                break
+            sample.append(b)
+            tok += lens[b]
+        with cf.ThreadPoolExecutor(max_workers=cores) as ex:
+            t0 = time.perf_counter()
+            list(ex.map(one, sorted(sample, key=lambda b: -lens[b])))
+            dt = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
     return {
         "value": round(tok * per_tok / dt / 1e9, 4),
         "unit": "GB/s",
-        "cores": threads,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"batches {sample[0]}..{sample[-1]} ({len(sample)} of {wc.batch}, {tok} tokens, all heads), "
-                  f"{dt:.1f} s float64 NumPy",
+        "sample": f"sequences {sample[0]}..{sample[-1]} ({len(sample)} of {wc.batch}, {tok} tokens, all heads), "
+                  f"{dt:.1f} s of float64 NumPy on {cores} threads (one per core, BLAS single-threaded)",
+        "cpu_model": _cpu_model(),
+        "seconds": round(dt, 2),
         "qtok_per_s": round(len(sample) / dt, 3),
     }
+
+
+def _pct(xs, p):
+    xs = sorted(xs)
+    k = min(len(xs) - 1, max(0, int(round(p / 100 * (len(xs) - 1)))))
+    return xs[k]
+
+
+def read_ceiling(ifa, torch, dev, gib: int = 4):
+    """HBM read rate of this device: the probe kernel over a buffer far larger
+    than the 256 MB Infinity Cache, best of a few launch shapes, median of
+    5 reads each."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    best = 0.0
+    for wg in (2048, 4096, 8192):
+        ifa.read_bandwidth_probe(buf, wg)
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            ifa.read_bandwidth_probe(buf, wg)
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        best = max(best, buf.numel() / (sorted(ts)[2] * 1e-3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return best
 
 
 def main():
@@ -158,6 +215,8 @@ def main():
     ap.add_argument("--q-seq", type=int, default=1, help="query tokens per sequence (1..16)")
     ap.add_argument("--mask", default="causal", choices=["none", "causal", "tree"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true")
+    ap.add_argument("--reps", type=int, default=100, help="reps of the step-median and kernel-time loops")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first, so that HBM byte "
@@ -215,33 +274,56 @@ def main():
 
     calls = [make_call(x, i) for i, x in enumerate(works)]
 
+    stream = torch.cuda.current_stream()
     for i in range(args.warmup):
         calls[i % copies].run()
     torch.cuda.synchronize()
 
+    # The timed region: K whole steps (ifa_decode: the split-KV kernel, then
+    # the combine), plain calls on the stream, events only around the loop.
     K = args.steps
-    stream = torch.cuda.current_stream()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    for e in ev_a + ev_b:  # create the events before the timed region
-        e.record(stream)
-    # The timed region: K steps; the runtime records ev_a[i] / ev_b[i] at the
-    # start and end of step i's split-KV kernel (hipExtLaunchKernel) on the
-    # launch stream.  Recording them delays the next dispatch a little, which
-    # the step time (and so `value`) includes.
     torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(K):
+        calls[i % copies].run()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / K
+
+    # Step distribution: R steps, each between two events on the stream
+    # (median, p10, p90).
+    R = max(args.reps, 1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
+    for e in ev:
+        e.record(stream)
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(R):
+        calls[i % copies].run()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(R)]
+
+    # The split-KV kernel's own duration: R more steps whose split-KV launch
+    # records a pair of events at the kernel's start and end
+    # (hipExtLaunchKernel).  Those events delay the next dispatch, which is
+    # why they stay out of the timed region above.
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(R)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(R)]
+    for e in ev_a + ev_b:
+        e.record(stream)
+    torch.cuda.synchronize()
+    for i in range(R):
         c = calls[i % copies]
         c.splitkv_timed(ev_a[i], ev_b[i])
         c.combine()
-    t_end.record(stream)
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / K
-    kern_ms = sum(a.elapsed_time(b) for a, b in zip(ev_a, ev_b)) / K
+    kern = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
+    kern_ms = sum(kern) / R
+
+    ceiling = None if args.no_read_ceiling else read_ceiling(ifa, torch, dev)
 
     achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
     value = kv_bytes / (ms_step * 1e-3) / 1e9
@@ -264,6 +346,10 @@ def main():
         "dtype": dtype_name[w.kv_dtype],
         "data": "synthetic",
         "qtok_per_s": round(w.batch * args.q_seq / (ms_step * 1e-3), 1),
+        "step_us": {"mean": round(ms_step * 1e3, 2), "median": round(_pct(step_ms, 50) * 1e3, 2),
+                    "p10": round(_pct(step_ms, 10) * 1e3, 2), "p90": round(_pct(step_ms, 90) * 1e3, 2),
+                    "reps": R, "step_frac_of_peak": round(kv_bytes / (_pct(step_ms, 50) * 1e-3) / 1e9
+                                                          / HBM_PEAK_GBS, 4)},
         "config": {
             "workload": w.name,
             "batch": w.batch,
@@ -291,9 +377,12 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "kernel_us": round(kern_ms * 1e3, 2),
-            "kernel_timing": "events recorded at each split-KV launch's own start and end (hipExtLaunchKernel) "
-                             "in the timed region",
+            "kernel_us_median": round(_pct(kern, 50) * 1e3, 2),
+            "kernel_timing": f"mean of {R} launches, events recorded at the split-KV kernel's own start and end "
+                             "(hipExtLaunchKernel), in a loop after the timed region",
             "combine_and_gaps_us": round((ms_step - kern_ms) * 1e3, 2),
+            "read_ceiling_gbs": None if ceiling is None else round(ceiling, 1),
+            "frac_of_read_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
             "flops_per_launch": flops,
             "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2) if w.qk_dim == 576 else None,
             "mfma_frac_bf16_dense": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)

@@ -261,6 +261,18 @@ ifa_status ifa_kv_cache_write(const void* src, const int64_t* slot_index, void* 
  * below 1. */
 int64_t ifa_paged_block_count(const int64_t* lengths, int64_t batch, int64_t block_size);
 
+/* Measurement helper: the HBM read rate of this device, for setting the
+ * decode's achieved bandwidth against a ceiling measured in the same run.
+ * Reads every 16-byte chunk of `buf` (device, 16-byte aligned, `bytes` a
+ * multiple of 16) once with non-temporal loads spread over `workgroups`
+ * workgroups of 256 lanes, and writes one 32-bit word per workgroup to `out`
+ * (device, `workgroups` words; the XOR of what the workgroup read, which
+ * keeps the loads live).  Asynchronous on `stream`; bytes == 0 is a no-op.
+ * IFA_ERR_PARAM_INVALID for workgroups outside [1, 2^20] or misaligned
+ * sizes, IFA_ERR_PARAM_NULLPTR for a NULL pointer. */
+ifa_status ifa_read_bandwidth_probe(const void* buf, size_t bytes, uint32_t* out, int32_t workgroups,
+                                    hipStream_t stream);
+
 /* Description of the last error on the calling thread ("" if none).  The
  * string is owned by the library and valid until the next call on the
  * thread. */

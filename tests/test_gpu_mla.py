@@ -18,7 +18,7 @@ import attention_ifa_decode_amd as ifa
 import oracle
 from synth import config_workload, make_workload
 
-from test_gpu_decode import _announce, _compare, _full_check, _sampled_rows
+from test_gpu_decode import _announce, _compare, _full_check, _sampled_rows, whole_sequence_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -117,7 +117,9 @@ def test_mla_partials_match_oracle_triples():
 
 def test_c5_full_size_sampled_rows():
     """The MLA config at its full size, in the launch configuration the
-    benchmark times; the oracle recomputes a sample of rows one by one."""
+    benchmark times (balanced split: the longest sequence spans about eight
+    runs); the oracle recomputes all 128 heads of the longest, the shortest
+    and a median sequence, and a few random rows."""
     wg = config_workload(5, device="cuda")
     _announce(f"full size config 5: {wg.name}")
     out, lse = ifa.decode_workload(wg)
@@ -128,7 +130,7 @@ def test_c5_full_size_sampled_rows():
     w = wg.to("cpu")
     del wg
     torch.cuda.empty_cache()
-    rows = _sampled_rows(w, 8, 5)
+    rows = whole_sequence_rows(w, 5)
     ref_out, ref_lse = oracle.decode_workload(w, rows=rows)
     _compare(w, out, lse, ref_out, ref_lse, rows=rows)
 

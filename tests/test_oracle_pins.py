@@ -463,6 +463,92 @@ def test_blocknum_worked_example():
     assert oracle.block_count(lens, g["block_size"]) == g["expected_block_num"]
 
 
+# ---------------------------------------------------------------- P18
+_ROWS_CASES = [
+    # (layout, kv dtype, N_q, N_kv passed, D, V dim, MLA value prefix, sink, antiquant mode)
+    ("paged", "f32", 6, 2, 8, 8, False, False, "channel"),
+    ("paged", "bf16", 6, 2, 8, 8, False, True, "channel"),
+    ("bnsd", "f16", 4, 4, 8, 8, False, True, "channel"),
+    ("bnsd", "f32", 4, 0, 4, 4, False, False, "channel"),
+    ("paged", "i8", 8, 2, 8, 8, False, True, "channel"),
+    ("paged_bsh", "i8", 6, 3, 8, 8, False, False, "tensor"),
+    ("bsnd", "bf16", 6, 3, 8, 8, False, True, "channel"),
+    ("paged", "bf16", 4, 1, 12, 8, True, False, "channel"),
+]
+
+
+def _stored(cache, layout, bt, bs, b, g, j):
+    """Token j of sequence b, KV head g, read by its storage index alone
+    (aclnnIncreFlashAttentionV3 "Constraints", page attention scenario)."""
+    if layout == "paged":
+        return cache[bt[b][j // bs], g, j % bs]
+    if layout == "paged_bsh":
+        return cache[bt[b][j // bs], j % bs, g]
+    if layout == "bnsd":
+        return cache[b, g, j]
+    return cache[b, j, g]
+
+
+@pytest.mark.parametrize("case", range(len(_ROWS_CASES)))
+def test_decode_rows_matches_bruteforce(case):
+    """decode_rows, the per-row entry used wherever only some rows are
+    checked, against the literal formula evaluated in pure Python for every
+    requested (b, h), in a shuffled order with repeats: GQA (query head h
+    reads KV head h // (N_q / N_kv), reading R3), MHA, numKeyValueHeads = 0
+    meaning N_kv = N_q (aclnnIncreFlashAttentionV3 "Parameters"), paged,
+    token-major and contiguous layouts, a learnable sink
+    (aclnnFlashAttentionScoreV4 formula), int8 with per-channel and
+    per-tensor (x + offset) * scale (reading R2), and the MLA value prefix
+    (V = the first v_dim channels of the key row).  It must also return
+    exactly what decode returns for those rows."""
+    layout, kv, nq, nkv, d, dv, mla, use_sink, aq = _ROWS_CASES[case]
+    B, bs = 3, 4
+    lengths = [9, 0, 6] if case % 2 else [5, 11, 1]
+    w = make_workload(batch=B, n_q=nq, n_kv=nkv, qk_dim=d, v_dim=dv, kv_dtype=kv, layout=layout,
+                      block_size=bs, lengths=lengths, s_cap=12, seed=90 + case, sink=use_sink,
+                      antiquant_mode=aq, v_aliases_k=mla, extra_blocks=1)
+    n_kv = nq if nkv == 0 else nkv
+    G = nq // n_kv
+    kc = w.k_cache.double().numpy()
+    vc = kc if mla else w.v_cache.double().numpy()
+    bt = w.block_table.long().tolist() if w.block_table is not None else None
+    qf = w.q.double().numpy()
+    sc = w.antiquant_scale.double().numpy() if w.antiquant_scale is not None else None
+    off = w.antiquant_offset.double().numpy() if w.antiquant_offset is not None else None
+    rng = np.random.default_rng(case)
+    rows = [(b, h) for b in range(B) for h in range(nq)]
+    rows = [rows[i] for i in rng.permutation(len(rows))] + rows[:3]
+    out, lse = oracle.decode_rows(w.q, w.k_cache, w.v_cache, layout, w.seq_lens, nkv, w.scale, rows,
+                                  block_table=w.block_table, block_size=w.block_size, sink=w.sink,
+                                  antiquant_scale=w.antiquant_scale, antiquant_offset=w.antiquant_offset,
+                                  v_dim=dv, v_from_k=mla)
+    assert out.shape == (len(rows), dv) and lse.shape == (len(rows),)
+
+    def deq(x, i, g, c):
+        if sc is None:
+            return float(x)
+        if sc.ndim == 1:
+            return (float(x) + off[i]) * sc[i]
+        return (float(x) + off[i, g, c]) * sc[i, g, c]
+
+    for r, (b, h) in enumerate(rows):
+        g = h // G
+        L = lengths[b]
+        K = [[deq(_stored(kc, layout, bt, bs, b, g, j)[c], 0, g, c) for c in range(d)] for j in range(L)]
+        V = [[deq(_stored(vc, layout, bt, bs, b, g, j)[c], 1, g, c) for c in range(dv)] for j in range(L)]
+        sk = float(w.sink[h]) if use_sink else None
+        if L == 0 and sk is None:
+            assert np.all(out[r] == 0) and lse[r] == -np.inf
+            continue
+        ob, lb = _bruteforce_row(qf[b, h].tolist(), K, V if L else [[0.0] * dv], w.scale, sk)
+        np.testing.assert_allclose(out[r], ob, rtol=1e-11, atol=1e-13)
+        assert abs(lse[r] - lb) < 1e-11
+    full_o, full_l = oracle.decode_workload(w)
+    for r, (b, h) in enumerate(rows):
+        np.testing.assert_array_equal(out[r], full_o[b, h])
+        assert lse[r] == full_l[b, h] or (np.isinf(lse[r]) and np.isinf(full_l[b, h]))
+
+
 # ---------------------------------------------------------------- attn_update rows
 def test_attn_update_rows_match_full_attention():
     """Row-wise aclnnRingAttentionUpdate over several (b, h) rows: merging the
@@ -497,7 +583,9 @@ def test_planted_mistakes_are_caught(monkeypatch):
                          ("sink", lambda: test_sink_closed_form(8.0)),
                          ("paged", lambda: test_paged_equals_contiguous(16, [1, 15, 16, 17, 40])),
                          ("token-major", lambda: test_token_major_layouts_equal_logical_kv(16, [0, 1, 15, 16, 17, 40])),
-                         ("per-tensor", test_per_tensor_antiquant_is_per_channel_with_constant_vectors)]:
+                         ("per-tensor", test_per_tensor_antiquant_is_per_channel_with_constant_vectors),
+                         ("rows", lambda: test_decode_rows_matches_bruteforce(0)),
+                         ("rows-int8", lambda: test_decode_rows_matches_bruteforce(4))]:
             try:
                 fn()
             except (AssertionError, IndexError):  # a wrong index may also fall outside the cache
@@ -541,7 +629,26 @@ def test_planted_mistakes_are_caught(monkeypatch):
         return orig_kv_rows(k_cache, v_cache, layout, b, g, L, block_table, block_size, qk_dim, v_dim, v_from_k,
                             aq_scale, aq_offset)
 
-    slips = [("attention_row", no_scale), ("attention_row", sink_in_numerator),
+    def rows_wrong_group(q, k_cache, v_cache, layout, seq_lens, n_kv, scale, rows, block_table=None,
+                         block_size=0, sink=None, antiquant_scale=None, antiquant_offset=None, v_dim=None,
+                         v_from_k=False):
+        # decode_rows with query head h sent to KV head h % N_kv (interleaved
+        # instead of contiguous groups), everything else as in the oracle
+        qf = attn_ref.as_f64(q)
+        n_q, qk_dim = qf.shape[1], qf.shape[2]
+        n_kv = n_q if n_kv == 0 else n_kv
+        v_dim = qk_dim if v_dim is None else v_dim
+        lens = attn_ref._as_int(seq_lens)
+        sinkf = attn_ref.as_f64(sink)
+        aq_s, aq_o = attn_ref.as_f64(antiquant_scale), attn_ref.as_f64(antiquant_offset)
+        out, lse = np.zeros((len(rows), v_dim)), np.zeros(len(rows))
+        for i, (b, h) in enumerate(rows):
+            K, V = attn_ref._kv_rows(k_cache, v_cache, layout, b, h % n_kv, int(lens[b]), block_table, block_size,
+                                     qk_dim, v_dim, v_from_k, aq_s, aq_o)
+            out[i], lse[i] = attn_ref.attention_row(qf[b, h], K, V, scale, None if sinkf is None else float(sinkf[h]))
+        return out, lse
+
+    slips = [("decode_rows", rows_wrong_group), ("attention_row", no_scale), ("attention_row", sink_in_numerator),
              ("attention_row", transposed), ("merge", unweighted_merge),
              ("gather_kv", wrong_batch_row), ("gather_kv", wrong_head),
              ("gather_kv", token_major_read_as_head_major), ("_kv_rows", per_tensor_k_v_swapped)]
