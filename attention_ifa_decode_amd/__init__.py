@@ -55,6 +55,7 @@ EXPORTED = (
     "ifa_decode_num_splits",
     "ifa_decode_split_mode",
     "ifa_decode",
+    "ifa_decode_noalloc",
     "ifa_decode_splitkv",
     "ifa_decode_splitkv_timed",
     "ifa_decode_combine",
@@ -127,6 +128,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     for fn in (lib.ifa_decode, lib.ifa_decode_splitkv):
         fn.argtypes = [args_p, P, SZ, P]
     lib.ifa_decode_splitkv_timed.argtypes = [args_p, P, SZ, P, P, P]
+    lib.ifa_decode_noalloc.argtypes = [args_p, P]
     lib.ifa_decode_combine.argtypes = [args_p, P, SZ, P]
     lib.attn_update.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I32, I32, P]
     lib.ifa_kv_cache_write.argtypes = [P, P, P, I64, I64, I64, I64, I64, I64, I64, I32, I32, P]
@@ -138,6 +140,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     for name in ("ifa_decode_workspace_size", "ifa_decode_num_splits", "ifa_decode_split_mode", "ifa_decode",
                  "ifa_decode_splitkv",
                  "ifa_decode_splitkv_timed", "ifa_decode_combine", "attn_update", "ifa_kv_cache_write",
+                 "ifa_decode_noalloc",
                  "ifa_read_bandwidth_probe"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
@@ -182,7 +185,8 @@ class DecodeCall:
                  num_key_value_heads: int, scale_value: float, learnable_sink=None, antiquant_scale=None,
                  antiquant_offset=None, num_splits: int = 0, v_dim: Optional[int] = None,
                  out_dtype: Optional[torch.dtype] = None, with_lse: bool = True, out=None, lse=None,
-                 kv_layout: Optional[str] = None, sparse_mode: int = IFA_MASK_NONE, tree_mask=None):
+                 kv_layout: Optional[str] = None, sparse_mode: int = IFA_MASK_NONE, tree_mask=None,
+                 noalloc: bool = False):
         lib = load_library()
         sh = check_decode(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads, num_key_value_heads,
                           learnable_sink, antiquant_scale, antiquant_offset, v_dim, out_dtype, out, lse, kv_layout,
@@ -234,8 +238,12 @@ class DecodeCall:
         bal = ctypes.c_int32(0)
         _check(lib.ifa_decode_split_mode(ctypes.byref(a), ctypes.byref(bal)))
         self.balanced = bool(bal.value)
-        self.workspace_bytes = sz.value
-        self.workspace = torch.empty(max(1, sz.value), dtype=torch.uint8, device=dev)
+        self.noalloc = noalloc
+        if noalloc:  # partials in the library's fixed array (ifa_decode_noalloc)
+            self.workspace_bytes, self.workspace = 0, None
+        else:
+            self.workspace_bytes = sz.value
+            self.workspace = torch.empty(max(1, sz.value), dtype=torch.uint8, device=dev)
         # keep the inputs alive as long as the call object
         self._keep = (q, k_cache, v_cache, block_table, actual_seq_lengths, learnable_sink,
                       antiquant_scale, antiquant_offset, tree_mask)
@@ -243,11 +251,16 @@ class DecodeCall:
         self._lib = lib
 
     def run(self):
-        _check(self._lib.ifa_decode(ctypes.byref(self.args), self.workspace.data_ptr(), self.workspace_bytes,
-                                    _stream_handle()))
+        if self.noalloc:
+            _check(self._lib.ifa_decode_noalloc(ctypes.byref(self.args), _stream_handle()))
+        else:
+            _check(self._lib.ifa_decode(ctypes.byref(self.args), self.workspace.data_ptr(), self.workspace_bytes,
+                                        _stream_handle()))
         return self.out, self.lse
 
     def _ws(self) -> int:
+        if self.noalloc:
+            raise ValueError("a call made with noalloc=True has no workspace of its own")
         return self.workspace.data_ptr()
 
     def splitkv(self):

@@ -413,6 +413,18 @@ ifa_status run_combine(const ifa_decode_args* a, const Plan& p, const void* ws, 
 
 }  // namespace
 
+namespace ifa {
+ifa_status set_last_error(ifa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+}  // namespace ifa
+
 extern "C" {
 
 ifa_status ifa_decode_workspace_size(const ifa_decode_args* args, size_t* workspace_bytes) {

@@ -199,6 +199,23 @@ ifa_status ifa_decode(const ifa_decode_args* args, void* workspace, size_t works
 ifa_status ifa_decode_splitkv(const ifa_decode_args* args, void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
+/* Size of the fixed device array that ifa_decode_noalloc keeps its split
+ * partials in (per device, held until the process ends): 128 MiB. */
+#define IFA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ifa_decode
+ * with no workspace argument.  The split partials go to a fixed array of
+ * IFA_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ * on; the call allocates nothing and computes exactly what ifa_decode
+ * computes.  The caller still passes every input and output in `args`, on the
+ * device current at the call (the first call on a device takes the array's
+ * address with that device current).  A call whose partials need more than
+ * the array (ifa_decode_workspace_size) fails with IFA_ERR_PLAN before
+ * anything is queued.  All calls on one device share the array: calls that
+ * overlap on one device (different streams, or unordered threads) race. */
+ifa_status ifa_decode_noalloc(const ifa_decode_args* args, hipStream_t stream);
+
 /* ifa_decode_splitkv for measurement: the same work, launched so that the
  * runtime records `start` and `stop` (events the caller created on this
  * device with timing enabled) at the split-KV kernel's own start and end

@@ -310,3 +310,18 @@ def test_mla_balanced_split_plan():
     # a run longer than 1022 blocks of 16 tokens falls back to the per-sequence split
     big = dict(mla, batch=256, block_size=16, max_blocks_per_seq=1 << 14)
     assert split_mode(base_args(num_splits=0, **big)) == 0
+
+
+def test_noalloc_rejects_oversize_calls_on_the_host():
+    """ifa_decode_noalloc refuses, before touching any device, a call whose
+    partials exceed its fixed array (IFA_NOALLOC_SCRATCH_BYTES, 128 MiB): the
+    MLA shape with 256 splits of 40 sequences needs 40*128*256*514*4 bytes."""
+    a = base_args(batch=40, num_heads=128, num_key_value_heads=1, qk_dim=576, v_dim=512, max_blocks_per_seq=1,
+                  num_blocks=64, num_splits=256)
+    a.value_cache = a.key_cache
+    st, sz = ws_size(a)
+    assert st == ifa.IFA_OK and sz > (128 << 20)
+    assert lib().ifa_decode_noalloc(ctypes.byref(a), None) == ifa.IFA_ERR_PLAN
+    assert "scratch" in ifa.last_error()
+    bad = base_args(num_heads=0)
+    assert lib().ifa_decode_noalloc(ctypes.byref(bad), None) == ifa.IFA_ERR_PARAM_INVALID
