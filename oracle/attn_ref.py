@@ -32,6 +32,12 @@ R1  merge: the printed update omits cur_softmax_sum and the sum weights of the
     any split of the KV axis gives the attention over the whole axis.
 R2  antiquant: x_hat = (x + offset) * scale per (kv head, channel).  The sign
     convention of the offset is parity unpinned.
+R24 per-token antiquant ([FIA] antiquantMode list: 1 per-token, 3 per-token
+    with per-head; no shape is printed): fp32 parameters (2, B, S) with one
+    (scale, offset) pair per logical token position j < S of sequence b,
+    applied to every channel (and every KV head) of that token, or
+    (2, B, KV_N, S) with one pair per token and KV head; the R2 form
+    x_hat = (x + offset) * scale; index 0 is K, 1 is V.
 R3  GQA: query head h reads KV head h // (N_q / N_kv) (contiguous groups).
     Parity unpinned as to convention.
 R4  the sink is a logit in the units of the scaled score scale * q.k.
@@ -208,26 +214,46 @@ def attn_update(prev_out, prev_max, prev_sum, cur_out, cur_max, cur_sum):
 # the whole decode call
 # ----------------------------------------------------------------------------
 
+def antiquant_mode_of(aq_scale, mode: Optional[str] = None) -> Optional[str]:
+    """The antiquant mode of a parameter array: "tensor" for shape (2),
+    "channel" for (2, KV_N, D), "token_head" for (2, B, KV_N, S); a 3-D array
+    is per channel unless ``mode`` says "token" ((2, B, S))."""
+    if aq_scale is None:
+        return None
+    if mode:
+        return mode
+    return {1: "tensor", 3: "channel", 4: "token_head"}[np.ndim(aq_scale)]
+
+
 def _kv_rows(k_cache, v_cache, layout, b, g, L, block_table, block_size,
-             qk_dim, v_dim, v_from_k, aq_scale, aq_offset):
+             qk_dim, v_dim, v_from_k, aq_scale, aq_offset, aq_mode=None):
     K = gather_kv(k_cache, layout, b, g, L, block_table, block_size, dim=qk_dim)
     if v_from_k:
         V = K[:, :v_dim]  # R17: V is the first v_dim channels of the key row
     else:
         V = gather_kv(v_cache, layout, b, g, L, block_table, block_size, dim=v_dim)
-    if aq_scale is not None and aq_scale.ndim == 1:  # per tensor, shape (2): [K, V]
+    mode = antiquant_mode_of(aq_scale, aq_mode)
+    if mode == "tensor":  # shape (2): [K, V]
         K = dequant(K, aq_scale[0], aq_offset[0])
         V = dequant(V, aq_scale[1], aq_offset[1])
-    elif aq_scale is not None:  # per channel, (2, KV_N, D)
+    elif mode == "channel":  # (2, KV_N, D)
         K = dequant(K, aq_scale[0, g, :qk_dim], aq_offset[0, g, :qk_dim])
         V = dequant(V, aq_scale[1, g, :v_dim], aq_offset[1, g, :v_dim])
+    elif mode == "token":  # (2, B, S): one pair per logical token of sequence b, every channel and head
+        K = dequant(K, aq_scale[0, b, :L, None], aq_offset[0, b, :L, None])
+        V = dequant(V, aq_scale[1, b, :L, None], aq_offset[1, b, :L, None])
+    elif mode == "token_head":  # (2, B, KV_N, S): one pair per logical token and KV head
+        K = dequant(K, aq_scale[0, b, g, :L, None], aq_offset[0, b, g, :L, None])
+        V = dequant(V, aq_scale[1, b, g, :L, None], aq_offset[1, b, g, :L, None])
+    elif mode is not None:
+        raise ValueError(f"unknown antiquant mode {mode!r}")
     return K, V
 
 
 def decode_rows(q, k_cache, v_cache, layout: str, seq_lens, n_kv: int, scale: float,
                 rows: Sequence[Tuple[int, int]], block_table=None, block_size: int = 0,
                 sink=None, antiquant_scale=None, antiquant_offset=None,
-                v_dim: Optional[int] = None, v_from_k: bool = False):
+                v_dim: Optional[int] = None, v_from_k: bool = False, antiquant_mode: Optional[str] = None):
     """Decode attention for the listed (batch, query head) rows only.
 
     q is (B, N_q, qk_dim); query head h reads KV head h // (N_q / N_kv)
@@ -252,7 +278,7 @@ def decode_rows(q, k_cache, v_cache, layout: str, seq_lens, n_kv: int, scale: fl
         g = h // G
         if (b, g) not in cache:
             cache[(b, g)] = _kv_rows(k_cache, v_cache, layout, b, g, int(lens[b]), block_table,
-                                     block_size, qk_dim, v_dim, v_from_k, aq_s, aq_o)
+                                     block_size, qk_dim, v_dim, v_from_k, aq_s, aq_o, antiquant_mode)
         K, V = cache[(b, g)]
         out[i], lse[i] = attention_row(qf[b, h], K, V, scale,
                                        None if sinkf is None else float(sinkf[h]))
@@ -261,7 +287,8 @@ def decode_rows(q, k_cache, v_cache, layout: str, seq_lens, n_kv: int, scale: fl
 
 def decode(q, k_cache, v_cache, layout: str, seq_lens, n_kv: int, scale: float,
            block_table=None, block_size: int = 0, sink=None, antiquant_scale=None,
-           antiquant_offset=None, v_dim: Optional[int] = None, v_from_k: bool = False):
+           antiquant_offset=None, v_dim: Optional[int] = None, v_from_k: bool = False,
+           antiquant_mode: Optional[str] = None):
     """Decode attention for every (batch, query head): (out (B, N_q, v_dim),
     lse (B, N_q)).  Loops batch by batch and KV head by KV head."""
     qf = as_f64(q)
@@ -278,7 +305,7 @@ def decode(q, k_cache, v_cache, layout: str, seq_lens, n_kv: int, scale: float,
     for b in range(B):
         for g in range(n_kv_e):
             K, V = _kv_rows(k_cache, v_cache, layout, b, g, int(lens[b]), block_table, block_size,
-                            qk_dim, v_dim, v_from_k, aq_s, aq_o)
+                            qk_dim, v_dim, v_from_k, aq_s, aq_o, antiquant_mode)
             for h in range(g * G, (g + 1) * G):
                 out[b, h], lse[b, h] = attention_row(qf[b, h], K, V, scale,
                                                      None if sinkf is None else float(sinkf[h]))
@@ -290,7 +317,7 @@ def decode_workload(w, rows=None):
     object carrying the decode arguments as attributes."""
     kw = dict(block_table=w.block_table, block_size=w.block_size, sink=w.sink,
               antiquant_scale=w.antiquant_scale, antiquant_offset=w.antiquant_offset,
-              v_dim=w.v_dim, v_from_k=w.v_aliases_k)
+              v_dim=w.v_dim, v_from_k=w.v_aliases_k, antiquant_mode=getattr(w, "antiquant_mode", None))
     if rows is None:
         return decode(w.q, w.k_cache, w.v_cache, w.layout, w.seq_lens, w.n_kv, w.scale, **kw)
     return decode_rows(w.q, w.k_cache, w.v_cache, w.layout, w.seq_lens, w.n_kv, w.scale, rows, **kw)

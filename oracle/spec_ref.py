@@ -50,7 +50,7 @@ def visible_tokens(L: int, q_seq: int, i: int, mode: int, tree_row=None) -> np.n
 def decode_multi(q, k_cache, v_cache, layout: str, seq_lens, n_kv: int, scale: float,
                  sparse_mode: int = MASK_NONE, tree_mask=None, block_table=None, block_size: int = 0,
                  sink=None, antiquant_scale=None, antiquant_offset=None, v_dim: Optional[int] = None,
-                 v_from_k: bool = False):
+                 v_from_k: bool = False, antiquant_mode: Optional[str] = None):
     """q (B, Q_S, N_q, qk_dim) -> (out (B, Q_S, N_q, v_dim), lse (B, Q_S, N_q)):
     each (query token, head) row is the decode attention of that row over
     the tokens the mask leaves it."""
@@ -69,7 +69,7 @@ def decode_multi(q, k_cache, v_cache, layout: str, seq_lens, n_kv: int, scale: f
         L = int(lens[b])
         for g in range(n_kv_e):
             K, V = _kv_rows(k_cache, v_cache, layout, b, g, L, block_table, block_size, qk_dim, v_dim, v_from_k,
-                            aq_s, aq_o)
+                            aq_s, aq_o, antiquant_mode)
             for i in range(q_seq):
                 idx = visible_tokens(L, q_seq, i, sparse_mode, None if tm is None else tm[b, i])
                 for h in range(g * G, (g + 1) * G):

@@ -52,8 +52,11 @@ class Workload:
     scale: float
     out_dtype: torch.dtype
     sink: Optional[torch.Tensor] = None  # fp32 (N_q,)
-    antiquant_scale: Optional[torch.Tensor] = None  # fp32 (2, N_kv, D) per channel, or (2,) per tensor
+    # fp32 (2, N_kv, D) per channel, (2,) per tensor, (2, B, s_cap) per token,
+    # (2, B, N_kv, s_cap) per token and KV head
+    antiquant_scale: Optional[torch.Tensor] = None
     antiquant_offset: Optional[torch.Tensor] = None  # the same shape as antiquant_scale
+    antiquant_mode: Optional[str] = None  # "channel", "tensor", "token", "token_head" (None without antiquant)
     num_splits: int = 0
 
     @property
@@ -200,7 +203,10 @@ def make_workload(
     channels serve as V.  ``poison`` fills every stored slot that the decode
     must never read (contiguous padding past the length, tail slots of a
     sequence's last block, unused pool blocks) with NaN (127 for int8).
-    ``antiquant_mode`` "channel" gives (2, N_kv, D) parameters, "tensor" (2,).
+    ``antiquant_mode`` "channel" gives (2, N_kv, D) parameters, "tensor" (2,),
+    "token" (2, B, s_cap) (one pair per logical token position) and
+    "token_head" (2, B, N_kv, s_cap), with s_cap the paged capacity
+    max_blocks_per_seq * block_size or the contiguous padded length.
     """
     v_dim = qk_dim if v_dim is None else v_dim
     n_kv_eff = n_q if n_kv == 0 else n_kv
@@ -274,7 +280,8 @@ def make_workload(
     sink_t = torch.randn(n_q, generator=vgen, device=dev, dtype=torch.float32) if sink else None
     aq_s = aq_o = None
     if antiquant:
-        ashape = (2,) if antiquant_mode == "tensor" else (2, n_kv_eff, qk_dim)
+        ashape = {"tensor": (2,), "channel": (2, n_kv_eff, qk_dim), "token": (2, batch, s_cap_eff),
+                  "token_head": (2, batch, n_kv_eff, s_cap_eff)}[antiquant_mode]
         aq_s = torch.rand(ashape, generator=vgen, device=dev, dtype=torch.float32) * 0.02 + 0.02
         aq_o = torch.rand(ashape, generator=vgen, device=dev, dtype=torch.float32) * 2.0 - 1.0
     return Workload(
@@ -296,6 +303,7 @@ def make_workload(
         sink=sink_t,
         antiquant_scale=aq_s,
         antiquant_offset=aq_o,
+        antiquant_mode=antiquant_mode if antiquant else None,
         num_splits=num_splits,
     )
 

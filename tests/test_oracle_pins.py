@@ -463,6 +463,86 @@ def test_blocknum_worked_example():
     assert oracle.block_count(lens, g["block_size"]) == g["expected_block_num"]
 
 
+# ---------------------------------------------------------------- P19
+@pytest.mark.parametrize("layout,mode", [("paged", "token"), ("paged_bsh", "token"), ("bnsd", "token_head"),
+                                         ("paged", "token_head")])
+def test_per_token_antiquant_bruteforce(layout, mode):
+    """Per-token antiquant (FusedInferAttentionScore blog, antiquantMode 1
+    per-token and 3 per-token with per-head; reading R24: fp32 (2, B, S) or
+    (2, B, N_kv, S), one (scale, offset) pair per logical token position,
+    x_hat = (x + offset) * scale).  The whole decode against the literal
+    formula evaluated in pure Python, each K and V element dequantised from
+    its stored byte with the pair of its sequence, token (and head); the
+    paged pool is a random block permutation, so the pair must follow the
+    logical position, not the storage slot."""
+    B, nq, nkv, d, bs = 2, 4, 2, 8, 4
+    lengths = [11, 6]
+    w = make_workload(batch=B, n_q=nq, n_kv=nkv, qk_dim=d, kv_dtype="i8", layout=layout, block_size=bs,
+                      lengths=lengths, s_cap=12, seed=33, sink=True, antiquant_mode=mode, extra_blocks=1)
+    assert w.antiquant_mode == mode
+    out, lse = oracle.decode_workload(w)
+    kc, vc = w.k_cache.double().numpy(), w.v_cache.double().numpy()
+    bt = w.block_table.long().tolist() if w.block_table is not None else None
+    sc, off = w.antiquant_scale.double().numpy(), w.antiquant_offset.double().numpy()
+    qf = w.q.double().numpy()
+    G = nq // nkv
+    for b in range(B):
+        L = lengths[b]
+        for h in range(nq):
+            g = h // G
+
+            def pair(i, j):
+                return (sc[i, b, j], off[i, b, j]) if mode == "token" else (sc[i, b, g, j], off[i, b, g, j])
+
+            K = [[(float(_stored(kc, layout, bt, bs, b, g, j)[c]) + pair(0, j)[1]) * pair(0, j)[0] for c in range(d)]
+                 for j in range(L)]
+            V = [[(float(_stored(vc, layout, bt, bs, b, g, j)[c]) + pair(1, j)[1]) * pair(1, j)[0] for c in range(d)]
+                 for j in range(L)]
+            ob, lb = _bruteforce_row(qf[b, h].tolist(), K, V, w.scale, float(w.sink[h]))
+            np.testing.assert_allclose(out[b, h], ob, rtol=1e-11, atol=1e-13)
+            assert abs(lse[b, h] - lb) < 1e-11
+
+
+def test_per_token_antiquant_special_cases():
+    """Reading R24 reduces to the other modes where it must: a per-token pair
+    constant over tokens and sequences is the per-tensor pair (aclnnIncre-
+    FlashAttentionV3 "Constraints": per-tensor shape (2)); per-token-per-head
+    pairs equal over heads are the per-token pairs; and K scales all equal
+    to c with zero K offsets are a change of the softmax scale from scale to
+    scale * c over the raw K bytes (aclnnIncreFlashAttentionV3 "Function",
+    the scale multiplies every logit)."""
+    w = make_workload(batch=2, n_q=4, n_kv=2, qk_dim=16, kv_dtype="i8", layout="paged", block_size=16,
+                      lengths=[37, 20], seed=34, antiquant_mode="token")
+    kw = dict(block_table=w.block_table, block_size=16)
+    S = w.antiquant_scale.shape[2]
+    ts, to = torch.tensor([0.031, 0.022]), torch.tensor([0.4, -0.7])
+    tok_s = ts[:, None, None].expand(2, 2, S).contiguous()
+    tok_o = to[:, None, None].expand(2, 2, S).contiguous()
+    o1, l1 = oracle.decode(w.q, w.k_cache, w.v_cache, "paged", w.seq_lens, 2, w.scale, antiquant_scale=tok_s,
+                           antiquant_offset=tok_o, antiquant_mode="token", **kw)
+    o2, l2 = oracle.decode(w.q, w.k_cache, w.v_cache, "paged", w.seq_lens, 2, w.scale, antiquant_scale=ts,
+                           antiquant_offset=to, **kw)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+    # per token and head, equal over heads
+    sth = w.antiquant_scale[:, :, None, :].expand(2, 2, 2, S).contiguous()
+    oth = w.antiquant_offset[:, :, None, :].expand(2, 2, 2, S).contiguous()
+    o3, l3 = oracle.decode(w.q, w.k_cache, w.v_cache, "paged", w.seq_lens, 2, w.scale, antiquant_scale=sth,
+                           antiquant_offset=oth, **kw)
+    o4, l4 = oracle.decode_workload(w)
+    np.testing.assert_array_equal(o3, o4)
+    np.testing.assert_array_equal(l3, l4)
+    # K side: all scales c, offsets 0 -> softmax scale * c over the raw bytes; V side identity
+    c = float(torch.tensor(0.037, dtype=torch.float32))  # the value the fp32 parameter holds
+    ks = torch.ones_like(w.antiquant_scale); ks[0] = c
+    ko = torch.zeros_like(w.antiquant_offset)
+    o5, l5 = oracle.decode(w.q, w.k_cache, w.v_cache, "paged", w.seq_lens, 2, w.scale, antiquant_scale=ks,
+                           antiquant_offset=ko, antiquant_mode="token", **kw)
+    o6, l6 = oracle.decode(w.q, w.k_cache.double(), w.v_cache.double(), "paged", w.seq_lens, 2, w.scale * c, **kw)
+    np.testing.assert_allclose(o5, o6, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l5, l6, rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- P18
 _ROWS_CASES = [
     # (layout, kv dtype, N_q, N_kv passed, D, V dim, MLA value prefix, sink, antiquant mode)
@@ -474,6 +554,8 @@ _ROWS_CASES = [
     ("paged_bsh", "i8", 6, 3, 8, 8, False, False, "tensor"),
     ("bsnd", "bf16", 6, 3, 8, 8, False, True, "channel"),
     ("paged", "bf16", 4, 1, 12, 8, True, False, "channel"),
+    ("paged", "i8", 6, 2, 8, 8, False, True, "token"),
+    ("bnsd", "i8", 6, 3, 8, 8, False, False, "token_head"),
 ]
 
 
@@ -521,21 +603,25 @@ def test_decode_rows_matches_bruteforce(case):
     out, lse = oracle.decode_rows(w.q, w.k_cache, w.v_cache, layout, w.seq_lens, nkv, w.scale, rows,
                                   block_table=w.block_table, block_size=w.block_size, sink=w.sink,
                                   antiquant_scale=w.antiquant_scale, antiquant_offset=w.antiquant_offset,
-                                  v_dim=dv, v_from_k=mla)
+                                  v_dim=dv, v_from_k=mla, antiquant_mode=w.antiquant_mode)
     assert out.shape == (len(rows), dv) and lse.shape == (len(rows),)
 
-    def deq(x, i, g, c):
+    def deq(x, i, g, c, b, j):
         if sc is None:
             return float(x)
-        if sc.ndim == 1:
+        if aq == "tensor":
             return (float(x) + off[i]) * sc[i]
+        if aq == "token":
+            return (float(x) + off[i, b, j]) * sc[i, b, j]
+        if aq == "token_head":
+            return (float(x) + off[i, b, g, j]) * sc[i, b, g, j]
         return (float(x) + off[i, g, c]) * sc[i, g, c]
 
     for r, (b, h) in enumerate(rows):
         g = h // G
         L = lengths[b]
-        K = [[deq(_stored(kc, layout, bt, bs, b, g, j)[c], 0, g, c) for c in range(d)] for j in range(L)]
-        V = [[deq(_stored(vc, layout, bt, bs, b, g, j)[c], 1, g, c) for c in range(dv)] for j in range(L)]
+        K = [[deq(_stored(kc, layout, bt, bs, b, g, j)[c], 0, g, c, b, j) for c in range(d)] for j in range(L)]
+        V = [[deq(_stored(vc, layout, bt, bs, b, g, j)[c], 1, g, c, b, j) for c in range(dv)] for j in range(L)]
         sk = float(w.sink[h]) if use_sink else None
         if L == 0 and sk is None:
             assert np.all(out[r] == 0) and lse[r] == -np.inf
@@ -585,7 +671,9 @@ def test_planted_mistakes_are_caught(monkeypatch):
                          ("token-major", lambda: test_token_major_layouts_equal_logical_kv(16, [0, 1, 15, 16, 17, 40])),
                          ("per-tensor", test_per_tensor_antiquant_is_per_channel_with_constant_vectors),
                          ("rows", lambda: test_decode_rows_matches_bruteforce(0)),
-                         ("rows-int8", lambda: test_decode_rows_matches_bruteforce(4))]:
+                         ("rows-int8", lambda: test_decode_rows_matches_bruteforce(4)),
+                         ("per-token", lambda: test_per_token_antiquant_bruteforce("paged", "token")),
+                         ("per-token-head", lambda: test_per_token_antiquant_bruteforce("bnsd", "token_head"))]:
             try:
                 fn()
             except (AssertionError, IndexError):  # a wrong index may also fall outside the cache
@@ -623,15 +711,34 @@ def test_planted_mistakes_are_caught(monkeypatch):
     orig_kv_rows = attn_ref._kv_rows
 
     def per_tensor_k_v_swapped(k_cache, v_cache, layout, b, g, L, block_table, block_size, qk_dim, v_dim, v_from_k,
-                               aq_scale, aq_offset):
+                               aq_scale, aq_offset, aq_mode=None):
         if aq_scale is not None and aq_scale.ndim == 1:
             aq_scale, aq_offset = aq_scale[::-1].copy(), aq_offset[::-1].copy()
         return orig_kv_rows(k_cache, v_cache, layout, b, g, L, block_table, block_size, qk_dim, v_dim, v_from_k,
-                            aq_scale, aq_offset)
+                            aq_scale, aq_offset, aq_mode)
+
+    def per_token_reversed(k_cache, v_cache, layout, b, g, L, block_table, block_size, qk_dim, v_dim, v_from_k,
+                           aq_scale, aq_offset, aq_mode=None):
+        # token parameters read from the end of the sequence's row backwards
+        if aq_mode == "token":
+            aq_scale, aq_offset = aq_scale.copy(), aq_offset.copy()
+            aq_scale[:, b, :L] = aq_scale[:, b, :L][:, ::-1]
+            aq_offset[:, b, :L] = aq_offset[:, b, :L][:, ::-1]
+        return orig_kv_rows(k_cache, v_cache, layout, b, g, L, block_table, block_size, qk_dim, v_dim, v_from_k,
+                            aq_scale, aq_offset, aq_mode)
+
+    def per_token_first_sequence(k_cache, v_cache, layout, b, g, L, block_table, block_size, qk_dim, v_dim,
+                                 v_from_k, aq_scale, aq_offset, aq_mode=None):
+        # every sequence reads the token parameters of sequence 0
+        if aq_mode in ("token", "token_head"):
+            aq_scale, aq_offset = aq_scale.copy(), aq_offset.copy()
+            aq_scale[:, b], aq_offset[:, b] = aq_scale[:, 0], aq_offset[:, 0]
+        return orig_kv_rows(k_cache, v_cache, layout, b, g, L, block_table, block_size, qk_dim, v_dim, v_from_k,
+                            aq_scale, aq_offset, aq_mode)
 
     def rows_wrong_group(q, k_cache, v_cache, layout, seq_lens, n_kv, scale, rows, block_table=None,
                          block_size=0, sink=None, antiquant_scale=None, antiquant_offset=None, v_dim=None,
-                         v_from_k=False):
+                         v_from_k=False, antiquant_mode=None):
         # decode_rows with query head h sent to KV head h % N_kv (interleaved
         # instead of contiguous groups), everything else as in the oracle
         qf = attn_ref.as_f64(q)
@@ -644,14 +751,15 @@ def test_planted_mistakes_are_caught(monkeypatch):
         out, lse = np.zeros((len(rows), v_dim)), np.zeros(len(rows))
         for i, (b, h) in enumerate(rows):
             K, V = attn_ref._kv_rows(k_cache, v_cache, layout, b, h % n_kv, int(lens[b]), block_table, block_size,
-                                     qk_dim, v_dim, v_from_k, aq_s, aq_o)
+                                     qk_dim, v_dim, v_from_k, aq_s, aq_o, antiquant_mode)
             out[i], lse[i] = attn_ref.attention_row(qf[b, h], K, V, scale, None if sinkf is None else float(sinkf[h]))
         return out, lse
 
     slips = [("decode_rows", rows_wrong_group), ("attention_row", no_scale), ("attention_row", sink_in_numerator),
              ("attention_row", transposed), ("merge", unweighted_merge),
              ("gather_kv", wrong_batch_row), ("gather_kv", wrong_head),
-             ("gather_kv", token_major_read_as_head_major), ("_kv_rows", per_tensor_k_v_swapped)]
+             ("gather_kv", token_major_read_as_head_major), ("_kv_rows", per_tensor_k_v_swapped),
+             ("_kv_rows", per_token_reversed), ("_kv_rows", per_token_first_sequence)]
     for fn_name, bad in slips:
         with monkeypatch.context() as mp:
             mp.setattr(attn_ref, fn_name, bad)
