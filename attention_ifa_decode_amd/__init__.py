@@ -41,11 +41,11 @@ IFA_ERR_PLAN = 561002
 
 IFA_F32, IFA_F16, IFA_BF16, IFA_I8 = 0, 1, 2, 3
 IFA_KV_BNSD, IFA_KV_PAGED, IFA_KV_PAGED_BSH, IFA_KV_BSND = 0, 1, 2, 3
-IFA_ANTIQUANT_PER_CHANNEL, IFA_ANTIQUANT_PER_TENSOR = 0, 1
+IFA_ANTIQUANT_PER_CHANNEL, IFA_ANTIQUANT_PER_TENSOR, IFA_ANTIQUANT_PER_TOKEN, IFA_ANTIQUANT_PER_TOKEN_HEAD = 0, 1, 2, 3
 IFA_MASK_NONE, IFA_MASK_CAUSAL, IFA_MASK_TREE = 0, 3, 9
 _LAYOUT_CODE = {"bnsd": IFA_KV_BNSD, "paged": IFA_KV_PAGED, "paged_bsh": IFA_KV_PAGED_BSH, "bsnd": IFA_KV_BSND}
 
-_AQ_CODE = {"": 0, "channel": 0, "tensor": 1}
+_AQ_CODE = {"": 0, "channel": 0, "tensor": 1, "token": 2, "token_head": 3}
 
 _DTYPE_CODE = {torch.float32: IFA_F32, torch.float16: IFA_F16, torch.bfloat16: IFA_BF16, torch.int8: IFA_I8}
 
@@ -186,11 +186,11 @@ class DecodeCall:
                  antiquant_offset=None, num_splits: int = 0, v_dim: Optional[int] = None,
                  out_dtype: Optional[torch.dtype] = None, with_lse: bool = True, out=None, lse=None,
                  kv_layout: Optional[str] = None, sparse_mode: int = IFA_MASK_NONE, tree_mask=None,
-                 noalloc: bool = False):
+                 noalloc: bool = False, antiquant_mode: Optional[str] = None):
         lib = load_library()
         sh = check_decode(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads, num_key_value_heads,
                           learnable_sink, antiquant_scale, antiquant_offset, v_dim, out_dtype, out, lse, kv_layout,
-                          sparse_mode, tree_mask)
+                          sparse_mode, tree_mask, antiquant_mode=antiquant_mode)
         B, q_seq, n_q, qk_dim, v_dim = sh.batch, sh.q_seq, sh.n_q, sh.qk_dim, sh.v_dim
         kv_layout, out_dtype = sh.layout, sh.out_dtype
         num_blocks, block_size, max_blocks, s_cap = sh.num_blocks, sh.block_size, sh.max_blocks, sh.s_cap
@@ -323,17 +323,23 @@ def decode(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads: int,
            scale_value: float, learnable_sink=None, antiquant_scale=None, antiquant_offset=None,
            num_splits: int = 0, v_dim: Optional[int] = None,
            out_dtype: Optional[torch.dtype] = None, kv_layout: Optional[str] = None,
-           sparse_mode: int = IFA_MASK_NONE, tree_mask=None) -> Tuple[torch.Tensor, torch.Tensor]:
+           sparse_mode: int = IFA_MASK_NONE, tree_mask=None,
+           antiquant_mode: Optional[str] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Decode attention; returns (attention_out (B, N_q, v_dim), softmax_lse (B, N_q) fp32).
     kv_layout: "paged" (default with a block table), "paged_bsh", "bnsd"
     (default without one) or "bsnd"; antiquant parameters of shape (2,) are
     per tensor.  A query of shape (B, S_q, N_q, D) decodes S_q tokens per
     sequence (the last S_q of its length) under ``sparse_mode`` (IFA_MASK_NONE,
     IFA_MASK_CAUSAL, or IFA_MASK_TREE with ``tree_mask`` uint8 (B, S_q, S_q));
-    then out is (B, S_q, N_q, v_dim) and lse (B, S_q, N_q)."""
+    then out is (B, S_q, N_q, v_dim) and lse (B, S_q, N_q).  int8 antiquant
+    parameters are per tensor (2,), per channel (2, N_kv, D), per token
+    (2, B, S) or per token and KV head (2, B, N_kv, S), S the logical
+    capacity; ``antiquant_mode`` ("channel", "tensor", "token", "token_head")
+    names the mode where shapes coincide."""
     call = DecodeCall(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads, num_key_value_heads,
                       scale_value, learnable_sink, antiquant_scale, antiquant_offset, num_splits, v_dim,
-                      out_dtype, kv_layout=kv_layout, sparse_mode=sparse_mode, tree_mask=tree_mask)
+                      out_dtype, kv_layout=kv_layout, sparse_mode=sparse_mode, tree_mask=tree_mask,
+                      antiquant_mode=antiquant_mode)
     out, lse = call.run()
     # the workspace must outlive the queued kernels: the caching allocator
     # keeps it reserved for this stream
@@ -413,7 +419,8 @@ def decode_workload(w, num_splits: Optional[int] = None, **kw):
     return decode(w.q, w.k_cache, w.v_cache, w.block_table, w.seq_lens, w.n_q, w.n_kv, w.scale,
                   learnable_sink=w.sink, antiquant_scale=w.antiquant_scale, antiquant_offset=w.antiquant_offset,
                   num_splits=w.num_splits if num_splits is None else num_splits,
-                  v_dim=w.v_dim, out_dtype=w.out_dtype, kv_layout=w.layout, **kw)
+                  v_dim=w.v_dim, out_dtype=w.out_dtype, kv_layout=w.layout,
+                  antiquant_mode=getattr(w, "antiquant_mode", None), **kw)
 
 
 def call_for_workload(w, num_splits: Optional[int] = None, **kw) -> DecodeCall:
@@ -421,4 +428,5 @@ def call_for_workload(w, num_splits: Optional[int] = None, **kw) -> DecodeCall:
                       learnable_sink=w.sink, antiquant_scale=w.antiquant_scale,
                       antiquant_offset=w.antiquant_offset,
                       num_splits=w.num_splits if num_splits is None else num_splits, v_dim=w.v_dim,
-                      out_dtype=w.out_dtype, kv_layout=w.layout, **kw)
+                      out_dtype=w.out_dtype, kv_layout=w.layout, antiquant_mode=getattr(w, "antiquant_mode", None),
+                      **kw)

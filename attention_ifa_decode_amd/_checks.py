@@ -72,7 +72,8 @@ def _shape(t, want, name):
 def check_decode(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads: int, num_key_value_heads: int,
                  learnable_sink=None, antiquant_scale=None, antiquant_offset=None, v_dim: Optional[int] = None,
                  out_dtype: Optional[torch.dtype] = None, out=None, lse=None, kv_layout: Optional[str] = None,
-                 sparse_mode: int = MASK_NONE, tree_mask=None, device_check: bool = True) -> DecodeShape:
+                 sparse_mode: int = MASK_NONE, tree_mask=None, device_check: bool = True,
+                 antiquant_mode: Optional[str] = None) -> DecodeShape:
     """Check every tensor of a decode call against the others; return its sizes.
 
     Layouts (aclnnIncreFlashAttentionV3 "Constraints", page attention
@@ -176,13 +177,23 @@ def check_decode(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads
         if antiquant_offset.shape != antiquant_scale.shape:
             raise ValueError("antiquant_offset must have the shape of antiquant_scale")
         shp = tuple(antiquant_scale.shape)
-        if shp == (2,):
-            aq_mode = "tensor"
-        elif shp == (2, n_kv, qk_dim):
-            aq_mode = "channel"
+        S = max_blocks * block_size if paged else s_cap  # logical positions of a sequence
+        shapes = {"tensor": (2,), "channel": (2, n_kv, qk_dim), "token": (2, B, S), "token_head": (2, B, n_kv, S)}
+        if antiquant_mode is None:  # by shape; per channel where (2, N_kv, D) and (2, B, S) coincide
+            aq_mode = next((m for m in ("tensor", "channel", "token", "token_head") if shapes[m] == shp), None)
+            if aq_mode is None:
+                raise ValueError(f"antiquant parameters must be (2,), (2, N_kv={n_kv}, D={qk_dim}), "
+                                 f"(2, B={B}, S={S}) or (2, B, N_kv, S), got {shp}")
         else:
-            raise ValueError(f"antiquant parameters must be (2,) or (2, N_kv={n_kv}, D={qk_dim}), got {shp}")
-    elif antiquant_scale is not None or antiquant_offset is not None:
+            if antiquant_mode not in shapes:
+                raise ValueError(f"unknown antiquant_mode {antiquant_mode!r}")
+            if shp != shapes[antiquant_mode]:
+                raise ValueError(f"antiquant_mode {antiquant_mode!r} needs parameters of shape "
+                                 f"{shapes[antiquant_mode]}, got {shp}")
+            aq_mode = antiquant_mode
+        if aq_mode in ("token", "token_head") and qk_dim != 128:
+            raise ValueError("per-token antiquant needs head dim 128")
+    elif antiquant_scale is not None or antiquant_offset is not None or antiquant_mode is not None:
         raise ValueError("antiquant parameters are for an int8 KV cache only")
 
     if sparse_mode not in (MASK_NONE, MASK_CAUSAL, MASK_TREE):

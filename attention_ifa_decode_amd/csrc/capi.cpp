@@ -160,8 +160,10 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
   if (a->kv_dtype == IFA_I8) {
     if (a->antiquant_scale == nullptr || a->antiquant_offset == nullptr)
       return fail(IFA_ERR_PARAM_NULLPTR, "int8 KV needs antiquant_scale and antiquant_offset");
-    if (a->antiquant_mode != IFA_ANTIQUANT_PER_CHANNEL && a->antiquant_mode != IFA_ANTIQUANT_PER_TENSOR)
+    if (a->antiquant_mode < IFA_ANTIQUANT_PER_CHANNEL || a->antiquant_mode > IFA_ANTIQUANT_PER_TOKEN_HEAD)
       return fail(IFA_ERR_PARAM_INVALID, "antiquant_mode %d not supported", a->antiquant_mode);
+    if (a->antiquant_mode >= IFA_ANTIQUANT_PER_TOKEN && a->qk_dim != 128)
+      return fail(IFA_ERR_PARAM_INVALID, "per-token antiquant needs qk_dim 128");
   } else if (a->antiquant_mode != 0) {
     return fail(IFA_ERR_PARAM_INVALID, "antiquant_mode is set for a non-int8 KV cache");
   } else if (!is_float_dtype(a->kv_dtype)) {
@@ -353,6 +355,14 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
     L.aq_stride_kv = per_tensor ? 1 : (int)(p.n_kv * a->qk_dim);
     L.aq_stride_g = per_tensor ? 0 : (int)a->qk_dim;
     L.aq_stride_d = per_tensor ? 0 : 1;
+    // per token: (2, B, S) or (2, B, N_kv, S) over the logical positions S = max_len
+    L.aq_token = a->kv_dtype == IFA_I8 && a->antiquant_mode >= IFA_ANTIQUANT_PER_TOKEN;
+    if (L.aq_token) {
+      const int64_t heads = a->antiquant_mode == IFA_ANTIQUANT_PER_TOKEN_HEAD ? p.n_kv : 1;
+      L.aq_tok_stride_g = heads > 1 ? max_len : 0;
+      L.aq_tok_stride_b = heads * max_len;
+      L.aq_tok_stride_kv = a->batch * heads * max_len;
+    }
     L.scale_log2 = scale_log2;
     if (L.paged) ifa::make_divisor((uint32_t)a->block_size, &L.bs_magic, &L.bs_shift);
     L.plan = plan;

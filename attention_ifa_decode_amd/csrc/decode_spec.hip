@@ -52,7 +52,7 @@ constexpr int kRowB16 = kD * 2;          // bytes of a 16-bit row (and of the in
 constexpr float kRescale = 8.f;
 constexpr float kMrefInit = -1e30f;
 
-template <int KV>
+template <int KV, bool TOK>
 struct SpecShape {
   static constexpr int ESZ = KV == kI8 ? 1 : 2;
   // tiles in the ring: one tile is computed while the next one loads (a
@@ -62,7 +62,10 @@ struct SpecShape {
   static constexpr int CPR = RB / 16;       // 16-byte chunks per row
   static constexpr int TB = kTile * RB;     // bytes of the K (and of the V) tile
   static constexpr int LT = TB / 1024;      // DMA instructions per K (and per V) tile
-  static constexpr int SLOT = 2 * TB;       // K then V
+  // per-token antiquant: the tile's K scale, K offset, V scale and V offset
+  // (32 fp32 each) follow K and V in the slot
+  static constexpr int PB = TOK ? 4 * kTile * 4 : 0;
+  static constexpr int SLOT = 2 * TB + PB;  // K, V, then the per-token parameters
   static constexpr int SMEM = STAGES * SLOT;
   static constexpr int MK = KV == kBF16 ? kBF16 : kF16;  // MFMA operand type
   static_assert(2 * LT * (STAGES - 1) <= 63 && STAGES >= 2 && STAGES <= 3, "vmcnt, ring");
@@ -72,6 +75,15 @@ __device__ __forceinline__ int swz(int t) { return (2 * (t & 3) + ((t >> 2) & 1)
 
 __device__ __forceinline__ void dma16_lane(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off offset:0 nt" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// 4 bytes per lane, lane l's at LDS byte address lds + 4 l
+__device__ __forceinline__ void dma4_lane(const void* src, uint32_t lds) {
+  asm volatile("global_load_lds_dword %0, off offset:0" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ f32x4_t lds_read_f32x4(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) f32x4_t*)(uintptr_t)addr;
 }
 
 template <int N>
@@ -144,9 +156,9 @@ __device__ __forceinline__ u32x2 widen_i8(uint32_t w) {
   return u32x2{__builtin_amdgcn_perm(0x64646464u, b, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u)};
 }
 
-template <int QT, int KV, bool PAGED>
+template <int QT, int KV, bool PAGED, bool TOK>
 __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int work_items) {
-  using S = SpecShape<KV>;
+  using S = SpecShape<KV, TOK>;
   constexpr int RB = S::RB, CPR = S::CPR, TB = S::TB, LT = S::LT, SLOT = S::SLOT, MK = S::MK;
   constexpr int kStages = S::STAGES;
   constexpr bool I8 = KV == kI8;
@@ -199,7 +211,26 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
   // ---- Q^T operand: channels 16 ks + 8 h .. + 7 per k-step (zero for padding rows) ----
   u32x4 qreg[kKSteps];
   float kconst = 0.f;  // int8: sum_d q'_d (offset_d - 1152) over the row
-  if constexpr (I8) {
+  float qsum = 0.f;    // per-token int8: sum_d q_d of the fp16 query
+  if constexpr (I8 && TOK) {
+    // q in fp16 as given (the K scale varies per token and multiplies the score)
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t pair = 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int d = 16 * ks + 8 * h + 2 * w + e;
+          const _Float16 qh = row_ok ? (_Float16)load_as_f32<QT>(a.q, qrow * kD + d) : (_Float16)0.f;
+          part += (float)qh;
+          pair |= (uint32_t)__builtin_bit_cast(uint16_t, qh) << (16 * e);
+        }
+        qreg[ks][w] = pair;
+      }
+    qsum = xor32_sum(part);
+  } else if constexpr (I8) {
     // q' = q * scale_K rounded to fp16, and this lane's half of the constant
     float part = 0.f;
 #pragma unroll
@@ -233,6 +264,18 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
 #pragma unroll
   for (int ks = 0; ks < kKSteps; ++ks) settle(qreg[ks]);
   settle(kconst);
+  settle(qsum);
+
+  // per-token antiquant: rows of this sequence (and KV head) in the K scale,
+  // K offset, V scale and V offset arrays
+  const float* tokp[4] = {nullptr, nullptr, nullptr, nullptr};
+  if constexpr (TOK) {
+    const int64_t base = (int64_t)b * a.aq_tok_stride_b + (int64_t)g * a.aq_tok_stride_g;
+    tokp[0] = a.aq_scale + base;
+    tokp[1] = a.aq_offset + base;
+    tokp[2] = a.aq_scale + a.aq_tok_stride_kv + base;
+    tokp[3] = a.aq_offset + a.aq_tok_stride_kv + base;
+  }
 
   // ---- block-table slice of the split: lane k holds its k-th block id ----
   const uint32_t bi_first = PAGED ? fast_div((uint32_t)start, a.bs_magic, a.bs_shift) : 0;
@@ -289,6 +332,13 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
       dma16_lane(kbase + off, dst + 1024 * i);
       dma16_lane(vbase + off, dst + TB + 1024 * i);
     }
+    if constexpr (TOK) {
+      // parameter array 2 k + (lane / 32), token tstart + lane % 32 (clamped
+      // to the split's last token), to slot byte 2 TB + 128 (2 k + lane / 32)
+      const int tok = min(tstart + (lane & 31), end - 1);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) dma4_lane((lane >> 5 ? tokp[2 * k + 1] : tokp[2 * k]) + tok, dst + 2 * TB + 256 * k);
+    }
   };
 
 #pragma unroll
@@ -322,6 +372,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
   }
 
   float mref = kMrefInit, mtrue = kNegInf, lsum = 0.f, lsum_r = 0.f;
+  float vbias = 0.f;  // per-token int8: sum over tokens of rounded weight * (offset_V - 1152)
   f32x16_t acc[kMTiles];
 #pragma unroll
   for (int mt = 0; mt < kMTiles; ++mt)
@@ -393,8 +444,21 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     // ---- online softmax over this lane's row (column) ----
     // accumulator register r holds token 8 (r / 4) + 4 h + r % 4 of the tile
     float sv[16];
+    if constexpr (TOK) {
+      // score of token t: scale_K[t] (q . (1152 + x_t) + (offset_K[t] - 1152) sum q); this lane's
+      // tokens 8 q4 + 4 h + e lie in four 16-byte groups of each parameter array
+      const uint32_t pa = slot + 2 * TB + 16 * h;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sv[r] = (sacc[r] + kconst) * a.scale_log2;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4_t sk = lds_read_f32x4(pa + 32 * q4), ok = lds_read_f32x4(pa + 128 + 32 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sv[4 * q4 + e] = sk[e] * fmaf(ok[e] - 1152.f, qsum, sacc[4 * q4 + e]) * a.scale_log2;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[r] = (sacc[r] + kconst) * a.scale_log2;
+    }
     if (tstart + kTile > end || tstart + kTile > draft0) {  // the split's tail, or draft tokens
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -415,6 +479,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
       const float alpha = fast_exp2(mref - mnew);  // 0 on the first scores
       lsum *= alpha;
       lsum_r *= alpha;
+      vbias *= alpha;
 #pragma unroll
       for (int mt = 0; mt < kMTiles; ++mt) scale_acc(acc[mt], alpha);
       mref = mnew;
@@ -423,17 +488,35 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     // 0) or 8 + j (k-step 1), rounded to the MFMA operand type
     u32x4 pb[2];
     float pr[16];
+    float pscale[16], pbias[16];  // per-token int8: V scale and offset - 1152 of each token
+    if constexpr (TOK) {
+      const uint32_t pa = slot + 2 * TB + 256 + 16 * h;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4_t sv4 = lds_read_f32x4(pa + 32 * q4), ov4 = lds_read_f32x4(pa + 128 + 32 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pscale[4 * q4 + e] = sv4[e], pbias[4 * q4 + e] = ov4[e] - 1152.f;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float pf = fast_exp2(sv[r] - mref);  // <= 2^8; 0 for removed tokens
       lsum += pf;
-      const uint16_t bits = round16<MK>(pf);
+      // per-token int8: the weight that multiplies the widened V row is
+      // p * scale_V[t]; its rounded value also removes the 1152 bias and adds
+      // the V offset through vbias
+      const uint16_t bits = round16<MK>(TOK ? pf * pscale[r] : pf);
       pr[r] = MK == kBF16 ? (float)__builtin_bit_cast(__bf16, bits) : (float)__builtin_bit_cast(_Float16, bits);
       if (r & 1) pb[r >> 3][(r & 7) >> 1] |= (uint32_t)bits << 16;
       else pb[r >> 3][(r & 7) >> 1] = bits;
     }
+    if constexpr (TOK) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) lsum_r += pr[r];
+      for (int r = 0; r < 16; ++r) vbias = fmaf(pr[r], pbias[r], vbias);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lsum_r += pr[r];
+    }
 
     // ---- O^T += V^T . P^T (MFMA n: k-step n / 4, row tile n % 4) ----
     const uint32_t vt = I8 ? slot : slot + TB;
@@ -453,8 +536,12 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
 
   // ---- partial triple: normalised out, true max, sum relative to it ----
   const float ltot = xor32_sum(lsum);
-  const float lr = xor32_sum(lsum_r);
+  // normaliser: the rounded weights PV applied (per-channel int8 and 16-bit:
+  // this also cancels the 1152 bias exactly), or, per-token, the fp32 weights
+  // whose scaled and rounded values PV applied (the bias leaves through vbias)
+  const float lr = TOK ? ltot : xor32_sum(lsum_r);
   const float inv = lr > 0.f ? 1.f / lr : 0.f;  // 0: every token of the split removed for this row
+  const float vb = TOK ? xor32_sum(vbias) * inv : 0.f;
 #pragma unroll
   for (int mt = 0; mt < kMTiles; ++mt) scale_acc(acc[mt], inv);
   if (row_ok) {
@@ -467,7 +554,10 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
         f32x4_t v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[mt][4 * r4 + e];
-        if constexpr (I8) {
+        if constexpr (TOK) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] += vb;
+        } else if constexpr (I8) {
           // P V ran on 1152 + x: x_hat = (x + offset) * scale per channel (index 1)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -484,15 +574,20 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
   }
 }
 
-template <int QT, int KV>
+template <int QT, int KV, bool TOK>
 hipError_t launch_kv(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
   const int items = p.batch * p.n_kv * ((p.rows_kv + 31) / 32) * p.n_split;
   if (items == 0) return hipSuccess;
   if (p.paged)
-    launch_kernel(gqa_mfma_kernel<QT, KV, true>, dim3(items), dim3(64), stream, ev, p, items);
+    launch_kernel(gqa_mfma_kernel<QT, KV, true, TOK>, dim3(items), dim3(64), stream, ev, p, items);
   else
-    launch_kernel(gqa_mfma_kernel<QT, KV, false>, dim3(items), dim3(64), stream, ev, p, items);
+    launch_kernel(gqa_mfma_kernel<QT, KV, false, TOK>, dim3(items), dim3(64), stream, ev, p, items);
   return hipGetLastError();
+}
+
+template <int QT>
+hipError_t launch_i8(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
+  return p.aq_token ? launch_kv<QT, kI8, true>(p, stream, ev) : launch_kv<QT, kI8, false>(p, stream, ev);
 }
 
 }  // namespace
@@ -507,12 +602,14 @@ hipError_t launch_gqa_mfma(const GqaLaunch& p, hipStream_t stream, const LaunchE
   if (!gqa_mfma_supported(p.q_dtype, p.kv_dtype, p.head_dim)) return hipErrorInvalidValue;
   if (p.kv_dtype == kI8) {
     switch (p.q_dtype) {
-      case kF32: return launch_kv<kF32, kI8>(p, stream, ev);
-      case kF16: return launch_kv<kF16, kI8>(p, stream, ev);
-      default: return launch_kv<kBF16, kI8>(p, stream, ev);
+      case kF32: return launch_i8<kF32>(p, stream, ev);
+      case kF16: return launch_i8<kF16>(p, stream, ev);
+      default: return launch_i8<kBF16>(p, stream, ev);
     }
   }
-  return p.kv_dtype == kBF16 ? launch_kv<kBF16, kBF16>(p, stream, ev) : launch_kv<kF16, kF16>(p, stream, ev);
+  if (p.aq_token) return hipErrorInvalidValue;
+  return p.kv_dtype == kBF16 ? launch_kv<kBF16, kBF16, false>(p, stream, ev)
+                             : launch_kv<kF16, kF16, false>(p, stream, ev);
 }
 
 }  // namespace ifa

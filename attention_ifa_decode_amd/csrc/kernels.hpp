@@ -19,6 +19,11 @@ struct GqaLaunch {
   // entry (i, g, d) of the parameters, i = 0 for K and 1 for V:
   // i * aq_stride_kv + g * aq_stride_g + d * aq_stride_d
   int aq_stride_kv, aq_stride_g, aq_stride_d;
+  // per-token antiquant (MFMA path): entry (i, b, g, token j) of
+  // (2, B, S) or (2, B, N_kv, S) parameters at
+  // i * aq_tok_stride_kv + b * aq_tok_stride_b + g * aq_tok_stride_g + j
+  bool aq_token;
+  int64_t aq_tok_stride_kv, aq_tok_stride_b, aq_tok_stride_g;
   float* ws_o;             // [B][q_seq][n_q][n_split][D]
   float* ws_m;             // [B][q_seq][n_q][n_split]
   float* ws_l;             // [B][q_seq][n_q][n_split]

@@ -91,8 +91,19 @@ typedef enum {
 
 /* Antiquant parameter shapes (aclnnIncreFlashAttentionV3 "Constraints" on
  * antiquantScale and antiquantOffset): per channel (2, N_kv, qk_dim), or per
- * tensor (2); index 0 applies to K, 1 to V. */
-typedef enum { IFA_ANTIQUANT_PER_CHANNEL = 0, IFA_ANTIQUANT_PER_TENSOR = 1 } ifa_antiquant_mode;
+ * tensor (2); index 0 applies to K, 1 to V.  Per token (the
+ * FusedInferAttentionScore blog's antiquantMode 1 per-token and 3 per-token
+ * with per-head, whose shapes the pages do not print): fp32 (2, B, S), or
+ * (2, B, N_kv, S) per token and KV head, one (scale, offset) pair per logical
+ * token position j < S of sequence b, applied to every channel of that
+ * token; S is s_cap for the contiguous layouts and max_blocks_per_seq *
+ * block_size for the paged ones.  Per-token modes need qk_dim 128. */
+typedef enum {
+  IFA_ANTIQUANT_PER_CHANNEL = 0,
+  IFA_ANTIQUANT_PER_TENSOR = 1,
+  IFA_ANTIQUANT_PER_TOKEN = 2,
+  IFA_ANTIQUANT_PER_TOKEN_HEAD = 3
+} ifa_antiquant_mode;
 
 /* Masks of a multi-token decode (the sparseMode values of the
  * FusedInferAttentionScore pages).  With S_q query tokens per sequence of

@@ -170,3 +170,35 @@ def test_update_operands():
         check_update(o, m, m, o, m, m, out=torch.zeros(5, 64, dtype=torch.float16), device_check=False)
     with pytest.raises(ValueError, match="sum_out"):
         check_update(o, m, m, o, m, m, sum_out=torch.zeros(6), device_check=False)
+
+
+def test_per_token_antiquant_shapes():
+    """Per-token parameters (2, B, S) and (2, B, N_kv, S) over the logical
+    capacity S (max_blocks_per_seq * block_size paged, S_cap contiguous);
+    where (2, B, S) coincides with (2, N_kv, D) the mode must be named."""
+    a = _gqa()  # B 3, N_kv 2, block 16, 4 blocks per sequence: S = 64
+    a["k_cache"] = torch.zeros(10, 2, 16, 128, dtype=torch.int8)
+    a["v_cache"] = torch.zeros(10, 2, 16, 128, dtype=torch.int8)
+    for shp, mode in (((2, 3, 64), "token"), ((2, 3, 2, 64), "token_head")):
+        a["antiquant_scale"], a["antiquant_offset"] = torch.zeros(shp), torch.zeros(shp)
+        assert check(**a).antiquant_mode == mode
+        assert check(antiquant_mode=mode, **a).antiquant_mode == mode
+    a["antiquant_scale"], a["antiquant_offset"] = torch.zeros(2, 3, 63), torch.zeros(2, 3, 63)
+    with pytest.raises(ValueError, match="antiquant parameters"):
+        check(**a)
+    a["antiquant_scale"], a["antiquant_offset"] = torch.zeros(2, 3, 64), torch.zeros(2, 3, 64)
+    with pytest.raises(ValueError, match="needs parameters of shape"):
+        check(antiquant_mode="channel", **a)
+    # (2, B, S) == (2, N_kv, D): per channel unless named
+    b = _gqa(B=2, nkv=2, mb=8)  # S = 128 = D
+    b["k_cache"] = torch.zeros(10, 2, 16, 128, dtype=torch.int8)
+    b["v_cache"] = torch.zeros(10, 2, 16, 128, dtype=torch.int8)
+    b["antiquant_scale"], b["antiquant_offset"] = torch.zeros(2, 2, 128), torch.zeros(2, 2, 128)
+    assert check(**b).antiquant_mode == "channel"
+    assert check(antiquant_mode="token", **b).antiquant_mode == "token"
+    c = _gqa(d=64)
+    c["k_cache"] = torch.zeros(10, 2, 16, 64, dtype=torch.int8)
+    c["v_cache"] = torch.zeros(10, 2, 16, 64, dtype=torch.int8)
+    c["antiquant_scale"], c["antiquant_offset"] = torch.zeros(2, 3, 64), torch.zeros(2, 3, 64)
+    with pytest.raises(ValueError, match="head dim 128"):
+        check(antiquant_mode="token", **c)

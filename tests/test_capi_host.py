@@ -141,7 +141,7 @@ def test_int8_rules():
     a = base_args(kv_dtype=ifa.IFA_I8, antiquant_scale=FAKE, antiquant_offset=FAKE,
                   antiquant_mode=ifa.IFA_ANTIQUANT_PER_TENSOR)
     assert ws_size(a)[0] == ifa.IFA_OK
-    a = base_args(kv_dtype=ifa.IFA_I8, antiquant_scale=FAKE, antiquant_offset=FAKE, antiquant_mode=2)
+    a = base_args(kv_dtype=ifa.IFA_I8, antiquant_scale=FAKE, antiquant_offset=FAKE, antiquant_mode=5)
     assert ws_size(a)[0] == ifa.IFA_ERR_PARAM_INVALID
 
 
@@ -325,3 +325,16 @@ def test_noalloc_rejects_oversize_calls_on_the_host():
     assert "scratch" in ifa.last_error()
     bad = base_args(num_heads=0)
     assert lib().ifa_decode_noalloc(ctypes.byref(bad), None) == ifa.IFA_ERR_PARAM_INVALID
+
+
+def test_per_token_antiquant_modes_on_the_host():
+    """Per-token (2) and per-token-per-head (3) antiquant modes are accepted
+    for int8 K/V with head dim 128 and rejected elsewhere; other codes are
+    invalid."""
+    i8 = dict(kv_dtype=ifa.IFA_I8, antiquant_scale=FAKE + 0x500, antiquant_offset=FAKE + 0x600)
+    for mode in (ifa.IFA_ANTIQUANT_PER_TOKEN, ifa.IFA_ANTIQUANT_PER_TOKEN_HEAD):
+        assert ws_size(base_args(antiquant_mode=mode, **i8))[0] == ifa.IFA_OK, ifa.last_error()
+        st, _ = ws_size(base_args(antiquant_mode=mode, qk_dim=64, v_dim=64, **i8))
+        assert st == ifa.IFA_ERR_PARAM_INVALID and "128" in ifa.last_error()
+    assert ws_size(base_args(antiquant_mode=4, **i8))[0] == ifa.IFA_ERR_PARAM_INVALID
+    assert ws_size(base_args(antiquant_mode=ifa.IFA_ANTIQUANT_PER_TOKEN))[0] == ifa.IFA_ERR_PARAM_INVALID

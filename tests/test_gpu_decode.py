@@ -426,6 +426,48 @@ def test_per_tensor_antiquant(layout, splits):
     _full_check(w, splits)
 
 
+@pytest.mark.parametrize("layout", ["paged", "paged_bsh", "bnsd", "bsnd"])
+@pytest.mark.parametrize("mode", ["token", "token_head"])
+@pytest.mark.parametrize("splits", [1, 3])
+def test_per_token_antiquant(layout, mode, splits):
+    """int8 K/V with one (scale, offset) pair per logical token position
+    (FusedInferAttentionScore blog antiquantMode 1, and 3 with per-head
+    pairs; reading R24): ragged lengths across tile and block boundaries,
+    a sink, a permuted paged pool, NaN-poisoned unread slots."""
+    lens = [0, 1, 31, 32, 33, 129, 300, 517]
+    kw = dict(block_size=32, extra_blocks=2) if layout.startswith("paged") else dict(s_cap=520)
+    w = make_workload(batch=len(lens), n_q=16, n_kv=4, qk_dim=128, kv_dtype="i8", layout=layout, lengths=lens,
+                      seed=91 + splits, sink=True, antiquant_mode=mode, **kw)
+    assert w.antiquant_scale.dim() == (3 if mode == "token" else 4)
+    _full_check(w, splits)
+
+
+def test_per_token_antiquant_full_size_sampled_rows():
+    """The int8 workload at full size (B=32, N_q=64, N_kv=8, 16384 tokens,
+    paged block 128, sink) with per-token antiquant pairs (2, 32, 16384);
+    every head of three whole sequences against the oracle."""
+    wg = config_workload(4, device="cuda", antiquant_mode="token")
+    _announce("full size config 4 with per-token antiquant")
+    out, lse = ifa.decode_workload(wg)
+    torch.cuda.synchronize()
+    out = out.double().cpu().numpy()
+    lse = lse.double().cpu().numpy()
+    assert not np.isnan(out).any()
+    w = wg.to("cpu")
+    del wg
+    torch.cuda.empty_cache()
+    rows = whole_sequence_rows(w, 44)
+    ref_out, ref_lse = oracle.decode_workload(w, rows=rows)
+    _compare(w, out, lse, ref_out, ref_lse, rows=rows)
+
+
+def test_per_token_antiquant_rejects_head_dim_64():
+    w = make_workload(batch=2, n_q=4, n_kv=2, qk_dim=64, kv_dtype="i8", layout="paged", block_size=32,
+                      lengths=[40, 7], seed=95, antiquant_mode="token").to("cuda")
+    with pytest.raises(ValueError, match="head dim 128"):
+        ifa.decode_workload(w)
+
+
 def test_full_size_token_major_pool_sampled_rows():
     """The paged bf16 GQA workload at full size (B=64, N_q=32, N_kv=8,
     lengths U[512, 8192]) with its pool in the (blocknum, blocksize, H)

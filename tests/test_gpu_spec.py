@@ -39,14 +39,15 @@ def _check(w, q, mode, tm, splits):
                           learnable_sink=wg.sink, antiquant_scale=wg.antiquant_scale,
                           antiquant_offset=wg.antiquant_offset, num_splits=splits, v_dim=w.v_dim,
                           out_dtype=w.out_dtype, kv_layout=w.layout, sparse_mode=MODES[mode],
-                          tree_mask=None if tm is None else tm.cuda())
+                          tree_mask=None if tm is None else tm.cuda(), antiquant_mode=w.antiquant_mode)
     torch.cuda.synchronize()
     out = out.double().cpu().numpy()
     lse = lse.double().cpu().numpy()
     ref_o, ref_l = oracle.decode_multi(q, w.k_cache, w.v_cache, w.layout, w.seq_lens, w.n_kv, w.scale,
                                        sparse_mode=MODES[mode], tree_mask=tm, block_table=w.block_table,
                                        block_size=w.block_size, sink=w.sink, antiquant_scale=w.antiquant_scale,
-                                       antiquant_offset=w.antiquant_offset, v_dim=w.v_dim)
+                                       antiquant_offset=w.antiquant_offset, v_dim=w.v_dim,
+                                       antiquant_mode=w.antiquant_mode)
     assert out.shape == ref_o.shape and not np.isnan(out).any()
     tol = TOL_F32 if w.kv_dtype == torch.float32 else TOL_LOWP
     excess = np.abs(out - ref_o) - half_ulp(np.maximum(np.abs(out), np.abs(ref_o)), w.out_dtype)
@@ -67,6 +68,18 @@ def test_multi_token_every_dtype(mode, kv):
                       lengths=lens, seed=101, sink=(kv == "i8"), extra_blocks=1)
     q = _query(len(lens), q_seq, 8, 128, w.q.dtype, 102)
     _check(w, q, mode, _tree(len(lens), q_seq, 103) if mode == "tree" else None, 3)
+
+
+@pytest.mark.parametrize("mode", ["causal", "tree"])
+@pytest.mark.parametrize("aq", ["token", "token_head"])
+def test_multi_token_per_token_antiquant(mode, aq):
+    """S_q 4 over an int8 cache with per-token antiquant pairs: the pairs
+    follow the cached token positions, whatever the query token."""
+    q_seq, lens = 4, [2, 5, 33, 300]
+    w = make_workload(batch=len(lens), n_q=16, n_kv=4, qk_dim=128, kv_dtype="i8", layout="paged", block_size=32,
+                      lengths=lens, seed=140, sink=True, antiquant_mode=aq, extra_blocks=1)
+    q = _query(len(lens), q_seq, 16, 128, torch.bfloat16, 141)
+    _check(w, q, mode, _tree(len(lens), q_seq, 142) if mode == "tree" else None, 2)
 
 
 @pytest.mark.parametrize("q_seq,n_q,n_kv,d", [(2, 32, 8, 128), (3, 64, 8, 128), (7, 4, 4, 64), (16, 8, 8, 64),
