@@ -46,8 +46,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kD = 128;
 constexpr int kTile = 32;                // tokens per tile
-constexpr int kKSteps = kD / 16;         // MFMA k-steps of S^T
-constexpr int kMTiles = kD / 32;         // row tiles of O^T
 constexpr int kRowB16 = kD * 2;          // bytes of a 16-bit row (and of the int8 V tile's fp16 copy)
 constexpr float kRescale = 8.f;
 constexpr float kMrefInit = -1e30f;
@@ -129,6 +127,49 @@ __device__ __forceinline__ f32x16_t mfma(const u32x4& x, const u32x4& y, const f
                                                   0, 0, 0);
 }
 
+// 16x16x32 MFMA on 16-bit operands held as raw 16-byte vectors
+template <int KV>
+__device__ __forceinline__ f32x4_t mfma16(const u32x4& x, const u32x4& y, const f32x4_t& c) {
+  if constexpr (KV == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, x), __builtin_bit_cast(bf16x8_t, y), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, x), __builtin_bit_cast(f16x8_t, y), c,
+                                                  0, 0, 0);
+}
+
+// Accumulator tile of the NC-column layout: 32x32 (16 registers) or 16x16 (4)
+template <int NC>
+struct Acc;
+template <>
+struct Acc<32> {
+  typedef f32x16_t type;
+};
+template <>
+struct Acc<16> {
+  typedef f32x4_t type;
+};
+
+template <int NC, int KV>
+__device__ __forceinline__ typename Acc<NC>::type mfma_nc(const u32x4& x, const u32x4& y,
+                                                          const typename Acc<NC>::type& c) {
+  if constexpr (NC == 32) return mfma<KV>(x, y, c);
+  else return mfma16<KV>(x, y, c);
+}
+
+// Sum / max over the lanes that hold the same MFMA column: lanes l ^ 32 (32
+// columns), or l ^ 16, l ^ 32, l ^ 48 (16 columns).
+template <int NC>
+__device__ __forceinline__ float col_sum(float x) {
+  if constexpr (NC == 16) x = xor16_sum(x);
+  return xor32_sum(x);
+}
+template <int NC>
+__device__ __forceinline__ float col_max(float x) {
+  if constexpr (NC == 16) x = xor16_max(x);
+  return xor32_max(x);
+}
+
 // the 16-bit pattern of `v` rounded to the K/V dtype
 template <int KV>
 __device__ __forceinline__ uint16_t round16(float v) {
@@ -138,9 +179,10 @@ __device__ __forceinline__ uint16_t round16(float v) {
 
 // In-place scale of one accumulator tile, kept in accumulator registers (a
 // plain multiply would make the allocator copy the tiles to VGPRs).
-__device__ __forceinline__ void scale_acc(f32x16_t& v, float s) {
+template <typename V>
+__device__ __forceinline__ void scale_acc(V& v, float s) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
+  for (int r = 0; r < (int)(sizeof(V) / sizeof(float)); ++r) {
     float x = v[r];
     float tmp;
     asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
@@ -156,20 +198,30 @@ __device__ __forceinline__ u32x2 widen_i8(uint32_t w) {
   return u32x2{__builtin_amdgcn_perm(0x64646464u, b, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u)};
 }
 
-template <int QT, int KV, bool PAGED, bool TOK>
+template <int QT, int KV, bool PAGED, bool TOK, int NC>
 __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int work_items) {
   using S = SpecShape<KV, TOK>;
   constexpr int RB = S::RB, CPR = S::CPR, TB = S::TB, LT = S::LT, SLOT = S::SLOT, MK = S::MK;
   constexpr int kStages = S::STAGES;
   constexpr bool I8 = KV == kI8;
+  // NC query rows per wave in the MFMA columns: 32 (32x32x16 MFMAs) or 16
+  // (16x16x32, for KV heads with at most 16 query rows)
+  constexpr int KSTEP = NC == 32 ? 16 : 32;  // channels per S^T k-step
+  constexpr int NKS = kD / KSTEP;            // S^T k-steps
+  constexpr int AW = NC == 32 ? 16 : 4;      // registers per accumulator tile
+  constexpr int NSA = kTile / NC;            // S^T tiles per 32-token tile
+  constexpr int NSV = NSA * AW;              // scores per lane and tile
+  constexpr int TS = NC == 32 ? 8 : 16;      // token step between register quads
+  constexpr int NOT = kD / NC;               // O^T tiles
+  typedef typename Acc<NC>::type AccT;
   __shared__ __attribute__((aligned(16))) char ring[S::SMEM];
 
   const int lane = threadIdx.x;
-  const int h = lane >> 5;  // which half of an MFMA k-range this lane feeds
-  const int col = lane & 31;
+  const int kg = lane / NC;  // which group of 8 k-slots of an MFMA this lane feeds
+  const int col = lane % NC;
 
   // ---- work item: (row group, split, KV head, sequence rank) ----
-  const int HG = (a.rows_kv + 31) / 32;
+  const int HG = (a.rows_kv + NC - 1) / NC;
   int rem = blockIdx.x;
   if (rem >= work_items) return;
   const int hg = rem % HG;
@@ -194,7 +246,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
   const int ntiles = (end - start + kTile - 1) / kTile;
 
   // ---- this lane's row (the MFMA column it holds), its mask over the drafts ----
-  const int rr = hg * 32 + col;  // row of the KV head's q_seq * group rows
+  const int rr = hg * NC + col;  // row of the KV head's q_seq * group rows
   const bool row_ok = rr < a.rows_kv;
   const int qi = row_ok ? rr / a.group : 0;
   const int64_t qrow = ((int64_t)b * a.q_seq + qi) * a.n_q + g * a.group + (row_ok ? rr - qi * a.group : 0);
@@ -208,39 +260,39 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     for (int k = 0; k < a.q_seq; ++k) vis |= (m[k] == 0 ? 1u : 0u) << k;
   }
 
-  // ---- Q^T operand: channels 16 ks + 8 h .. + 7 per k-step (zero for padding rows) ----
-  u32x4 qreg[kKSteps];
+  // ---- Q^T operand: channels KSTEP ks + 8 kg .. + 7 per k-step (zero for padding rows) ----
+  u32x4 qreg[NKS];
   float kconst = 0.f;  // int8: sum_d q'_d (offset_d - 1152) over the row
   float qsum = 0.f;    // per-token int8: sum_d q_d of the fp16 query
   if constexpr (I8 && TOK) {
     // q in fp16 as given (the K scale varies per token and multiplies the score)
     float part = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint32_t pair = 0;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int d = 16 * ks + 8 * h + 2 * w + e;
+          const int d = KSTEP * ks + 8 * kg + 2 * w + e;
           const _Float16 qh = row_ok ? (_Float16)load_as_f32<QT>(a.q, qrow * kD + d) : (_Float16)0.f;
           part += (float)qh;
           pair |= (uint32_t)__builtin_bit_cast(uint16_t, qh) << (16 * e);
         }
         qreg[ks][w] = pair;
       }
-    qsum = xor32_sum(part);
+    qsum = col_sum<NC>(part);
   } else if constexpr (I8) {
     // q' = q * scale_K rounded to fp16, and this lane's half of the constant
     float part = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         uint32_t pair = 0;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-          const int d = 16 * ks + 8 * h + 2 * w + e;
+          const int d = KSTEP * ks + 8 * kg + 2 * w + e;
           const int kq = g * a.aq_stride_g + d * a.aq_stride_d;  // K parameters (index 0)
           const _Float16 qh = row_ok ? (_Float16)(load_as_f32<QT>(a.q, qrow * kD + d) * a.aq_scale[kq]) : (_Float16)0.f;
           part = fmaf((float)qh, a.aq_offset[kq] - 1152.f, part);
@@ -248,21 +300,22 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
         }
         qreg[ks][w] = pair;
       }
-    kconst = xor32_sum(part);  // lanes l and l ^ 32 hold the two halves of the channels
+    kconst = col_sum<NC>(part);  // the lanes of one column hold its channels between them
   } else if ((reinterpret_cast<uintptr_t>(a.q) & 15) == 0) {  // 16-byte loads
-    const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + qrow * RB) + h;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + qrow * RB) + kg;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qreg[ks] = row_ok ? qp[2 * ks] : u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < NKS; ++ks) qreg[ks] = row_ok ? qp[KSTEP / 8 * ks] : u32x4{0u, 0u, 0u, 0u};
   } else {  // a query buffer aligned to its element only
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.q) + qrow * RB) + 8 * h;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.q) + qrow * RB) + 8 * kg;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int w = 0; w < 4; ++w)
-        qreg[ks][w] = row_ok ? (uint32_t)qp[16 * ks + 2 * w] | ((uint32_t)qp[16 * ks + 2 * w + 1] << 16) : 0u;
+        qreg[ks][w] =
+            row_ok ? (uint32_t)qp[KSTEP * ks + 2 * w] | ((uint32_t)qp[KSTEP * ks + 2 * w + 1] << 16) : 0u;
   }
 #pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks) settle(qreg[ks]);
+  for (int ks = 0; ks < NKS; ++ks) settle(qreg[ks]);
   settle(kconst);
   settle(qsum);
 
@@ -346,38 +399,50 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     if (s < ntiles) queue_tile(s, s);
 
   // ---- per-lane LDS offsets within a slot ----
-  // S^T A operand: token t = lane % 32, channels 16 ks + 8 h .. + 7: chunk
-  // 2 ks + h of a 16-bit row, or the half h of chunk ks of an int8 row
-  uint32_t offS[kKSteps];
+  // S^T A operand of S^T tile m: token t = NC m + col, channels KSTEP ks + 8 kg
+  // .. + 7: 16-byte chunk KSTEP ks / 8 + kg of a 16-bit row, or 8 bytes of an
+  // int8 row (chunk (KSTEP ks + 8 kg) / 16, half ((KSTEP ks + 8 kg) / 8) % 2)
+  uint32_t offS[NSA][NKS];
 #pragma unroll
-  for (int ks = 0; ks < kKSteps; ++ks)
-    offS[ks] = I8 ? col * RB + 16 * (ks ^ swz(col)) + 8 * h : col * RB + 16 * ((2 * ks + h) ^ swz(col));
+  for (int m = 0; m < NSA; ++m)
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int t = NC * m + col;
+      const int c8 = (KSTEP * ks + 8 * kg) / 8;  // 8-channel group of the row
+      offS[m][ks] = I8 ? t * RB + 16 * ((c8 >> 1) ^ swz(t)) + 8 * (c8 & 1) : t * RB + 16 * (c8 ^ swz(t));
+    }
   // V^T A operand (transposing read) on 16-bit rows (the int8 V tile's fp16
-  // copy): in 16-lane group gq, source lane s reads 4 channels of row
-  // 8 rd + 4 (gq >> 1) + s / 4 at chunk 4 odd + 2 (gq & 1) + (s % 4) / 2, half
-  // (s % 2); the read hands each lane 4 tokens of one channel
-  uint32_t offV[2][2];
+  // copy).  In 16-lane group gq, source lane s = 4 r + q reads 4 channels of
+  // one row, the group a 4-row x 16-channel block, and the read hands lane i
+  // of the group the 4 tokens of channel i of the block.
+  //   32 columns: row 8 rd + 4 (gq / 2) + r, chunk 4 (tile & 1) + 2 (gq & 1)
+  //     + q / 2 (+ 8 (tile / 2) as an immediate), for the k-slots 4 h + 0..3
+  //     (rd 0) and 8 + 4 h + 0..3 (rd 1) of each 16-token k-step;
+  //   16 columns: row 16 rd + 4 gq + r, chunk 2 (tile & 3) + q / 2 (+ 8
+  //     (tile / 4)), for the k-slots 0..3 (tokens 4 kg + 0..3) and 4..7
+  //     (tokens 16 + 4 kg + 0..3) of the single 32-token k-step.
+  // Offsets [tile part][rd]; half q % 2.
+  uint32_t offV[4][2];
   {
     const int s = lane & 15, gq = lane >> 4;
     const int r = s >> 2, q = s & 3;
 #pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-      const int t = 8 * rd + 4 * (gq >> 1) + r;
+    for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-      for (int odd = 0; odd < 2; ++odd) {
-        const int x = 4 * odd + 2 * (gq & 1) + (q >> 1);
-        offV[odd][rd] = t * kRowB16 + 16 * (x ^ swz(t)) + 8 * (q & 1);
+      for (int tp = 0; tp < 4; ++tp) {
+        const int t = NC == 32 ? 8 * rd + 4 * (gq >> 1) + r : 16 * rd + 4 * gq + r;
+        const int x = NC == 32 ? 4 * (tp & 1) + 2 * (gq & 1) + (q >> 1) : 2 * tp + (q >> 1);
+        offV[tp][rd] = t * kRowB16 + 16 * (x ^ swz(t)) + 8 * (q & 1);
       }
-    }
   }
 
   float mref = kMrefInit, mtrue = kNegInf, lsum = 0.f, lsum_r = 0.f;
   float vbias = 0.f;  // per-token int8: sum over tokens of rounded weight * (offset_V - 1152)
-  f32x16_t acc[kMTiles];
+  AccT acc[NOT];
 #pragma unroll
-  for (int mt = 0; mt < kMTiles; ++mt)
+  for (int mt = 0; mt < NOT; ++mt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.f;
+    for (int r = 0; r < AW; ++r) acc[mt][r] = 0.f;
 
   for (int i = 0; i < ntiles; ++i) {
     // tile i has landed once only the loads of the tiles queued after it
@@ -399,22 +464,28 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     const int tstart = start + kTile * i;
 
     // ---- S^T = K . Q^T ----
-    f32x16_t sacc;
+    AccT sacc[NSA];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-    u32x4 kb[kKSteps];
+    for (int m = 0; m < NSA; ++m)
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      if constexpr (I8) {
-        const u32x2 x = lds_read_b64(slot + offS[ks]);
-        const u32x2 w0 = widen_i8(x[0]), w1 = widen_i8(x[1]);
-        kb[ks] = u32x4{w0[0], w0[1], w1[0], w1[1]};
-      } else {
-        kb[ks] = lds_read_b128(slot + offS[ks]);
+      for (int r = 0; r < AW; ++r) sacc[m][r] = 0.f;
+    u32x4 kb[NSA][NKS];
+#pragma unroll
+    for (int m = 0; m < NSA; ++m)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if constexpr (I8) {
+          const u32x2 x = lds_read_b64(slot + offS[m][ks]);
+          const u32x2 w0 = widen_i8(x[0]), w1 = widen_i8(x[1]);
+          kb[m][ks] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+        } else {
+          kb[m][ks] = lds_read_b128(slot + offS[m][ks]);
+        }
       }
-    }
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) sacc = mfma<MK>(kb[ks], qreg[ks], sacc);
+    for (int m = 0; m < NSA; ++m)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) sacc[m] = mfma_nc<NC, MK>(kb[m][ks], qreg[ks], sacc[m]);
 
     // int8: widen this V tile into an fp16 copy in 16-bit row layout, written
     // over the whole slot (K and V, 2 x 4 KB), whose K operands are in
@@ -442,27 +513,30 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     }
 
     // ---- online softmax over this lane's row (column) ----
-    // accumulator register r holds token 8 (r / 4) + 4 h + r % 4 of the tile
-    float sv[16];
+    // score register r (accumulator register r % AW of S^T tile r / AW) holds
+    // token TS (r / 4) + 4 kg + r % 4 of the tile
+    float sv[NSV];
     if constexpr (TOK) {
       // score of token t: scale_K[t] (q . (1152 + x_t) + (offset_K[t] - 1152) sum q); this lane's
-      // tokens 8 q4 + 4 h + e lie in four 16-byte groups of each parameter array
-      const uint32_t pa = slot + 2 * TB + 16 * h;
+      // tokens TS q4 + 4 kg + e lie in 16-byte groups of each parameter array
+      const uint32_t pa = slot + 2 * TB + 16 * kg;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4_t sk = lds_read_f32x4(pa + 32 * q4), ok = lds_read_f32x4(pa + 128 + 32 * q4);
+      for (int q4 = 0; q4 < NSV / 4; ++q4) {
+        const f32x4_t sk = lds_read_f32x4(pa + 4 * TS * q4), ok = lds_read_f32x4(pa + 128 + 4 * TS * q4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sv[4 * q4 + e] = sk[e] * fmaf(ok[e] - 1152.f, qsum, sacc[4 * q4 + e]) * a.scale_log2;
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * q4 + e;
+          sv[r] = sk[e] * fmaf(ok[e] - 1152.f, qsum, sacc[r / AW][r % AW]) * a.scale_log2;
+        }
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sv[r] = (sacc[r] + kconst) * a.scale_log2;
+      for (int r = 0; r < NSV; ++r) sv[r] = (sacc[r / AW][r % AW] + kconst) * a.scale_log2;
     }
     if (tstart + kTile > end || tstart + kTile > draft0) {  // the split's tail, or draft tokens
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = tstart + 8 * (r >> 2) + 4 * h + (r & 3);
+      for (int r = 0; r < NSV; ++r) {
+        const int tok = tstart + TS * (r >> 2) + 4 * kg + (r & 3);
         const uint32_t k = (uint32_t)(tok - draft0);  // draft index; huge for tokens before the drafts
         const uint32_t kept = k < 32u ? (vis >> k) & 1u : 1u;
         const uint32_t keep = (uint32_t)(tok < end) & kept;
@@ -471,8 +545,8 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     }
     float smax = kNegInf;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) smax = fmaxf(smax, sv[r]);
-    smax = xor32_max(smax);  // the other 16 tokens of the column sit in lane ^ 32
+    for (int r = 0; r < NSV; ++r) smax = fmaxf(smax, sv[r]);
+    smax = col_max<NC>(smax);  // the column's other tokens sit in the lanes l ^ 16 / 32 / 48
     mtrue = fmaxf(mtrue, smax);
     if (__builtin_amdgcn_ballot_w64(smax > mref + kRescale)) {
       const float mnew = smax > mref + kRescale ? smax : mref;
@@ -481,25 +555,26 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
       lsum_r *= alpha;
       vbias *= alpha;
 #pragma unroll
-      for (int mt = 0; mt < kMTiles; ++mt) scale_acc(acc[mt], alpha);
+      for (int mt = 0; mt < NOT; ++mt) scale_acc(acc[mt], alpha);
       mref = mnew;
     }
-    // P^T operand: k-slot j of lane half h is accumulator register j (k-step
-    // 0) or 8 + j (k-step 1), rounded to the MFMA operand type
-    u32x4 pb[2];
-    float pr[16];
-    float pscale[16], pbias[16];  // per-token int8: V scale and offset - 1152 of each token
+    // P^T operand: k-slot j of lane group kg in 16-token k-step kk is score
+    // register 8 kk + j (32 columns), or, in the one 32-token k-step, score
+    // register j (16 columns), rounded to the MFMA operand type
+    u32x4 pb[NSV / 8];
+    float pr[NSV];
+    float pscale[NSV], pbias[NSV];  // per-token int8: V scale and offset - 1152 of each token
     if constexpr (TOK) {
-      const uint32_t pa = slot + 2 * TB + 256 + 16 * h;
+      const uint32_t pa = slot + 2 * TB + 256 + 16 * kg;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4_t sv4 = lds_read_f32x4(pa + 32 * q4), ov4 = lds_read_f32x4(pa + 128 + 32 * q4);
+      for (int q4 = 0; q4 < NSV / 4; ++q4) {
+        const f32x4_t sv4 = lds_read_f32x4(pa + 4 * TS * q4), ov4 = lds_read_f32x4(pa + 128 + 4 * TS * q4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) pscale[4 * q4 + e] = sv4[e], pbias[4 * q4 + e] = ov4[e] - 1152.f;
       }
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < NSV; ++r) {
       const float pf = fast_exp2(sv[r] - mref);  // <= 2^8; 0 for removed tokens
       lsum += pf;
       // per-token int8: the weight that multiplies the widened V row is
@@ -512,45 +587,51 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     }
     if constexpr (TOK) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) vbias = fmaf(pr[r], pbias[r], vbias);
+      for (int r = 0; r < NSV; ++r) vbias = fmaf(pr[r], pbias[r], vbias);
     } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) lsum_r += pr[r];
+      for (int r = 0; r < NSV; ++r) lsum_r += pr[r];
     }
 
-    // ---- O^T += V^T . P^T (MFMA n: k-step n / 4, row tile n % 4) ----
+    // ---- O^T += V^T . P^T ----
+    // 32 columns: MFMA n takes k-step n / 4 and row tile n % 4 (32 channels);
+    // 16 columns: MFMA n takes row tile n (16 channels) over all 32 tokens
     const uint32_t vt = I8 ? slot : slot + TB;
-    const uint32_t bV[2][2] = {{vt + offV[0][0], vt + offV[0][1]}, {vt + offV[1][0], vt + offV[1][1]}};
-    u32x4 vb[2 * kMTiles];
+    u32x4 vb[8];
 #pragma unroll
-    for (int n = 0; n < 2 * kMTiles; ++n) {
-      const int kk = n / kMTiles, mt = n % kMTiles;
-      const uint32_t imm = kRowB16 * 16 * kk + 128 * (mt >> 1);
-      const s16x4_t lo = lds_read_tr16(bV[mt & 1][0] + imm);
-      const s16x4_t hi = lds_read_tr16(bV[mt & 1][1] + imm);
+    for (int n = 0; n < 8; ++n) {
+      const int kk = NC == 32 ? n / NOT : 0, mt = NC == 32 ? n % NOT : n;
+      const int tp = NC == 32 ? (mt & 1) : (mt & 3);
+      const uint32_t imm = kRowB16 * 16 * kk + 128 * (NC == 32 ? (mt >> 1) : (mt >> 2));
+      const s16x4_t lo = lds_read_tr16(vt + offV[tp][0] + imm);
+      const s16x4_t hi = lds_read_tr16(vt + offV[tp][1] + imm);
       vb[n] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
-    for (int n = 0; n < 2 * kMTiles; ++n) acc[n % kMTiles] = mfma<MK>(vb[n], pb[n / kMTiles], acc[n % kMTiles]);
+    for (int n = 0; n < 8; ++n) {
+      const int kk = NC == 32 ? n / NOT : 0, mt = NC == 32 ? n % NOT : n;
+      acc[mt] = mfma_nc<NC, MK>(vb[n], pb[kk], acc[mt]);
+    }
   }
 
   // ---- partial triple: normalised out, true max, sum relative to it ----
-  const float ltot = xor32_sum(lsum);
+  const float ltot = col_sum<NC>(lsum);
   // normaliser: the rounded weights PV applied (per-channel int8 and 16-bit:
   // this also cancels the 1152 bias exactly), or, per-token, the fp32 weights
   // whose scaled and rounded values PV applied (the bias leaves through vbias)
-  const float lr = TOK ? ltot : xor32_sum(lsum_r);
+  const float lr = TOK ? ltot : col_sum<NC>(lsum_r);
   const float inv = lr > 0.f ? 1.f / lr : 0.f;  // 0: every token of the split removed for this row
-  const float vb = TOK ? xor32_sum(vbias) * inv : 0.f;
+  const float vb = TOK ? col_sum<NC>(vbias) * inv : 0.f;
 #pragma unroll
-  for (int mt = 0; mt < kMTiles; ++mt) scale_acc(acc[mt], inv);
+  for (int mt = 0; mt < NOT; ++mt) scale_acc(acc[mt], inv);
   if (row_ok) {
+    // O^T tile mt, register 4 r4 + e: channel NC mt + 8 r4 + 4 kg + e
     float* o = a.ws_o + (qrow * a.n_split + split) * kD;
 #pragma unroll
-    for (int mt = 0; mt < kMTiles; ++mt)
+    for (int mt = 0; mt < NOT; ++mt)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = 32 * mt + 8 * r4 + 4 * h;
+      for (int r4 = 0; r4 < AW / 4; ++r4) {
+        const int d = NC * mt + 8 * r4 + 4 * kg;
         f32x4_t v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = acc[mt][4 * r4 + e];
@@ -567,22 +648,30 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
         }
         *reinterpret_cast<f32x4_t*>(o + d) = v;
       }
-    if (h == 0) {
+    if (kg == 0) {
       a.ws_m[qrow * a.n_split + split] = mtrue * kLn2;
       a.ws_l[qrow * a.n_split + split] = ltot > 0.f ? ltot * fast_exp2(mref - mtrue) : 0.f;
     }
   }
 }
 
-template <int QT, int KV, bool TOK>
-hipError_t launch_kv(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
-  const int items = p.batch * p.n_kv * ((p.rows_kv + 31) / 32) * p.n_split;
+template <int QT, int KV, bool TOK, int NC>
+hipError_t launch_nc(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
+  const int items = p.batch * p.n_kv * ((p.rows_kv + NC - 1) / NC) * p.n_split;
   if (items == 0) return hipSuccess;
   if (p.paged)
-    launch_kernel(gqa_mfma_kernel<QT, KV, true, TOK>, dim3(items), dim3(64), stream, ev, p, items);
+    launch_kernel(gqa_mfma_kernel<QT, KV, true, TOK, NC>, dim3(items), dim3(64), stream, ev, p, items);
   else
-    launch_kernel(gqa_mfma_kernel<QT, KV, false, TOK>, dim3(items), dim3(64), stream, ev, p, items);
+    launch_kernel(gqa_mfma_kernel<QT, KV, false, TOK, NC>, dim3(items), dim3(64), stream, ev, p, items);
   return hipGetLastError();
+}
+
+// A KV head's query rows fill MFMA columns: 16 per wave when there are at
+// most 16 of them (16x16x32 MFMAs: half the softmax, score and output
+// registers of the 32-column layout for the padding that remains), else 32.
+template <int QT, int KV, bool TOK>
+hipError_t launch_kv(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
+  return p.rows_kv <= 16 ? launch_nc<QT, KV, TOK, 16>(p, stream, ev) : launch_nc<QT, KV, TOK, 32>(p, stream, ev);
 }
 
 template <int QT>
