@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
                     [--num-splits N] [--kv-layout L] [--q-seq S --mask M]
-                    [--no-cpu-baseline] [--no-read-ceiling] [--reps R]
+                    [--no-cpu-baseline] [--no-read-ceiling] [--reps R] [--graph]
 
 One step = one pass of the whole path over one batch: the split-KV decode
 kernel (block-table gather, QK^T, online softmax, PV, partial triples) and the
@@ -54,6 +54,14 @@ TRAFFIC_FILES = {
 }
 
 
+# SQ / GRBM counter summaries (MFMA busy fraction, VALU issue fraction) per workload
+COUNTER_FILES = {
+    3: ("gqa_mfma_c3_bf16_paged_sq_counters.txt", GQA_MFMA_SOURCES),
+    4: ("gqa_mfma_c4_i8_paged_sink_sq_counters.txt", GQA_MFMA_SOURCES),
+    5: ("mla_splitkv_c5_bf16_paged_sq_counters.txt", MLA_SOURCES),
+}
+
+
 def kernel_source_hash(sources=GQA_MFMA_SOURCES) -> str:
     """Hash of the split-KV kernel's source with comments and whitespace
     removed, so that only a change to the code itself invalidates the stored
@@ -100,6 +108,35 @@ def read_traffic(config_idx: int):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def _summary_fields(path):
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip().split()[0] if v.strip() else ""
+    return kv
+
+
+def read_counters(config_idx: int):
+    """MFMA busy and VALU issue fractions of the split-KV kernel from the
+    committed SQ counter summary, or None if absent or taken on a different
+    kernel source."""
+    if config_idx not in COUNTER_FILES:
+        return None
+    name, sources = COUNTER_FILES[config_idx]
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    kv = _summary_fields(path)
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash(sources):
+        return None
+    try:
+        return {"mfma_busy_frac": float(kv["mfma_busy_frac"]), "valu_issue_frac": float(kv["valu_issue_frac"]),
+                "source": "profiles/" + name}
     except (KeyError, ValueError):
         return None
 
@@ -217,6 +254,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true")
     ap.add_argument("--reps", type=int, default=100, help="reps of the step-median and kernel-time loops")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of a captured HIP graph (one step per input copy)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first, so that HBM byte "
@@ -281,13 +320,38 @@ def main():
 
     # The timed region: K whole steps (ifa_decode: the split-KV kernel, then
     # the combine), plain calls on the stream, events only around the loop.
+    # With --graph the K steps are replays of one captured HIP graph that
+    # holds `copies` steps (one per input copy), so the host does not pace
+    # small workloads.
     K = args.steps
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    graph = None
+    if args.graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for c in calls:
+                c.run()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for c in calls:
+                c.run()
+        torch.cuda.synchronize()
+        K = -(-K // copies) * copies  # whole replays
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     t_start.record(stream)
-    for i in range(K):
-        calls[i % copies].run()
+    if graph is not None:
+        for _ in range(K // copies):
+            graph.replay()
+    else:
+        for i in range(K):
+            calls[i % copies].run()
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / K
@@ -366,6 +430,7 @@ def main():
             "mask": args.mask if args.q_seq > 1 else "none",
             "kv_bytes_per_step": kv_bytes,
             "input_copies": copies,
+            "timed_as": "HIP graph replays" if args.graph else "plain ifa_decode calls",
             "parallelism": "none (1 GPU)",
         },
         "roofline": {
@@ -384,6 +449,7 @@ def main():
             "read_ceiling_gbs": None if ceiling is None else round(ceiling, 1),
             "frac_of_read_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
             "flops_per_launch": flops,
+            "counters": read_counters(args.config) if args.kv_layout is None and args.q_seq == 1 else None,
             "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2) if w.qk_dim == 576 else None,
             "mfma_frac_bf16_dense": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
             if w.qk_dim == 576 else None,

@@ -54,3 +54,25 @@ def test_source_hash_ignores_comments_and_whitespace(tmp_path, monkeypatch):
     assert bench.kernel_source_hash(["a.hip"]) == h0
     a.write_text("int f(int x) { return x + 2; }\n")
     assert bench.kernel_source_hash(["a.hip"]) != h0
+
+
+def test_every_counter_summary_is_consistent():
+    """The MFMA busy fraction is the MFMA busy cycles over active cycles x
+    1024 SIMDs, and the busy cycles are the MFMA instructions times their
+    cycles (32 for 32x32x16, 16 for 16x16x32)."""
+    for cfg, (name, sources) in bench.COUNTER_FILES.items():
+        path = os.path.join(ROOT, "profiles", name)
+        assert os.path.exists(path), name
+        kv = _fields(path)
+        cyc = float(kv["GRBM_GUI_ACTIVE"]) / 8
+        assert abs(cyc - float(kv["active_cycles_per_xcd"])) < 1, name
+        frac = float(kv["SQ_VALU_MFMA_BUSY_CYCLES"]) / (cyc * 1024)
+        assert abs(frac - float(kv["mfma_busy_frac"])) < 1e-4, name
+        per = float(kv["SQ_VALU_MFMA_BUSY_CYCLES"]) / float(kv["SQ_INSTS_MFMA"])
+        assert per in (16.0, 32.0), name
+        assert 0 < frac < 1 and 0 < float(kv["valu_issue_frac"]) < 1, name
+        got = bench.read_counters(cfg)
+        if kv["kernel_source_sha256_16"] == bench.kernel_source_hash(sources):
+            assert got["mfma_busy_frac"] == float(kv["mfma_busy_frac"])
+        else:
+            assert got is None
