@@ -7,7 +7,8 @@
 
 namespace ifa {
 
-// Split-KV decode over one KV head group per workgroup (VALU path).
+// Split-KV decode of the GQA shapes: the MFMA kernel (head dim 128, 16-bit or
+// int8 K/V) and the VALU kernel (f32 K/V, head dim 64) take the same launch.
 struct GqaLaunch {
   const void* q;
   const void* k;
@@ -147,8 +148,9 @@ inline void launch_kernel(K kernel, dim3 grid, dim3 block, hipStream_t stream, c
 }
 
 hipError_t launch_gqa_splitkv(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev = nullptr);
-// Multi-token decode on MFMA: one wave per (sequence, KV head, 32 query rows,
-// split); 16-bit K/V with head dim 128.
+// GQA decode on the matrix cores (any number of query tokens): one wave per
+// (sequence, KV head, group of 16 or 32 query rows, split); 16-bit K/V, or
+// int8 K/V with per-channel, per-tensor or per-token antiquant, head dim 128.
 bool gqa_mfma_supported(int q_dtype, int kv_dtype, int head_dim);
 hipError_t launch_gqa_mfma(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev = nullptr);
 hipError_t launch_mla_splitkv(const MlaLaunch& p, hipStream_t stream, const LaunchEvents* ev = nullptr);
