@@ -23,7 +23,8 @@
 //       rounded to the K/V dtype (normalised by the sum of the rounded
 //       weights; the partial's sum uses the fp32 weights).
 // The operand and accumulator layouts are those of the MLA kernel, on
-// 256-byte rows: row t keeps its 16-byte chunk c at position c ^ swz(t).
+// 256-byte rows: row t keeps its 16-byte chunk c at position c ^ swz16(t)
+// (swz(t) on the 128-byte rows of an int8 tile).
 //
 // int8 K/V (antiquant x_hat = (x + offset) * scale, per channel or per
 // tensor): the stored bytes become the exact fp16 values 1152 + x with one
@@ -69,7 +70,25 @@ struct SpecShape {
   static_assert(2 * LT * (STAGES - 1) <= 63 && STAGES >= 2 && STAGES <= 3, "vmcnt, ring");
 };
 
+// Row t of an int8 tile (8 chunks of 16 bytes) keeps chunk c at position
+// c ^ swz(t).
 __device__ __forceinline__ int swz(int t) { return (2 * (t & 3) + ((t >> 2) & 1)) ^ (2 * ((t >> 3) & 1)); }
+
+// Row t of a 16-bit tile (16 chunks, 256 bytes: every row starts in LDS bank
+// 0) keeps chunk c at position c ^ swz16(t), with swz16 the bit order of
+// t mod 16 reversed and bit 0 also folded into the lowest bit:
+//   - 16 consecutive rows take 16 different positions (the S^T operand reads,
+//     16 rows per 16-lane phase);
+//   - 8 consecutive rows (from a multiple of 8) differ in swz16 / 2, and 4
+//     consecutive rows (from a multiple of 4) in swz16 / 4 (the transposing
+//     V^T reads: 8 rows x 2 chunks, or 4 rows x 4 chunks, per 32-lane phase);
+//   - rows 2j and 2j + 1 differ in parity (the int8 V widening writes: 2 rows
+//     x 8 even or 8 odd chunk positions per 16-lane phase).
+// So none of these accesses meets another in one bank (a 3-bit swizzle left
+// each of them two-way conflicted).
+__device__ __forceinline__ int swz16(int t) {
+  return 8 * (t & 1) + 4 * ((t >> 1) & 1) + 2 * ((t >> 2) & 1) + (((t >> 3) ^ t) & 1);
+}
 
 __device__ __forceinline__ void dma16_lane(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off offset:0 nt" ::"v"(src), "{m0}"(lds) : "memory");
@@ -348,7 +367,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
   const uint32_t ring_lds = lds_addr(ring);
 
   // Queue tile j into ring slot `slot`: LDS chunk position P of the K (or V)
-  // tile holds row t = P / CPR, chunk (P % CPR) ^ swz(t) of token tstart + t
+  // tile holds row t = P / CPR, chunk (P % CPR) ^ swz16(t) (int8: swz(t)) of token tstart + t
   // (rows past the split's end repeat its last row).  A tile's 32 tokens lie
   // in at most 3 cache blocks.
   auto queue_tile = [&](int j, int slot) {
@@ -367,7 +386,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     for (int i = 0; i < LT; ++i) {
       const int P = 64 * i + lane;
       const int t = P / CPR;
-      const int c = (P % CPR) ^ swz(t);
+      const int c = (P % CPR) ^ (I8 ? swz(t) : swz16(t));
       const uint32_t tok = (uint32_t)min(tstart + t, end - 1);
       uint64_t row;
       if constexpr (PAGED) {
@@ -409,31 +428,34 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     for (int ks = 0; ks < NKS; ++ks) {
       const int t = NC * m + col;
       const int c8 = (KSTEP * ks + 8 * kg) / 8;  // 8-channel group of the row
-      offS[m][ks] = I8 ? t * RB + 16 * ((c8 >> 1) ^ swz(t)) + 8 * (c8 & 1) : t * RB + 16 * (c8 ^ swz(t));
+      offS[m][ks] = I8 ? t * RB + 16 * ((c8 >> 1) ^ swz(t)) + 8 * (c8 & 1) : t * RB + 16 * (c8 ^ swz16(t));
     }
   // V^T A operand (transposing read) on 16-bit rows (the int8 V tile's fp16
   // copy).  In 16-lane group gq, source lane s = 4 r + q reads 4 channels of
   // one row, the group a 4-row x 16-channel block, and the read hands lane i
   // of the group the 4 tokens of channel i of the block.
-  //   32 columns: row 8 rd + 4 (gq / 2) + r, chunk 4 (tile & 1) + 2 (gq & 1)
-  //     + q / 2 (+ 8 (tile / 2) as an immediate), for the k-slots 4 h + 0..3
-  //     (rd 0) and 8 + 4 h + 0..3 (rd 1) of each 16-token k-step;
-  //   16 columns: row 16 rd + 4 gq + r, chunk 2 (tile & 3) + q / 2 (+ 8
-  //     (tile / 4)), for the k-slots 0..3 (tokens 4 kg + 0..3) and 4..7
-  //     (tokens 16 + 4 kg + 0..3) of the single 32-token k-step.
-  // Offsets [tile part][rd]; half q % 2.
-  uint32_t offV[4][2];
+  //   32 columns: row 8 rd + 4 (gq / 2) + r, chunk 8 hi + 4 (tile & 1) + 2
+  //     (gq & 1) + q / 2 with hi = tile / 2, for the k-slots 4 h + 0..3 (rd 0)
+  //     and 8 + 4 h + 0..3 (rd 1) of each 16-token k-step (k-step 1: rows
+  //     16 further, an immediate, as the swizzle repeats every 16 rows);
+  //   16 columns: row 16 rd + 4 gq + r, chunk 8 hi + 2 (tile & 3) + q / 2
+  //     with hi = tile / 4, for the k-slots 0..3 (tokens 4 kg + 0..3) and
+  //     4..7 (tokens 16 + 4 kg + 0..3) of the single 32-token k-step.
+  // Offsets [hi][tile part][rd]; half q % 2.
+  uint32_t offV[2][4][2];
   {
     const int s = lane & 15, gq = lane >> 4;
     const int r = s >> 2, q = s & 3;
 #pragma unroll
-    for (int rd = 0; rd < 2; ++rd)
+    for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-      for (int tp = 0; tp < 4; ++tp) {
-        const int t = NC == 32 ? 8 * rd + 4 * (gq >> 1) + r : 16 * rd + 4 * gq + r;
-        const int x = NC == 32 ? 4 * (tp & 1) + 2 * (gq & 1) + (q >> 1) : 2 * tp + (q >> 1);
-        offV[tp][rd] = t * kRowB16 + 16 * (x ^ swz(t)) + 8 * (q & 1);
-      }
+      for (int rd = 0; rd < 2; ++rd)
+#pragma unroll
+        for (int tp = 0; tp < 4; ++tp) {
+          const int t = NC == 32 ? 8 * rd + 4 * (gq >> 1) + r : 16 * rd + 4 * gq + r;
+          const int x = 8 * hi + (NC == 32 ? 4 * (tp & 1) + 2 * (gq & 1) + (q >> 1) : 2 * tp + (q >> 1));
+          offV[hi][tp][rd] = t * kRowB16 + 16 * (x ^ swz16(t)) + 8 * (q & 1);
+        }
   }
 
   float mref = kMrefInit, mtrue = kNegInf, lsum = 0.f, lsum_r = 0.f;
@@ -504,8 +526,8 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
         const int c = (P & 7) ^ swz(t);
         const u32x2 w0 = widen_i8(x[k][0]), w1 = widen_i8(x[k][1]), w2 = widen_i8(x[k][2]), w3 = widen_i8(x[k][3]);
         const u32x4 lo = {w0[0], w0[1], w1[0], w1[1]}, hi = {w2[0], w2[1], w3[0], w3[1]};
-        lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c) ^ swz(t)), lo);
-        lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c + 1) ^ swz(t)), hi);
+        lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c) ^ swz16(t)), lo);
+        lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c + 1) ^ swz16(t)), hi);
       }
       // the reads below see this wave's writes
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -602,9 +624,10 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     for (int n = 0; n < 8; ++n) {
       const int kk = NC == 32 ? n / NOT : 0, mt = NC == 32 ? n % NOT : n;
       const int tp = NC == 32 ? (mt & 1) : (mt & 3);
-      const uint32_t imm = kRowB16 * 16 * kk + 128 * (NC == 32 ? (mt >> 1) : (mt >> 2));
-      const s16x4_t lo = lds_read_tr16(vt + offV[tp][0] + imm);
-      const s16x4_t hi = lds_read_tr16(vt + offV[tp][1] + imm);
+      const int hi8 = NC == 32 ? (mt >> 1) : (mt >> 2);
+      const uint32_t imm = kRowB16 * 16 * kk;
+      const s16x4_t lo = lds_read_tr16(vt + offV[hi8][tp][0] + imm);
+      const s16x4_t hi = lds_read_tr16(vt + offV[hi8][tp][1] + imm);
       vb[n] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 #pragma unroll
