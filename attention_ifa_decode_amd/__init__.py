@@ -43,6 +43,7 @@ IFA_F32, IFA_F16, IFA_BF16, IFA_I8 = 0, 1, 2, 3
 IFA_KV_BNSD, IFA_KV_PAGED, IFA_KV_PAGED_BSH, IFA_KV_BSND = 0, 1, 2, 3
 IFA_ANTIQUANT_PER_CHANNEL, IFA_ANTIQUANT_PER_TENSOR, IFA_ANTIQUANT_PER_TOKEN, IFA_ANTIQUANT_PER_TOKEN_HEAD = 0, 1, 2, 3
 IFA_MASK_NONE, IFA_MASK_CAUSAL, IFA_MASK_TREE = 0, 3, 9
+IFA_CHECK_BAD_LENGTH, IFA_CHECK_BAD_BLOCK = 1, 2
 _LAYOUT_CODE = {"bnsd": IFA_KV_BNSD, "paged": IFA_KV_PAGED, "paged_bsh": IFA_KV_PAGED_BSH, "bsnd": IFA_KV_BSND}
 
 _AQ_CODE = {"": 0, "channel": 0, "tensor": 1, "token": 2, "token_head": 3}
@@ -63,6 +64,7 @@ EXPORTED = (
     "ifa_kv_cache_write",
     "ifa_paged_block_count",
     "ifa_read_bandwidth_probe",
+    "ifa_decode_check_inputs",
     "ifa_last_error",
 )
 
@@ -135,12 +137,13 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.ifa_paged_block_count.argtypes = [ctypes.POINTER(I64), I64, I64]
     lib.ifa_paged_block_count.restype = I64
     lib.ifa_read_bandwidth_probe.argtypes = [P, SZ, P, I32, P]
+    lib.ifa_decode_check_inputs.argtypes = [args_p, P, P]
     lib.ifa_last_error.argtypes = []
     lib.ifa_last_error.restype = ctypes.c_char_p
     for name in ("ifa_decode_workspace_size", "ifa_decode_num_splits", "ifa_decode_split_mode", "ifa_decode",
                  "ifa_decode_splitkv",
                  "ifa_decode_splitkv_timed", "ifa_decode_combine", "attn_update", "ifa_kv_cache_write",
-                 "ifa_decode_noalloc",
+                 "ifa_decode_noalloc", "ifa_decode_check_inputs",
                  "ifa_read_bandwidth_probe"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
@@ -257,6 +260,15 @@ class DecodeCall:
             _check(self._lib.ifa_decode(ctypes.byref(self.args), self.workspace.data_ptr(), self.workspace_bytes,
                                         _stream_handle()))
         return self.out, self.lse
+
+    def check_inputs(self) -> torch.Tensor:
+        """Queue the input check (ifa_decode_check_inputs) on the current
+        stream; returns a one-element int32 GPU tensor holding, once the
+        stream has run it, IFA_CHECK_BAD_LENGTH | IFA_CHECK_BAD_BLOCK bits for
+        the lengths and block-table entries the decode would clamp (0: none)."""
+        flags = torch.empty(1, dtype=torch.int32, device=self.out.device)
+        _check(self._lib.ifa_decode_check_inputs(ctypes.byref(self.args), flags.data_ptr(), _stream_handle()))
+        return flags
 
     def _ws(self) -> int:
         if self.noalloc:

@@ -589,6 +589,24 @@ int64_t ifa_paged_block_count(const int64_t* lengths, int64_t batch, int64_t blo
   return total;
 }
 
+ifa_status ifa_decode_check_inputs(const ifa_decode_args* args, int32_t* flags, hipStream_t stream) {
+  if (!flags) return fail(IFA_ERR_PARAM_NULLPTR, "flags is NULL");
+  Plan p;
+  ifa_status st = validate_and_plan(args, &p);
+  if (st != IFA_OK) return st;
+  ifa::CheckLaunch C{};
+  C.seq_lens = args->actual_seq_lengths;
+  C.block_table = is_paged(args->kv_layout) ? args->block_table : nullptr;
+  C.flags = flags;
+  C.batch = args->batch;
+  C.block_size = is_paged(args->kv_layout) ? args->block_size : 1;
+  C.max_blocks = is_paged(args->kv_layout) ? args->max_blocks_per_seq : 0;
+  C.s_cap = is_paged(args->kv_layout) ? args->max_blocks_per_seq * args->block_size : args->s_cap;
+  C.num_blocks = args->num_blocks;
+  if ((st = runtime(ifa::launch_check(C, stream), "input check launch")) != IFA_OK) return st;
+  return ok();
+}
+
 ifa_status ifa_read_bandwidth_probe(const void* buf, size_t bytes, uint32_t* out, int32_t workgroups,
                                     hipStream_t stream) {
   if (workgroups < 1 || workgroups > (1 << 20)) return fail(IFA_ERR_PARAM_INVALID, "workgroups outside [1, 2^20]");

@@ -159,6 +159,18 @@ hipError_t launch_combine(const CombineLaunch& p, hipStream_t stream);
 // sequence, for the longest-first dispatch of the split-KV kernels.
 hipError_t launch_plan(const int64_t* seq_lens, int batch, int64_t cap, int2* plan, hipStream_t stream);
 hipError_t launch_update(const UpdateLaunch& p, hipStream_t stream);
+// Input check: bit kCheckBadLength if a length lies outside [0, s_cap], bit
+// kCheckBadBlock if a block-table entry the call reads lies outside
+// [0, num_blocks); one int32 word to flags.
+constexpr int32_t kCheckBadLength = 1, kCheckBadBlock = 2;
+struct CheckLaunch {
+  const int64_t* seq_lens;
+  const int32_t* block_table;  // null for the contiguous layouts
+  int32_t* flags;
+  int64_t batch, s_cap, block_size, max_blocks, num_blocks;
+};
+hipError_t launch_check(const CheckLaunch& p, hipStream_t stream);
+
 // Read-stream probe: reads bytes / 16 chunks of buf once, writes one word per
 // workgroup to out.
 hipError_t launch_read_probe(const void* buf, uint64_t bytes, uint32_t* out, int workgroups, hipStream_t stream);

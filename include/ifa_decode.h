@@ -137,8 +137,10 @@ typedef struct {
   int64_t v_dim;                     /* == qk_dim, or 512 with qk_dim 576 (MLA) */
   int64_t block_size;                /* paged: multiple of 16 (32 for int8), 16..1024 */
   int64_t max_blocks_per_seq;        /* paged: second dim of block_table */
-  int64_t num_blocks;                /* paged: pool size; block ids are clamped to it */
-  int64_t s_cap;                     /* contiguous: padded length; lengths are clamped to it */
+  int64_t num_blocks;                /* paged: pool size; block ids are clamped to it
+                                        (ifa_decode_check_inputs reports ids outside it) */
+  int64_t s_cap;                     /* contiguous: padded length; lengths are clamped to it
+                                        (ifa_decode_check_inputs reports lengths outside it) */
   double scale_value;                /* usually 1/sqrt(d) */
   int32_t q_dtype;                   /* IFA_F32 / IFA_F16 / IFA_BF16 */
   int32_t kv_dtype;                  /* == q_dtype, or IFA_I8 */
@@ -288,6 +290,23 @@ ifa_status ifa_kv_cache_write(const void* src, const int64_t* slot_index, void* 
  * returns -1 for a NULL pointer, a negative batch or length, or a block_size
  * below 1. */
 int64_t ifa_paged_block_count(const int64_t* lengths, int64_t batch, int64_t block_size);
+
+/* Reports the arguments that ifa_decode would clamp rather than follow.  The
+ * decode clamps a length to [0, S] (S = s_cap, or max_blocks_per_seq *
+ * block_size for the paged layouts) and a block id to [0, num_blocks), so a
+ * corrupt argument never takes it outside its buffers but silently changes
+ * the result.  This call queues, on `stream`, one small kernel that reads the
+ * lengths and every block-table entry the decode would read (entries
+ * 0 .. ceil(clamped length / block_size) - 1 of each row) and writes to
+ * `flags` (one device int32, overwritten) the OR of
+ *   IFA_CHECK_BAD_LENGTH (1): a length outside [0, S];
+ *   IFA_CHECK_BAD_BLOCK  (2): a block-table entry outside [0, num_blocks).
+ * 0 means the call's lengths and table are in range.  The other arguments
+ * are validated as by ifa_decode_workspace_size; no workspace is needed.
+ * Asynchronous: read `flags` after the stream's work has finished. */
+#define IFA_CHECK_BAD_LENGTH 1
+#define IFA_CHECK_BAD_BLOCK 2
+ifa_status ifa_decode_check_inputs(const ifa_decode_args* args, int32_t* flags, hipStream_t stream);
 
 /* Measurement helper: the HBM read rate of this device, for setting the
  * decode's achieved bandwidth against a ceiling measured in the same run.

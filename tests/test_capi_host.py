@@ -338,3 +338,12 @@ def test_per_token_antiquant_modes_on_the_host():
         assert st == ifa.IFA_ERR_PARAM_INVALID and "128" in ifa.last_error()
     assert ws_size(base_args(antiquant_mode=4, **i8))[0] == ifa.IFA_ERR_PARAM_INVALID
     assert ws_size(base_args(antiquant_mode=ifa.IFA_ANTIQUANT_PER_TOKEN))[0] == ifa.IFA_ERR_PARAM_INVALID
+
+
+def test_check_inputs_argument_errors_on_the_host():
+    """ifa_decode_check_inputs validates like the workspace query and needs a
+    flags pointer; nothing is queued on an error."""
+    assert lib().ifa_decode_check_inputs(ctypes.byref(base_args()), None, None) == ifa.IFA_ERR_PARAM_NULLPTR
+    assert lib().ifa_decode_check_inputs(ctypes.byref(base_args(num_heads=0)), FAKE, None) == ifa.IFA_ERR_PARAM_INVALID
+    assert lib().ifa_decode_check_inputs(ctypes.byref(base_args(block_table=0)), FAKE, None) == \
+        ifa.IFA_ERR_PARAM_NULLPTR

@@ -485,3 +485,46 @@ def test_full_size_token_major_pool_sampled_rows():
     rows = whole_sequence_rows(w, 33)
     ref_out, ref_lse = oracle.decode_workload(w, rows=rows)
     _compare(w, out, lse, ref_out, ref_lse, rows=rows)
+
+
+def test_check_inputs_reports_out_of_range_arguments():
+    """ifa_decode_check_inputs: 0 for in-range lengths and tables (unused
+    entries hold -1 and are not read); the bad-block bit for a used entry
+    outside the pool; the bad-length bit for a length above the capacity or
+    below 0; contiguous layouts check lengths against s_cap."""
+    w = make_workload(batch=3, n_q=8, n_kv=2, qk_dim=128, kv_dtype="bf16", layout="paged", block_size=32,
+                      lengths=[100, 40, 7], max_blocks_per_seq=5, seed=60)
+    wg = w.to("cuda")
+    _announce("input check")
+
+    def flags(table=None, lens=None, layout_w=wg):
+        c = ifa.DecodeCall(layout_w.q, layout_w.k_cache, layout_w.v_cache,
+                           layout_w.block_table if table is None else table,
+                           layout_w.seq_lens if lens is None else lens, w.n_q, w.n_kv, w.scale,
+                           kv_layout=layout_w.layout)
+        f = c.check_inputs()
+        torch.cuda.synchronize()
+        return int(f.item())
+
+    assert flags() == 0
+    bad = wg.block_table.clone()
+    bad[1, 1] = 10_000  # sequence 1 reads blocks 0 and 1
+    assert flags(table=bad) == ifa.IFA_CHECK_BAD_BLOCK
+    bad = wg.block_table.clone()
+    bad[0, 3] = -7
+    assert flags(table=bad) == ifa.IFA_CHECK_BAD_BLOCK
+    bad = wg.block_table.clone()
+    bad[2, 4] = 10_000  # beyond sequence 2's one block: never read
+    assert flags(table=bad) == 0
+    lens = wg.seq_lens.clone()
+    lens[2] = -1
+    assert flags(lens=lens) == ifa.IFA_CHECK_BAD_LENGTH
+    lens = wg.seq_lens.clone()
+    lens[1] = 161  # capacity 5 x 32 = 160; the clamped length reads all five entries, three of them -1
+    assert flags(lens=lens) == ifa.IFA_CHECK_BAD_LENGTH | ifa.IFA_CHECK_BAD_BLOCK
+    c = make_workload(batch=2, n_q=8, n_kv=2, qk_dim=128, kv_dtype="bf16", layout="bnsd", lengths=[10, 64],
+                      s_cap=64, seed=61).to("cuda")
+    assert flags(layout_w=c) == 0
+    lens = c.seq_lens.clone()
+    lens[0] = 65
+    assert flags(lens=lens, layout_w=c) == ifa.IFA_CHECK_BAD_LENGTH
