@@ -312,13 +312,14 @@ class DecodeCall:
 
     def partial_slots(self):
         """Views of the workspace after ``splitkv()`` with the balanced split:
-        (attn_out (n + B, N_q, v_dim), softmax_max (n + B, N_q), softmax_sum
-        (n + B, N_q), (first slot, slot count) int32 (B, 2)); run r's piece of
-        sequence b is slot r + b."""
+        (attn_out (n + B, S_q * N_q, v_dim), softmax_max (n + B, S_q * N_q),
+        softmax_sum (n + B, S_q * N_q), (first slot, slot count) int32 (B, 2));
+        run r's piece of sequence b is slot r + b, and query token t of head h
+        is row t * N_q + h of a slot."""
         if not self.balanced:
             raise ValueError("this call splits per sequence: read its partials with partials()")
         a = self.args
-        B, nq, dv = a.batch, a.num_heads, a.v_dim
+        B, nq, dv = a.batch, self.q_seq * a.num_heads, a.v_dim
         slots = self.num_splits + B
         f = self.workspace.view(torch.float32)
         rows = slots * nq

@@ -90,6 +90,35 @@ int auto_splits_mfma(const ifa_decode_args* a, int64_t n_kv, int rows_kv, int64_
   return (int)n;
 }
 
+// Balanced split of the GQA MFMA kernel: runs of the batch's 32-token tiles,
+// the same runs for every KV head, one one-wave workgroup per (run, KV head,
+// group of query rows): about 2048 workgroups in all, as the per-sequence
+// split, and at least 4 kGqaPieceCost units per run at the longest lengths
+// (on the padded fp16 decode of 16 sequences of up to 4096 tokens, 68 runs
+// measured as fast as the per-sequence split, 136 and 256 runs 5-10% slower).
+// The per-sequence split sizes its splits by each sequence's length, so with
+// mixed lengths the longest splits (and the tail of the kernel) are about
+// twice the mean; equal runs finish together.
+int balanced_runs_gqa(const ifa_decode_args* a, int64_t n_kv, int rows_kv, int64_t max_len) {
+  const int64_t per_run = n_kv * ((rows_kv + (rows_kv <= 16 ? 15 : 31)) / (rows_kv <= 16 ? 16 : 32));
+  int64_t r = (8LL * kTargetCUs + per_run - 1) / per_run;
+  const int64_t units = a->batch * ((max_len + 31) / 32 + ifa::kGqaPieceCost);
+  const int64_t by_len = (units + 4 * ifa::kGqaPieceCost - 1) / (4 * ifa::kGqaPieceCost);
+  if (r > by_len) r = by_len;
+  return (int)(r < 1 ? 1 : (r > kMaxSplits ? kMaxSplits : r));
+}
+
+// The automatic choice of the GQA MFMA kernel when the batch allows it (the
+// plan region holds one (first slot, count) pair per sequence, batch <= 256)
+// and the batch's cost units stay in 32 bits.  int8 K/V with more than 16
+// query rows per KV head (32-column MFMAs) keeps the per-sequence split: its
+// balanced kernel would not fit two waves per SIMD.
+bool use_balanced_gqa(const ifa_decode_args* a, int rows_kv, int64_t max_len) {
+  if (a->num_splits != 0 || a->batch > ifa::kLongestFirstMaxBatch) return false;
+  if (a->kv_dtype == IFA_I8 && rows_kv > 16) return false;
+  return a->batch * ((max_len + 31) / 32 + ifa::kGqaPieceCost) < (int64_t)1 << 31;
+}
+
 // Fewest splits for which one split of the longest sequence touches at most
 // kMlaMaxTableSlice block-table entries (paged layout).
 bool is_paged(int layout) { return layout == IFA_KV_PAGED || layout == IFA_KV_PAGED_BSH; }
@@ -260,7 +289,9 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
     p.mfma = ifa::gqa_mfma_supported(a->q_dtype, a->kv_dtype, (int)a->qk_dim);
     if (p.mfma) {
       p.heads_per_wg = 32;
-      p.n_split = a->num_splits ? a->num_splits : auto_splits_mfma(a, n_kv, rows_kv, max_len);
+      p.balanced = use_balanced_gqa(a, rows_kv, max_len);
+      p.n_split = p.balanced ? balanced_runs_gqa(a, n_kv, rows_kv, max_len)
+                             : (a->num_splits ? a->num_splits : auto_splits_mfma(a, n_kv, rows_kv, max_len));
     } else {
       p.n_split = a->num_splits ? a->num_splits : auto_splits_gqa(a, n_kv, rows_kv, gh, max_len);
     }
@@ -273,9 +304,9 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
                   "the MLA shape needs num_splits >= %lld so that a split spans at most %d cache blocks",
                   (long long)min_splits_mla(a, max_len), ifa::kMlaMaxTableSlice - 2);
   }
-  // partial rows: (sequence, query token, head, split), or (slot, head) with
-  // runs + batch slots in the balanced split
-  const size_t rows = p.balanced ? ((size_t)p.n_split + (size_t)a->batch) * (size_t)a->num_heads
+  // partial rows: (sequence, query token, head, split), or (slot, query
+  // token, head) with runs + batch slots in the balanced split
+  const size_t rows = p.balanced ? ((size_t)p.n_split + (size_t)a->batch) * (size_t)q_seq * (size_t)a->num_heads
                                  : (size_t)a->batch * (size_t)q_seq * (size_t)a->num_heads * (size_t)p.n_split;
   p.off_o = 0;
   p.off_m = align256(rows * (size_t)a->v_dim * sizeof(float));
@@ -367,6 +398,8 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
     if (L.paged) ifa::make_divisor((uint32_t)a->block_size, &L.bs_magic, &L.bs_shift);
     L.plan = plan;
     L.longest_first = longest_first;
+    L.balanced = p.balanced;
+    L.seg_desc = p.balanced ? reinterpret_cast<int2*>(w + p.off_plan) : nullptr;
     L.q_dtype = a->q_dtype;
     L.kv_dtype = a->kv_dtype;
     L.head_dim = (int)a->qk_dim;

@@ -93,15 +93,19 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
   const float *m, *l;
   int ostep, mstep, nload, nvalid = 0;
   if (a.seg_desc) {
-    const int2 d = a.seg_desc[b / a.q_seq];
+    // slot s holds rows (query token, head): row qi n_q + h of q_seq n_q
+    const int seq = b / a.q_seq, qi = b - seq * a.q_seq;
+    const int2 d = a.seg_desc[seq];
     const int slots = a.n_split + a.batch / a.q_seq;
     int s0 = 0;
     if (L > 0 && d.x >= 0 && d.x < slots) s0 = d.x, nvalid = min(d.y, min(slots - d.x, kMaxSplitsPerRow));
     nvalid = max(nvalid, 0);
-    o = reinterpret_cast<const float4*>(a.ws_o + ((int64_t)s0 * a.n_q + h) * VD);
-    m = a.ws_m + (int64_t)s0 * a.n_q + h;
-    l = a.ws_l + (int64_t)s0 * a.n_q + h;
-    ostep = a.n_q * kQuads, mstep = a.n_q, nload = nvalid;
+    const int per_slot = a.q_seq * a.n_q;
+    const int64_t first = (int64_t)s0 * per_slot + (int64_t)qi * a.n_q + h;
+    o = reinterpret_cast<const float4*>(a.ws_o + first * VD);
+    m = a.ws_m + first;
+    l = a.ws_l + first;
+    ostep = per_slot * kQuads, mstep = per_slot, nload = nvalid;
   } else {
     o = reinterpret_cast<const float4*>(a.ws_o + (int64_t)row * a.n_split * VD);
     m = a.ws_m + (int64_t)row * a.n_split;

@@ -8,8 +8,11 @@
 // v_mfma_f32_32x32x16_{bf16,f16} and writes the split partial triples
 // (aclnnRingAttentionUpdate, "功能说明") that the combine kernel merges.
 //
-// Work decomposition.  One workgroup = one wave = one (sequence, KV head,
-// group of up to 32 rows, split); rows are query token major.  The split's
+// Work decomposition.  One workgroup = one wave = one (KV head, group of up
+// to 32 rows) over either one split of one sequence, or, in the balanced
+// split, one run of the batch's tiles (equal runs of the tiles of all
+// sequences in turn; a run takes one piece of each sequence it touches and
+// writes a partial per piece).  Rows are query token major.  A piece's
 // tokens stream in tiles of 32 through a private LDS ring of 2 slots,
 // each slot the tile's K rows then its V rows (8 KB each for 16-bit K/V, 4 KB
 // for int8), loaded straight from HBM with global_load_lds_dwordx4.  Per tile:
@@ -50,6 +53,7 @@ constexpr int kTile = 32;                // tokens per tile
 constexpr int kRowB16 = kD * 2;          // bytes of a 16-bit row (and of the int8 V tile's fp16 copy)
 constexpr float kRescale = 8.f;
 constexpr float kMrefInit = -1e30f;
+constexpr int kBalChunks = kLongestFirstMaxBatch / 64;  // sequences per lane in the balanced split
 
 template <int KV, bool TOK>
 struct SpecShape {
@@ -217,7 +221,9 @@ __device__ __forceinline__ u32x2 widen_i8(uint32_t w) {
   return u32x2{__builtin_amdgcn_perm(0x64646464u, b, 0x04010400u), __builtin_amdgcn_perm(0x64646464u, b, 0x04030402u)};
 }
 
-template <int QT, int KV, bool PAGED, bool TOK, int NC>
+// BAL: the balanced split (a.balanced), a kernel of its own so that the
+// per-sequence kernel stays a single piece
+template <int QT, int KV, bool PAGED, bool TOK, int NC, bool BAL>
 __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int work_items) {
   using S = SpecShape<KV, TOK>;
   constexpr int RB = S::RB, CPR = S::CPR, TB = S::TB, LT = S::LT, SLOT = S::SLOT, MK = S::MK;
@@ -236,456 +242,574 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
   __shared__ __attribute__((aligned(16))) char ring[S::SMEM];
 
   const int lane = threadIdx.x;
-  const int kg = lane / NC;  // which group of 8 k-slots of an MFMA this lane feeds
-  const int col = lane % NC;
 
-  // ---- work item: (row group, split, KV head, sequence rank) ----
+  // ---- work item: (row group, split or run, KV head[, sequence rank]) ----
   const int HG = (a.rows_kv + NC - 1) / NC;
   int rem = blockIdx.x;
   if (rem >= work_items) return;
   const int hg = rem % HG;
   rem /= HG;
-  const int split = rem % a.n_split;
+  const int split = rem % a.n_split;  // the run, in the balanced split
   rem /= a.n_split;
   const int g = rem % a.n_kv;
   rem /= a.n_kv;
-  int b = rem, L;
-  if (a.longest_first) {  // the keys use the ring, which no load has reached yet
-    const BatchPick pick = batch_of_rank(rem, a.seq_lens, a.batch, a.s_cap, reinterpret_cast<uint32_t*>(ring));
-    b = pick.b;
-    L = pick.len;
-  } else {
-    const int64_t L64 = a.seq_lens[b];
-    L = (int)(L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64));
-  }
-  const int per = (int)split_chunk(L, a.n_split);
-  const int start = split * per;
-  const int end = min(L, start + per);
-  if (start >= end) return;  // empty split: nothing is written for it
-  const int ntiles = (end - start + kTile - 1) / kTile;
 
-  // ---- this lane's row (the MFMA column it holds), its mask over the drafts ----
-  const int rr = hg * NC + col;  // row of the KV head's q_seq * group rows
-  const bool row_ok = rr < a.rows_kv;
-  const int qi = row_ok ? rr / a.group : 0;
-  const int64_t qrow = ((int64_t)b * a.q_seq + qi) * a.n_q + g * a.group + (row_ok ? rr - qi * a.group : 0);
-  const int draft0 = L - a.q_seq;  // position of draft token 0
-  uint32_t vis = ~0u;              // bit k: the row attends to draft token k
-  if (a.mask_mode == 3) {
-    vis = (2u << qi) - 1u;
-  } else if (a.mask_mode == 9) {
-    vis = 0;
-    const uint8_t* m = a.tree_mask + ((int64_t)b * a.q_seq + qi) * a.q_seq;
-    for (int k = 0; k < a.q_seq; ++k) vis |= (m[k] == 0 ? 1u : 0u) << k;
-  }
-
-  // ---- Q^T operand: channels KSTEP ks + 8 kg .. + 7 per k-step (zero for padding rows) ----
-  u32x4 qreg[NKS];
-  float kconst = 0.f;  // int8: sum_d q'_d (offset_d - 1152) over the row
-  float qsum = 0.f;    // per-token int8: sum_d q_d of the fp16 query
-  if constexpr (I8 && TOK) {
-    // q in fp16 as given (the K scale varies per token and multiplies the score)
-    float part = 0.f;
+  // The pieces (sequence, token range) this workgroup reduces.  Per-sequence
+  // split: one, split `split` of the sequence of rank `rem`.  Balanced split:
+  // run `split` of the batch's tiles, which may end one sequence, take short
+  // ones whole and start another: one piece per sequence it touches.
+  int b = 0, L = 0, start = 0, end = 0;
+  int64_t pbase = 0;  // partial of query token qi, head h: pbase + (qi n_q + h) pstride
+  int pstride = 1;
+  // balanced split: lane l holds, for sequence 64 k + l, the cost of the
+  // sequences up to it (inclusive prefix) and its clamped length; the run
+  // takes the cost units [tcur, trun_end) of ttotal
+  int incl[kBalChunks] = {}, lenv[kBalChunks] = {};
+  int nrun = 0, tcur = 0, trun_end = 0, ttotal = 0;
+  auto at = [&](const int (&v)[kBalChunks], int idx) -> int {  // entry of sequence idx (wave-uniform)
+    const int k = idx >> 6, l = idx & 63;
+    int x = __builtin_amdgcn_readlane(v[0], l);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t pair = 0;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int d = KSTEP * ks + 8 * kg + 2 * w + e;
-          const _Float16 qh = row_ok ? (_Float16)load_as_f32<QT>(a.q, qrow * kD + d) : (_Float16)0.f;
-          part += (float)qh;
-          pair |= (uint32_t)__builtin_bit_cast(uint16_t, qh) << (16 * e);
-        }
-        qreg[ks][w] = pair;
-      }
-    qsum = col_sum<NC>(part);
-  } else if constexpr (I8) {
-    // q' = q * scale_K rounded to fp16, and this lane's half of the constant
-    float part = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        uint32_t pair = 0;
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int d = KSTEP * ks + 8 * kg + 2 * w + e;
-          const int kq = g * a.aq_stride_g + d * a.aq_stride_d;  // K parameters (index 0)
-          const _Float16 qh = row_ok ? (_Float16)(load_as_f32<QT>(a.q, qrow * kD + d) * a.aq_scale[kq]) : (_Float16)0.f;
-          part = fmaf((float)qh, a.aq_offset[kq] - 1152.f, part);
-          pair |= (uint32_t)__builtin_bit_cast(uint16_t, qh) << (16 * e);
-        }
-        qreg[ks][w] = pair;
-      }
-    kconst = col_sum<NC>(part);  // the lanes of one column hold its channels between them
-  } else if ((reinterpret_cast<uintptr_t>(a.q) & 15) == 0) {  // 16-byte loads
-    const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + qrow * RB) + kg;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) qreg[ks] = row_ok ? qp[KSTEP / 8 * ks] : u32x4{0u, 0u, 0u, 0u};
-  } else {  // a query buffer aligned to its element only
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.q) + qrow * RB) + 8 * kg;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        qreg[ks][w] =
-            row_ok ? (uint32_t)qp[KSTEP * ks + 2 * w] | ((uint32_t)qp[KSTEP * ks + 2 * w + 1] << 16) : 0u;
-  }
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) settle(qreg[ks]);
-  settle(kconst);
-  settle(qsum);
-
-  // per-token antiquant: rows of this sequence (and KV head) in the K scale,
-  // K offset, V scale and V offset arrays
-  const float* tokp[4] = {nullptr, nullptr, nullptr, nullptr};
-  if constexpr (TOK) {
-    const int64_t base = (int64_t)b * a.aq_tok_stride_b + (int64_t)g * a.aq_tok_stride_g;
-    tokp[0] = a.aq_scale + base;
-    tokp[1] = a.aq_offset + base;
-    tokp[2] = a.aq_scale + a.aq_tok_stride_kv + base;
-    tokp[3] = a.aq_offset + a.aq_tok_stride_kv + base;
-  }
-
-  // ---- block-table slice of the split: lane k holds its k-th block id ----
-  const uint32_t bi_first = PAGED ? fast_div((uint32_t)start, a.bs_magic, a.bs_shift) : 0;
-  int tbl = 0;
-  if constexpr (PAGED) {
-    const int nblk = (int)fast_div((uint32_t)(end - 1), a.bs_magic, a.bs_shift) - (int)bi_first + 1;
-    tbl = lanes_from_scalar_loads(a.block_table + (int64_t)b * a.max_blocks + bi_first, nblk < 64 ? nblk : 64, 0);
-  }
-  auto block_id = [&](uint32_t bi) -> uint32_t {  // wave-uniform
-    const uint32_t k = bi - bi_first;
-    int v = k < 64 ? __builtin_amdgcn_readlane(tbl, k) : ld_uniform(a.block_table, (int64_t)b * a.max_blocks + bi);
-    return (uint32_t)(v < 0 ? 0 : (v >= a.num_blocks ? a.num_blocks - 1 : v));
+    for (int c = 1; c < kBalChunks; ++c) x = k == c ? __builtin_amdgcn_readlane(v[c], l) : x;
+    return x;
   };
-
-  const char* kbase = static_cast<const char*>(a.k);
-  const char* vbase = static_cast<const char*>(a.v);
-  const uint32_t ring_lds = lds_addr(ring);
-
-  // Queue tile j into ring slot `slot`: LDS chunk position P of the K (or V)
-  // tile holds row t = P / CPR, chunk (P % CPR) ^ swz16(t) (int8: swz(t)) of token tstart + t
-  // (rows past the split's end repeat its last row).  A tile's 32 tokens lie
-  // in at most 3 cache blocks.
-  auto queue_tile = [&](int j, int slot) {
-    const int tstart = start + kTile * j;
-    uint32_t tok0 = 0, adj0 = 0, adj1 = 0, adj2 = 0;
-    if constexpr (PAGED) {
-      const uint32_t bi0 = fast_div((uint32_t)tstart, a.bs_magic, a.bs_shift);
-      const uint32_t bil = fast_div((uint32_t)(end - 1), a.bs_magic, a.bs_shift);
-      tok0 = bi0 * (uint32_t)a.block_size;
-      adj0 = block_id(bi0);
-      adj1 = block_id(bi0 + 1 <= bil ? bi0 + 1 : bil);
-      adj2 = block_id(bi0 + 2 <= bil ? bi0 + 2 : bil);
-    }
-    const uint32_t dst = ring_lds + slot * SLOT;
-#pragma unroll
-    for (int i = 0; i < LT; ++i) {
-      const int P = 64 * i + lane;
-      const int t = P / CPR;
-      const int c = (P % CPR) ^ (I8 ? swz(t) : swz16(t));
-      const uint32_t tok = (uint32_t)min(tstart + t, end - 1);
-      uint64_t row;
-      if constexpr (PAGED) {
-        const uint32_t bs = (uint32_t)a.block_size;
-        const uint32_t u = tok - tok0;
-        const uint32_t blk = u >= 2 * bs ? adj2 : (u >= bs ? adj1 : adj0);
-        const uint32_t slot_in = u - (u >= 2 * bs ? 2 * bs : (u >= bs ? bs : 0));
-        row = a.token_major ? ((uint64_t)blk * bs + slot_in) * (uint32_t)a.n_kv + (uint32_t)g
-                            : ((uint64_t)blk * (uint32_t)a.n_kv + (uint32_t)g) * bs + slot_in;
-      } else {
-        row = a.token_major ? ((uint64_t)b * (uint64_t)a.s_cap + tok) * (uint32_t)a.n_kv + (uint32_t)g
-                            : ((uint64_t)b * (uint32_t)a.n_kv + (uint32_t)g) * (uint64_t)a.s_cap + tok;
-      }
-      const uint64_t off = row * RB + 16u * (uint32_t)c;
-      dma16_lane(kbase + off, dst + 1024 * i);
-      dma16_lane(vbase + off, dst + TB + 1024 * i);
-    }
-    if constexpr (TOK) {
-      // parameter array 2 k + (lane / 32), token tstart + lane % 32 (clamped
-      // to the split's last token), to slot byte 2 TB + 128 (2 k + lane / 32)
-      const int tok = min(tstart + (lane & 31), end - 1);
-#pragma unroll
-      for (int k = 0; k < 2; ++k) dma4_lane((lane >> 5 ? tokp[2 * k + 1] : tokp[2 * k]) + tok, dst + 2 * TB + 256 * k);
-    }
-  };
-
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (s < ntiles) queue_tile(s, s);
-
-  // ---- per-lane LDS offsets within a slot ----
-  // S^T A operand of S^T tile m: token t = NC m + col, channels KSTEP ks + 8 kg
-  // .. + 7: 16-byte chunk KSTEP ks / 8 + kg of a 16-bit row, or 8 bytes of an
-  // int8 row (chunk (KSTEP ks + 8 kg) / 16, half ((KSTEP ks + 8 kg) / 8) % 2)
-  uint32_t offS[NSA][NKS];
-#pragma unroll
-  for (int m = 0; m < NSA; ++m)
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int t = NC * m + col;
-      const int c8 = (KSTEP * ks + 8 * kg) / 8;  // 8-channel group of the row
-      offS[m][ks] = I8 ? t * RB + 16 * ((c8 >> 1) ^ swz(t)) + 8 * (c8 & 1) : t * RB + 16 * (c8 ^ swz16(t));
-    }
-  // V^T A operand (transposing read) on 16-bit rows (the int8 V tile's fp16
-  // copy).  In 16-lane group gq, source lane s = 4 r + q reads 4 channels of
-  // one row, the group a 4-row x 16-channel block, and the read hands lane i
-  // of the group the 4 tokens of channel i of the block.
-  //   32 columns: row 8 rd + 4 (gq / 2) + r, chunk 8 hi + 4 (tile & 1) + 2
-  //     (gq & 1) + q / 2 with hi = tile / 2, for the k-slots 4 h + 0..3 (rd 0)
-  //     and 8 + 4 h + 0..3 (rd 1) of each 16-token k-step (k-step 1: rows
-  //     16 further, an immediate, as the swizzle repeats every 16 rows);
-  //   16 columns: row 16 rd + 4 gq + r, chunk 8 hi + 2 (tile & 3) + q / 2
-  //     with hi = tile / 4, for the k-slots 0..3 (tokens 4 kg + 0..3) and
-  //     4..7 (tokens 16 + 4 kg + 0..3) of the single 32-token k-step.
-  // Offsets [hi][tile part][rd]; half q % 2.
-  uint32_t offV[2][4][2];
-  {
-    const int s = lane & 15, gq = lane >> 4;
-    const int r = s >> 2, q = s & 3;
-#pragma unroll
-    for (int hi = 0; hi < 2; ++hi)
-#pragma unroll
-      for (int rd = 0; rd < 2; ++rd)
-#pragma unroll
-        for (int tp = 0; tp < 4; ++tp) {
-          const int t = NC == 32 ? 8 * rd + 4 * (gq >> 1) + r : 16 * rd + 4 * gq + r;
-          const int x = 8 * hi + (NC == 32 ? 4 * (tp & 1) + 2 * (gq & 1) + (q >> 1) : 2 * tp + (q >> 1));
-          offV[hi][tp][rd] = t * kRowB16 + 16 * (x ^ swz16(t)) + 8 * (q & 1);
-        }
-  }
-
-  float mref = kMrefInit, mtrue = kNegInf, lsum = 0.f, lsum_r = 0.f;
-  float vbias = 0.f;  // per-token int8: sum over tokens of rounded weight * (offset_V - 1152)
-  AccT acc[NOT];
-#pragma unroll
-  for (int mt = 0; mt < NOT; ++mt)
-#pragma unroll
-    for (int r = 0; r < AW; ++r) acc[mt][r] = 0.f;
-
-  for (int i = 0; i < ntiles; ++i) {
-    // tile i has landed once only the loads of the tiles queued after it
-    // (at most kStages - 2) remain (vmcnt retires in order)
-    const int after = min(kStages - 2, ntiles - 1 - i);
-    if constexpr (kStages == 3) {
-      if (after >= 1) wait_vmem<2 * LT>();
-      else wait_vmem<0>();
+  if constexpr (!BAL) {
+    b = rem;
+    if (a.longest_first) {  // the keys use the ring, which no load has reached yet
+      const BatchPick pick = batch_of_rank(rem, a.seq_lens, a.batch, a.s_cap, reinterpret_cast<uint32_t*>(ring));
+      b = pick.b;
+      L = pick.len;
     } else {
-      wait_vmem<0>();
+      const int64_t L64 = a.seq_lens[b];
+      L = (int)(L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64));
     }
-    // tile i + kStages - 1 goes into the slot of tile i - 1, whose operands
-    // this wave read during the last iteration, before their MFMAs.  Queued
-    // after the wait: with two slots one tile is in flight while this one is
-    // computed, which measured faster than queueing it before the wait (two
-    // in flight) or a third slot.
-    if (i + kStages - 1 < ntiles) queue_tile(i + kStages - 1, (i + kStages - 1) % kStages);
-    const uint32_t slot = ring_lds + (i % kStages) * SLOT;
-    const int tstart = start + kTile * i;
+    const int per = (int)split_chunk(L, a.n_split);
+    start = split * per;
+    end = min(L, start + per);
+    if (start >= end) return;  // empty split: nothing is written for it
+    pbase = (int64_t)b * a.q_seq * a.n_q * a.n_split + split;
+    pstride = a.n_split;
+  } else {
+    // Cost of a sequence: its tiles plus kGqaPieceCost for the start of a
+    // piece on it; none for an empty one.
+    int carry = 0;
+#pragma unroll
+    for (int k = 0; k < kBalChunks; ++k) {
+      if (64 * k >= a.batch) {  // wave-uniform: no sequences in this chunk
+        incl[k] = carry;
+        continue;
+      }
+      const int bb = 64 * k + lane;
+      int Lb = 0;
+      if (bb < a.batch) {
+        const int64_t L64 = a.seq_lens[bb];
+        Lb = (int)(L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64));
+      }
+      int t = Lb > 0 ? (Lb + kTile - 1) / kTile + kGqaPieceCost : 0;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(t, d);
+        if (lane >= d) t += y;
+      }
+      incl[k] = carry + t;
+      lenv[k] = Lb;
+      carry += __shfl(t, 63);
+    }
+    ttotal = carry;
+    // runs: min(n_split, total cost) of them, so that none is empty; run r
+    // covers cost units [r V / R, (r + 1) V / R) (floors)
+    nrun = min(a.n_split, ttotal);
+    if (split >= nrun) return;
+    tcur = (int)((int64_t)split * ttotal / nrun);
+    trun_end = (int)((int64_t)(split + 1) * ttotal / nrun);
+    // the sequence holding unit tcur: as many as have a prefix <= tcur precede it
+    int before = 0;
+#pragma unroll
+    for (int k = 0; k < kBalChunks; ++k)
+      before += __builtin_popcountll(__builtin_amdgcn_ballot_w64(64 * k + lane < a.batch && incl[k] <= tcur));
+    b = before;
+  }
 
-    // ---- S^T = K . Q^T ----
-    AccT sacc[NSA];
+  for (;;) {
+    if constexpr (BAL) {
+      // sequence b spans units [pb, pe): kGqaPieceCost for its start, then
+      // one per tile from z on.  The run's units hold its tiles
+      // [max(tcur, z), min(trun_end, pe)) - z; none when the run ends inside
+      // the start units (the next run takes the sequence).
+      const int pb = b == 0 ? 0 : at(incl, b - 1);
+      const int pe = at(incl, b);
+      const int z = pb + kGqaPieceCost;
+      if (trun_end <= z) break;
+      const int first = max(tcur, z);
+      L = at(lenv, b);
+      start = (first - z) * kTile;
+      end = min(L, (min(trun_end, pe) - z) * kTile);
+      pbase = (int64_t)(split + b) * a.q_seq * a.n_q;
+      pstride = 1;
+      if (first == z && g == 0 && hg == 0 && lane == 0) {
+        // the runs that take sequence b are this one .. the one holding its last unit
+        const int rlast = (int)(((int64_t)pe * nrun - 1) / ttotal);
+        a.seg_desc[b] = make_int2(split + b, rlast - split + 1);
+      }
+    }
+    const int ntiles = (end - start + kTile - 1) / kTile;
+    // This lane, made opaque for each piece in the balanced split: what
+    // derives from it (LDS offsets, channels, rows) is then computed per piece
+    // instead of being hoisted out of the piece loop and held across it.
+    int lane_p = lane;
+    if constexpr (BAL) asm volatile("" : "+v"(lane_p));
+    const int kg = lane_p / NC;  // which group of 8 k-slots of an MFMA this lane feeds
+    const int col = lane_p % NC;
+    // The antiquant parameters, read afresh for each piece: hoisted out of
+    // the piece loop, the per-channel ones would hold 128 registers across it.
+    const float* aq_scale = a.aq_scale;
+    const float* aq_offset = a.aq_offset;
+    int aq_g = __builtin_amdgcn_readfirstlane(g * a.aq_stride_g);  // the KV head's parameters
+    if constexpr (BAL) asm volatile("" : "+s"(aq_scale), "+s"(aq_offset), "+s"(aq_g));
+
+    // ---- this lane's row (the MFMA column it holds), its mask over the drafts ----
+    const int rr = hg * NC + col;  // row of the KV head's q_seq * group rows
+    const bool row_ok = rr < a.rows_kv;
+    const int qi = row_ok ? rr / a.group : 0;
+    const int hrow = g * a.group + (row_ok ? rr - qi * a.group : 0);  // query head
+    const int64_t qrow = ((int64_t)b * a.q_seq + qi) * a.n_q + hrow;
+    const int64_t pidx = pbase + ((int64_t)qi * a.n_q + hrow) * pstride;  // this row's partial
+    const int draft0 = L - a.q_seq;  // position of draft token 0
+    uint32_t vis = ~0u;              // bit k: the row attends to draft token k
+    if (a.mask_mode == 3) {
+      vis = (2u << qi) - 1u;
+    } else if (a.mask_mode == 9) {
+      vis = 0;
+      const uint8_t* m = a.tree_mask + ((int64_t)b * a.q_seq + qi) * a.q_seq;
+      for (int k = 0; k < a.q_seq; ++k) vis |= (m[k] == 0 ? 1u : 0u) << k;
+    }
+
+    // ---- Q^T operand: channels KSTEP ks + 8 kg .. + 7 per k-step (zero for padding rows) ----
+    u32x4 qreg[NKS];
+    float kconst = 0.f;  // int8: sum_d q'_d (offset_d - 1152) over the row
+    float qsum = 0.f;    // per-token int8: sum_d q_d of the fp16 query
+    if constexpr (I8 && TOK) {
+      // q in fp16 as given (the K scale varies per token and multiplies the score)
+      float part = 0.f;
 #pragma unroll
-    for (int m = 0; m < NSA; ++m)
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int r = 0; r < AW; ++r) sacc[m][r] = 0.f;
-    u32x4 kb[NSA][NKS];
+        for (int w = 0; w < 4; ++w) {
+          uint32_t pair = 0;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int d = KSTEP * ks + 8 * kg + 2 * w + e;
+            const _Float16 qh = row_ok ? (_Float16)load_as_f32<QT>(a.q, qrow * kD + d) : (_Float16)0.f;
+            part += (float)qh;
+            pair |= (uint32_t)__builtin_bit_cast(uint16_t, qh) << (16 * e);
+          }
+          qreg[ks][w] = pair;
+        }
+      qsum = col_sum<NC>(part);
+    } else if constexpr (I8) {
+      // q' = q * scale_K rounded to fp16, and this lane's half of the constant
+      float part = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t pair = 0;
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int d = KSTEP * ks + 8 * kg + 2 * w + e;
+            const int kq = aq_g + d * a.aq_stride_d;  // K parameters (index 0)
+            const _Float16 qh = row_ok ? (_Float16)(load_as_f32<QT>(a.q, qrow * kD + d) * aq_scale[kq]) : (_Float16)0.f;
+            part = fmaf((float)qh, aq_offset[kq] - 1152.f, part);
+            pair |= (uint32_t)__builtin_bit_cast(uint16_t, qh) << (16 * e);
+          }
+          qreg[ks][w] = pair;
+        }
+      kconst = col_sum<NC>(part);  // the lanes of one column hold its channels between them
+    } else if ((reinterpret_cast<uintptr_t>(a.q) & 15) == 0) {  // 16-byte loads
+      const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + qrow * RB) + kg;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qreg[ks] = row_ok ? qp[KSTEP / 8 * ks] : u32x4{0u, 0u, 0u, 0u};
+    } else {  // a query buffer aligned to its element only
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.q) + qrow * RB) + 8 * kg;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          qreg[ks][w] =
+              row_ok ? (uint32_t)qp[KSTEP * ks + 2 * w] | ((uint32_t)qp[KSTEP * ks + 2 * w + 1] << 16) : 0u;
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) settle(qreg[ks]);
+    settle(kconst);
+    settle(qsum);
+
+    // per-token antiquant: rows of this sequence (and KV head) in the K scale,
+    // K offset, V scale and V offset arrays
+    const float* tokp[4] = {nullptr, nullptr, nullptr, nullptr};
+    if constexpr (TOK) {
+      const int64_t base = (int64_t)b * a.aq_tok_stride_b + (int64_t)g * a.aq_tok_stride_g;
+      tokp[0] = aq_scale + base;
+      tokp[1] = aq_offset + base;
+      tokp[2] = aq_scale + a.aq_tok_stride_kv + base;
+      tokp[3] = aq_offset + a.aq_tok_stride_kv + base;
+    }
+
+    // ---- block-table slice of the split: lane k holds its k-th block id ----
+    const uint32_t bi_first = PAGED ? fast_div((uint32_t)start, a.bs_magic, a.bs_shift) : 0;
+    int tbl = 0;
+    if constexpr (PAGED) {
+      const int nblk = (int)fast_div((uint32_t)(end - 1), a.bs_magic, a.bs_shift) - (int)bi_first + 1;
+      tbl = lanes_from_scalar_loads(a.block_table + (int64_t)b * a.max_blocks + bi_first, nblk < 64 ? nblk : 64, 0);
+    }
+    auto block_id = [&](uint32_t bi) -> uint32_t {  // wave-uniform
+      const uint32_t k = bi - bi_first;
+      int v = k < 64 ? __builtin_amdgcn_readlane(tbl, k) : ld_uniform(a.block_table, (int64_t)b * a.max_blocks + bi);
+      return (uint32_t)(v < 0 ? 0 : (v >= a.num_blocks ? a.num_blocks - 1 : v));
+    };
+
+    const char* kbase = static_cast<const char*>(a.k);
+    const char* vbase = static_cast<const char*>(a.v);
+    const uint32_t ring_lds = lds_addr(ring);
+
+    // Queue tile j into ring slot `slot`: LDS chunk position P of the K (or V)
+    // tile holds row t = P / CPR, chunk (P % CPR) ^ swz16(t) (int8: swz(t)) of token tstart + t
+    // (rows past the split's end repeat its last row).  A tile's 32 tokens lie
+    // in at most 3 cache blocks.
+    auto queue_tile = [&](int j, int slot) {
+      const int tstart = start + kTile * j;
+      uint32_t tok0 = 0, adj0 = 0, adj1 = 0, adj2 = 0;
+      if constexpr (PAGED) {
+        const uint32_t bi0 = fast_div((uint32_t)tstart, a.bs_magic, a.bs_shift);
+        const uint32_t bil = fast_div((uint32_t)(end - 1), a.bs_magic, a.bs_shift);
+        tok0 = bi0 * (uint32_t)a.block_size;
+        adj0 = block_id(bi0);
+        adj1 = block_id(bi0 + 1 <= bil ? bi0 + 1 : bil);
+        adj2 = block_id(bi0 + 2 <= bil ? bi0 + 2 : bil);
+      }
+      const uint32_t dst = ring_lds + slot * SLOT;
+#pragma unroll
+      for (int i = 0; i < LT; ++i) {
+        const int P = 64 * i + lane_p;
+        const int t = P / CPR;
+        const int c = (P % CPR) ^ (I8 ? swz(t) : swz16(t));
+        const uint32_t tok = (uint32_t)min(tstart + t, end - 1);
+        uint64_t row;
+        if constexpr (PAGED) {
+          const uint32_t bs = (uint32_t)a.block_size;
+          const uint32_t u = tok - tok0;
+          const uint32_t blk = u >= 2 * bs ? adj2 : (u >= bs ? adj1 : adj0);
+          const uint32_t slot_in = u - (u >= 2 * bs ? 2 * bs : (u >= bs ? bs : 0));
+          row = a.token_major ? ((uint64_t)blk * bs + slot_in) * (uint32_t)a.n_kv + (uint32_t)g
+                              : ((uint64_t)blk * (uint32_t)a.n_kv + (uint32_t)g) * bs + slot_in;
+        } else {
+          row = a.token_major ? ((uint64_t)b * (uint64_t)a.s_cap + tok) * (uint32_t)a.n_kv + (uint32_t)g
+                              : ((uint64_t)b * (uint32_t)a.n_kv + (uint32_t)g) * (uint64_t)a.s_cap + tok;
+        }
+        const uint64_t off = row * RB + 16u * (uint32_t)c;
+        dma16_lane(kbase + off, dst + 1024 * i);
+        dma16_lane(vbase + off, dst + TB + 1024 * i);
+      }
+      if constexpr (TOK) {
+        // parameter array 2 k + (lane / 32), token tstart + lane % 32 (clamped
+        // to the split's last token), to slot byte 2 TB + 128 (2 k + lane / 32)
+        const int tok = min(tstart + (lane_p & 31), end - 1);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) dma4_lane((lane_p >> 5 ? tokp[2 * k + 1] : tokp[2 * k]) + tok, dst + 2 * TB + 256 * k);
+      }
+    };
+
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+      if (s < ntiles) queue_tile(s, s);
+
+    // ---- per-lane LDS offsets within a slot ----
+    // S^T A operand of S^T tile m: token t = NC m + col, channels KSTEP ks + 8 kg
+    // .. + 7: 16-byte chunk KSTEP ks / 8 + kg of a 16-bit row, or 8 bytes of an
+    // int8 row (chunk (KSTEP ks + 8 kg) / 16, half ((KSTEP ks + 8 kg) / 8) % 2)
+    uint32_t offS[NSA][NKS];
 #pragma unroll
     for (int m = 0; m < NSA; ++m)
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        if constexpr (I8) {
-          const u32x2 x = lds_read_b64(slot + offS[m][ks]);
-          const u32x2 w0 = widen_i8(x[0]), w1 = widen_i8(x[1]);
-          kb[m][ks] = u32x4{w0[0], w0[1], w1[0], w1[1]};
-        } else {
-          kb[m][ks] = lds_read_b128(slot + offS[m][ks]);
-        }
+        const int t = NC * m + col;
+        const int c8 = (KSTEP * ks + 8 * kg) / 8;  // 8-channel group of the row
+        offS[m][ks] = I8 ? t * RB + 16 * ((c8 >> 1) ^ swz(t)) + 8 * (c8 & 1) : t * RB + 16 * (c8 ^ swz16(t));
       }
+    // V^T A operand (transposing read) on 16-bit rows (the int8 V tile's fp16
+    // copy).  In 16-lane group gq, source lane s = 4 r + q reads 4 channels of
+    // one row, the group a 4-row x 16-channel block, and the read hands lane i
+    // of the group the 4 tokens of channel i of the block.
+    //   32 columns: row 8 rd + 4 (gq / 2) + r, chunk 8 hi + 4 (tile & 1) + 2
+    //     (gq & 1) + q / 2 with hi = tile / 2, for the k-slots 4 h + 0..3 (rd 0)
+    //     and 8 + 4 h + 0..3 (rd 1) of each 16-token k-step (k-step 1: rows
+    //     16 further, an immediate, as the swizzle repeats every 16 rows);
+    //   16 columns: row 16 rd + 4 gq + r, chunk 8 hi + 2 (tile & 3) + q / 2
+    //     with hi = tile / 4, for the k-slots 0..3 (tokens 4 kg + 0..3) and
+    //     4..7 (tokens 16 + 4 kg + 0..3) of the single 32-token k-step.
+    // Offsets [hi][tile part][rd]; half q % 2.
+    uint32_t offV[2][4][2];
+    {
+      const int s = lane_p & 15, gq = lane_p >> 4;
+      const int r = s >> 2, q = s & 3;
 #pragma unroll
-    for (int m = 0; m < NSA; ++m)
+      for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) sacc[m] = mfma_nc<NC, MK>(kb[m][ks], qreg[ks], sacc[m]);
-
-    // int8: widen this V tile into an fp16 copy in 16-bit row layout, written
-    // over the whole slot (K and V, 2 x 4 KB), whose K operands are in
-    // registers by now.  All int8 chunks are read before any write (a wave's
-    // LDS operations complete in order).  Lane takes positions P = lane + 64 k
-    // of the int8 V tile: row t = P / 8, chunk c = (P % 8) ^ swz(t) = channels
-    // 16 c .. 16 c + 15, which become fp16 chunks 2 c and 2 c + 1 of row t.
-    if constexpr (I8) {
-      u32x4 x[TB / 1024];
+        for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
-      for (int k = 0; k < TB / 1024; ++k) x[k] = lds_read_b128(slot + TB + 16 * (lane + 64 * k));
-#pragma unroll
-      for (int k = 0; k < TB / 1024; ++k) {
-        const int P = lane + 64 * k;
-        const int t = P >> 3;
-        const int c = (P & 7) ^ swz(t);
-        const u32x2 w0 = widen_i8(x[k][0]), w1 = widen_i8(x[k][1]), w2 = widen_i8(x[k][2]), w3 = widen_i8(x[k][3]);
-        const u32x4 lo = {w0[0], w0[1], w1[0], w1[1]}, hi = {w2[0], w2[1], w3[0], w3[1]};
-        lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c) ^ swz16(t)), lo);
-        lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c + 1) ^ swz16(t)), hi);
-      }
-      // the reads below see this wave's writes
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
+          for (int tp = 0; tp < 4; ++tp) {
+            const int t = NC == 32 ? 8 * rd + 4 * (gq >> 1) + r : 16 * rd + 4 * gq + r;
+            const int x = 8 * hi + (NC == 32 ? 4 * (tp & 1) + 2 * (gq & 1) + (q >> 1) : 2 * tp + (q >> 1));
+            offV[hi][tp][rd] = t * kRowB16 + 16 * (x ^ swz16(t)) + 8 * (q & 1);
+          }
     }
 
-    // ---- online softmax over this lane's row (column) ----
-    // score register r (accumulator register r % AW of S^T tile r / AW) holds
-    // token TS (r / 4) + 4 kg + r % 4 of the tile
-    float sv[NSV];
-    if constexpr (TOK) {
-      // score of token t: scale_K[t] (q . (1152 + x_t) + (offset_K[t] - 1152) sum q); this lane's
-      // tokens TS q4 + 4 kg + e lie in 16-byte groups of each parameter array
-      const uint32_t pa = slot + 2 * TB + 16 * kg;
-#pragma unroll
-      for (int q4 = 0; q4 < NSV / 4; ++q4) {
-        const f32x4_t sk = lds_read_f32x4(pa + 4 * TS * q4), ok = lds_read_f32x4(pa + 128 + 4 * TS * q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * q4 + e;
-          sv[r] = sk[e] * fmaf(ok[e] - 1152.f, qsum, sacc[r / AW][r % AW]) * a.scale_log2;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < NSV; ++r) sv[r] = (sacc[r / AW][r % AW] + kconst) * a.scale_log2;
-    }
-    if (tstart + kTile > end || tstart + kTile > draft0) {  // the split's tail, or draft tokens
-#pragma unroll
-      for (int r = 0; r < NSV; ++r) {
-        const int tok = tstart + TS * (r >> 2) + 4 * kg + (r & 3);
-        const uint32_t k = (uint32_t)(tok - draft0);  // draft index; huge for tokens before the drafts
-        const uint32_t kept = k < 32u ? (vis >> k) & 1u : 1u;
-        const uint32_t keep = (uint32_t)(tok < end) & kept;
-        sv[r] = keep ? sv[r] : kNegInf;  // a select, not a branch
-      }
-    }
-    float smax = kNegInf;
-#pragma unroll
-    for (int r = 0; r < NSV; ++r) smax = fmaxf(smax, sv[r]);
-    smax = col_max<NC>(smax);  // the column's other tokens sit in the lanes l ^ 16 / 32 / 48
-    mtrue = fmaxf(mtrue, smax);
-    if (__builtin_amdgcn_ballot_w64(smax > mref + kRescale)) {
-      const float mnew = smax > mref + kRescale ? smax : mref;
-      const float alpha = fast_exp2(mref - mnew);  // 0 on the first scores
-      lsum *= alpha;
-      lsum_r *= alpha;
-      vbias *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < NOT; ++mt) scale_acc(acc[mt], alpha);
-      mref = mnew;
-    }
-    // P^T operand: k-slot j of lane group kg in 16-token k-step kk is score
-    // register 8 kk + j (32 columns), or, in the one 32-token k-step, score
-    // register j (16 columns), rounded to the MFMA operand type
-    u32x4 pb[NSV / 8];
-    float pr[NSV];
-    float pscale[NSV], pbias[NSV];  // per-token int8: V scale and offset - 1152 of each token
-    if constexpr (TOK) {
-      const uint32_t pa = slot + 2 * TB + 256 + 16 * kg;
-#pragma unroll
-      for (int q4 = 0; q4 < NSV / 4; ++q4) {
-        const f32x4_t sv4 = lds_read_f32x4(pa + 4 * TS * q4), ov4 = lds_read_f32x4(pa + 128 + 4 * TS * q4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pscale[4 * q4 + e] = sv4[e], pbias[4 * q4 + e] = ov4[e] - 1152.f;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < NSV; ++r) {
-      const float pf = fast_exp2(sv[r] - mref);  // <= 2^8; 0 for removed tokens
-      lsum += pf;
-      // per-token int8: the weight that multiplies the widened V row is
-      // p * scale_V[t]; its rounded value also removes the 1152 bias and adds
-      // the V offset through vbias
-      const uint16_t bits = round16<MK>(TOK ? pf * pscale[r] : pf);
-      pr[r] = MK == kBF16 ? (float)__builtin_bit_cast(__bf16, bits) : (float)__builtin_bit_cast(_Float16, bits);
-      if (r & 1) pb[r >> 3][(r & 7) >> 1] |= (uint32_t)bits << 16;
-      else pb[r >> 3][(r & 7) >> 1] = bits;
-    }
-    if constexpr (TOK) {
-#pragma unroll
-      for (int r = 0; r < NSV; ++r) vbias = fmaf(pr[r], pbias[r], vbias);
-    } else {
-#pragma unroll
-      for (int r = 0; r < NSV; ++r) lsum_r += pr[r];
-    }
-
-    // ---- O^T += V^T . P^T ----
-    // 32 columns: MFMA n takes k-step n / 4 and row tile n % 4 (32 channels);
-    // 16 columns: MFMA n takes row tile n (16 channels) over all 32 tokens
-    const uint32_t vt = I8 ? slot : slot + TB;
-    u32x4 vb[8];
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int kk = NC == 32 ? n / NOT : 0, mt = NC == 32 ? n % NOT : n;
-      const int tp = NC == 32 ? (mt & 1) : (mt & 3);
-      const int hi8 = NC == 32 ? (mt >> 1) : (mt >> 2);
-      const uint32_t imm = kRowB16 * 16 * kk;
-      const s16x4_t lo = lds_read_tr16(vt + offV[hi8][tp][0] + imm);
-      const s16x4_t hi = lds_read_tr16(vt + offV[hi8][tp][1] + imm);
-      vb[n] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int kk = NC == 32 ? n / NOT : 0, mt = NC == 32 ? n % NOT : n;
-      acc[mt] = mfma_nc<NC, MK>(vb[n], pb[kk], acc[mt]);
-    }
-  }
-
-  // ---- partial triple: normalised out, true max, sum relative to it ----
-  const float ltot = col_sum<NC>(lsum);
-  // normaliser: the rounded weights PV applied (per-channel int8 and 16-bit:
-  // this also cancels the 1152 bias exactly), or, per-token, the fp32 weights
-  // whose scaled and rounded values PV applied (the bias leaves through vbias)
-  const float lr = TOK ? ltot : col_sum<NC>(lsum_r);
-  const float inv = lr > 0.f ? 1.f / lr : 0.f;  // 0: every token of the split removed for this row
-  const float vb = TOK ? col_sum<NC>(vbias) * inv : 0.f;
-#pragma unroll
-  for (int mt = 0; mt < NOT; ++mt) scale_acc(acc[mt], inv);
-  if (row_ok) {
-    // O^T tile mt, register 4 r4 + e: channel NC mt + 8 r4 + 4 kg + e
-    float* o = a.ws_o + (qrow * a.n_split + split) * kD;
+    float mref = kMrefInit, mtrue = kNegInf, lsum = 0.f, lsum_r = 0.f;
+    float vbias = 0.f;  // per-token int8: sum over tokens of rounded weight * (offset_V - 1152)
+    AccT acc[NOT];
 #pragma unroll
     for (int mt = 0; mt < NOT; ++mt)
 #pragma unroll
-      for (int r4 = 0; r4 < AW / 4; ++r4) {
-        const int d = NC * mt + 8 * r4 + 4 * kg;
-        f32x4_t v;
+      for (int r = 0; r < AW; ++r) acc[mt][r] = 0.f;
+
+    for (int i = 0; i < ntiles; ++i) {
+      // tile i has landed once only the loads of the tiles queued after it
+      // (at most kStages - 2) remain (vmcnt retires in order)
+      const int after = min(kStages - 2, ntiles - 1 - i);
+      if constexpr (kStages == 3) {
+        if (after >= 1) wait_vmem<2 * LT>();
+        else wait_vmem<0>();
+      } else {
+        wait_vmem<0>();
+      }
+      // tile i + kStages - 1 goes into the slot of tile i - 1, whose operands
+      // this wave read during the last iteration, before their MFMAs.  Queued
+      // after the wait: with two slots one tile is in flight while this one is
+      // computed, which measured faster than queueing it before the wait (two
+      // in flight) or a third slot.
+      if (i + kStages - 1 < ntiles) queue_tile(i + kStages - 1, (i + kStages - 1) % kStages);
+      const uint32_t slot = ring_lds + (i % kStages) * SLOT;
+      const int tstart = start + kTile * i;
+
+      // ---- S^T = K . Q^T ----
+      AccT sacc[NSA];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[mt][4 * r4 + e];
-        if constexpr (TOK) {
+      for (int m = 0; m < NSA; ++m)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] += vb;
-        } else if constexpr (I8) {
-          // P V ran on 1152 + x: x_hat = (x + offset) * scale per channel (index 1)
+        for (int r = 0; r < AW; ++r) sacc[m][r] = 0.f;
+      u32x4 kb[NSA][NKS];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int vq = a.aq_stride_kv + g * a.aq_stride_g + (d + e) * a.aq_stride_d;
-            v[e] = a.aq_scale[vq] * (v[e] - 1152.f + a.aq_offset[vq]);
+      for (int m = 0; m < NSA; ++m)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          if constexpr (I8) {
+            const u32x2 x = lds_read_b64(slot + offS[m][ks]);
+            const u32x2 w0 = widen_i8(x[0]), w1 = widen_i8(x[1]);
+            kb[m][ks] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+          } else {
+            kb[m][ks] = lds_read_b128(slot + offS[m][ks]);
           }
         }
-        *reinterpret_cast<f32x4_t*>(o + d) = v;
+#pragma unroll
+      for (int m = 0; m < NSA; ++m)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) sacc[m] = mfma_nc<NC, MK>(kb[m][ks], qreg[ks], sacc[m]);
+
+      // int8: widen this V tile into an fp16 copy in 16-bit row layout, written
+      // over the whole slot (K and V, 2 x 4 KB), whose K operands are in
+      // registers by now.  All int8 chunks are read before any write (a wave's
+      // LDS operations complete in order).  Lane takes positions P = lane + 64 k
+      // of the int8 V tile: row t = P / 8, chunk c = (P % 8) ^ swz(t) = channels
+      // 16 c .. 16 c + 15, which become fp16 chunks 2 c and 2 c + 1 of row t.
+      if constexpr (I8) {
+        u32x4 x[TB / 1024];
+#pragma unroll
+        for (int k = 0; k < TB / 1024; ++k) x[k] = lds_read_b128(slot + TB + 16 * (lane_p + 64 * k));
+#pragma unroll
+        for (int k = 0; k < TB / 1024; ++k) {
+          const int P = lane_p + 64 * k;
+          const int t = P >> 3;
+          const int c = (P & 7) ^ swz(t);
+          const u32x2 w0 = widen_i8(x[k][0]), w1 = widen_i8(x[k][1]), w2 = widen_i8(x[k][2]), w3 = widen_i8(x[k][3]);
+          const u32x4 lo = {w0[0], w0[1], w1[0], w1[1]}, hi = {w2[0], w2[1], w3[0], w3[1]};
+          lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c) ^ swz16(t)), lo);
+          lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c + 1) ^ swz16(t)), hi);
+        }
+        // the reads below see this wave's writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
       }
-    if (kg == 0) {
-      a.ws_m[qrow * a.n_split + split] = mtrue * kLn2;
-      a.ws_l[qrow * a.n_split + split] = ltot > 0.f ? ltot * fast_exp2(mref - mtrue) : 0.f;
+
+      // ---- online softmax over this lane's row (column) ----
+      // score register r (accumulator register r % AW of S^T tile r / AW) holds
+      // token TS (r / 4) + 4 kg + r % 4 of the tile
+      float sv[NSV];
+      if constexpr (TOK) {
+        // score of token t: scale_K[t] (q . (1152 + x_t) + (offset_K[t] - 1152) sum q); this lane's
+        // tokens TS q4 + 4 kg + e lie in 16-byte groups of each parameter array
+        const uint32_t pa = slot + 2 * TB + 16 * kg;
+#pragma unroll
+        for (int q4 = 0; q4 < NSV / 4; ++q4) {
+          const f32x4_t sk = lds_read_f32x4(pa + 4 * TS * q4), ok = lds_read_f32x4(pa + 128 + 4 * TS * q4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            sv[r] = sk[e] * fmaf(ok[e] - 1152.f, qsum, sacc[r / AW][r % AW]) * a.scale_log2;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < NSV; ++r) sv[r] = (sacc[r / AW][r % AW] + kconst) * a.scale_log2;
+      }
+      if (tstart + kTile > end || tstart + kTile > draft0) {  // the split's tail, or draft tokens
+#pragma unroll
+        for (int r = 0; r < NSV; ++r) {
+          const int tok = tstart + TS * (r >> 2) + 4 * kg + (r & 3);
+          const uint32_t k = (uint32_t)(tok - draft0);  // draft index; huge for tokens before the drafts
+          const uint32_t kept = k < 32u ? (vis >> k) & 1u : 1u;
+          const uint32_t keep = (uint32_t)(tok < end) & kept;
+          sv[r] = keep ? sv[r] : kNegInf;  // a select, not a branch
+        }
+      }
+      float smax = kNegInf;
+#pragma unroll
+      for (int r = 0; r < NSV; ++r) smax = fmaxf(smax, sv[r]);
+      smax = col_max<NC>(smax);  // the column's other tokens sit in the lanes l ^ 16 / 32 / 48
+      mtrue = fmaxf(mtrue, smax);
+      if (__builtin_amdgcn_ballot_w64(smax > mref + kRescale)) {
+        const float mnew = smax > mref + kRescale ? smax : mref;
+        const float alpha = fast_exp2(mref - mnew);  // 0 on the first scores
+        lsum *= alpha;
+        lsum_r *= alpha;
+        vbias *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < NOT; ++mt) scale_acc(acc[mt], alpha);
+        mref = mnew;
+      }
+      // P^T operand: k-slot j of lane group kg in 16-token k-step kk is score
+      // register 8 kk + j (32 columns), or, in the one 32-token k-step, score
+      // register j (16 columns), rounded to the MFMA operand type
+      u32x4 pb[NSV / 8];
+      float pr[NSV];
+      float pscale[NSV], pbias[NSV];  // per-token int8: V scale and offset - 1152 of each token
+      if constexpr (TOK) {
+        const uint32_t pa = slot + 2 * TB + 256 + 16 * kg;
+#pragma unroll
+        for (int q4 = 0; q4 < NSV / 4; ++q4) {
+          const f32x4_t sv4 = lds_read_f32x4(pa + 4 * TS * q4), ov4 = lds_read_f32x4(pa + 128 + 4 * TS * q4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pscale[4 * q4 + e] = sv4[e], pbias[4 * q4 + e] = ov4[e] - 1152.f;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < NSV; ++r) {
+        const float pf = fast_exp2(sv[r] - mref);  // <= 2^8; 0 for removed tokens
+        lsum += pf;
+        // per-token int8: the weight that multiplies the widened V row is
+        // p * scale_V[t]; its rounded value also removes the 1152 bias and adds
+        // the V offset through vbias
+        const uint16_t bits = round16<MK>(TOK ? pf * pscale[r] : pf);
+        pr[r] = MK == kBF16 ? (float)__builtin_bit_cast(__bf16, bits) : (float)__builtin_bit_cast(_Float16, bits);
+        if (r & 1) pb[r >> 3][(r & 7) >> 1] |= (uint32_t)bits << 16;
+        else pb[r >> 3][(r & 7) >> 1] = bits;
+      }
+      if constexpr (TOK) {
+#pragma unroll
+        for (int r = 0; r < NSV; ++r) vbias = fmaf(pr[r], pbias[r], vbias);
+      } else {
+#pragma unroll
+        for (int r = 0; r < NSV; ++r) lsum_r += pr[r];
+      }
+
+      // ---- O^T += V^T . P^T ----
+      // 32 columns: MFMA n takes k-step n / 4 and row tile n % 4 (32 channels);
+      // 16 columns: MFMA n takes row tile n (16 channels) over all 32 tokens
+      const uint32_t vt = I8 ? slot : slot + TB;
+      u32x4 vb[8];
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int kk = NC == 32 ? n / NOT : 0, mt = NC == 32 ? n % NOT : n;
+        const int tp = NC == 32 ? (mt & 1) : (mt & 3);
+        const int hi8 = NC == 32 ? (mt >> 1) : (mt >> 2);
+        const uint32_t imm = kRowB16 * 16 * kk;
+        const s16x4_t lo = lds_read_tr16(vt + offV[hi8][tp][0] + imm);
+        const s16x4_t hi = lds_read_tr16(vt + offV[hi8][tp][1] + imm);
+        vb[n] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int kk = NC == 32 ? n / NOT : 0, mt = NC == 32 ? n % NOT : n;
+        acc[mt] = mfma_nc<NC, MK>(vb[n], pb[kk], acc[mt]);
+      }
     }
+
+    // ---- partial triple: normalised out, true max, sum relative to it ----
+    const float ltot = col_sum<NC>(lsum);
+    // normaliser: the rounded weights PV applied (per-channel int8 and 16-bit:
+    // this also cancels the 1152 bias exactly), or, per-token, the fp32 weights
+    // whose scaled and rounded values PV applied (the bias leaves through vbias)
+    const float lr = TOK ? ltot : col_sum<NC>(lsum_r);
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;  // 0: every token of the split removed for this row
+    const float vb = TOK ? col_sum<NC>(vbias) * inv : 0.f;
+#pragma unroll
+    for (int mt = 0; mt < NOT; ++mt) scale_acc(acc[mt], inv);
+    if (row_ok) {
+      // O^T tile mt, register 4 r4 + e: channel NC mt + 8 r4 + 4 kg + e
+      float* o = a.ws_o + pidx * kD;
+#pragma unroll
+      for (int mt = 0; mt < NOT; ++mt)
+#pragma unroll
+        for (int r4 = 0; r4 < AW / 4; ++r4) {
+          const int d = NC * mt + 8 * r4 + 4 * kg;
+          f32x4_t v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[mt][4 * r4 + e];
+          if constexpr (TOK) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += vb;
+          } else if constexpr (I8) {
+            // P V ran on 1152 + x: x_hat = (x + offset) * scale per channel (index 1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int vq = a.aq_stride_kv + aq_g + (d + e) * a.aq_stride_d;
+              v[e] = aq_scale[vq] * (v[e] - 1152.f + aq_offset[vq]);
+            }
+          }
+          *reinterpret_cast<f32x4_t*>(o + d) = v;
+        }
+      if (kg == 0) {
+        a.ws_m[pidx] = mtrue * kLn2;
+        a.ws_l[pidx] = ltot > 0.f ? ltot * fast_exp2(mref - mtrue) : 0.f;
+      }
+    }
+
+    // next piece: the next sequence with tiles, while the run lasts
+    if constexpr (!BAL) break;
+    tcur = min(trun_end, at(incl, b));
+    if (tcur >= trun_end) break;
+    do {
+      ++b;  // stays below batch: units remain after tcur
+    } while (at(incl, b) == tcur);
   }
 }
 
 template <int QT, int KV, bool TOK, int NC>
 hipError_t launch_nc(const GqaLaunch& p, hipStream_t stream, const LaunchEvents* ev) {
-  const int items = p.batch * p.n_kv * ((p.rows_kv + NC - 1) / NC) * p.n_split;
+  // per-sequence split: (row group, split, KV head, sequence); balanced: (row group, run, KV head)
+  const int items = (p.balanced ? 1 : p.batch) * p.n_kv * ((p.rows_kv + NC - 1) / NC) * p.n_split;
   if (items == 0) return hipSuccess;
-  if (p.paged)
-    launch_kernel(gqa_mfma_kernel<QT, KV, true, TOK, NC>, dim3(items), dim3(64), stream, ev, p, items);
-  else
-    launch_kernel(gqa_mfma_kernel<QT, KV, false, TOK, NC>, dim3(items), dim3(64), stream, ev, p, items);
+  if constexpr (KV == kI8 && NC == 32) {
+    // the balanced int8 kernel with 32 columns would need more than the 256
+    // registers of two waves per SIMD: the host splits such shapes per sequence
+    if (p.balanced) return hipErrorInvalidValue;
+    launch_kernel(p.paged ? gqa_mfma_kernel<QT, KV, true, TOK, NC, false> : gqa_mfma_kernel<QT, KV, false, TOK, NC, false>,
+                  dim3(items), dim3(64), stream, ev, p, items);
+  } else {
+    auto kern = p.paged ? (p.balanced ? gqa_mfma_kernel<QT, KV, true, TOK, NC, true>
+                                      : gqa_mfma_kernel<QT, KV, true, TOK, NC, false>)
+                        : (p.balanced ? gqa_mfma_kernel<QT, KV, false, TOK, NC, true>
+                                      : gqa_mfma_kernel<QT, KV, false, TOK, NC, false>);
+    launch_kernel(kern, dim3(items), dim3(64), stream, ev, p, items);
+  }
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ struct GqaLaunch {
   // i * aq_tok_stride_kv + b * aq_tok_stride_b + g * aq_tok_stride_g + j
   bool aq_token;
   int64_t aq_tok_stride_kv, aq_tok_stride_b, aq_tok_stride_g;
-  float* ws_o;             // [B][q_seq][n_q][n_split][D]
+  float* ws_o;             // [B][q_seq][n_q][n_split][D] (balanced split: by slot, below)
   float* ws_m;             // [B][q_seq][n_q][n_split]
   float* ws_l;             // [B][q_seq][n_q][n_split]
   int batch, n_q, n_kv, group, heads_per_wg, n_split;
@@ -44,6 +44,14 @@ struct GqaLaunch {
   bool token_major;        // (blocks, block_size, N_kv, D) / (B, s_cap, N_kv, D) instead of head-major
   const int2* plan;        // [batch] (sequence, clamped length) in longest-first order, or null
   bool longest_first;      // without a plan: each workgroup ranks the lengths itself
+  // Balanced split of the MFMA kernel (batch <= kLongestFirstMaxBatch): the
+  // batch's 32-token tiles, sequence after sequence, each sequence's first
+  // one weighted kGqaPieceCost more, are cut into n_split runs of equal
+  // weight, the same runs for every KV head; run r's piece of sequence b
+  // writes partial slot r + b ([slot][q_seq][n_q] statistics,
+  // [slot][q_seq][n_q][D] outputs), and seg_desc[b] = (first slot, slot count).
+  bool balanced;
+  int2* seg_desc;
 };
 
 // MLA-shaped decode: all query heads share one latent KV head (MFMA path).
@@ -83,9 +91,9 @@ struct CombineLaunch {
   int batch, n_q, n_split, v_dim, out_dtype;  // batch counts (sequence, query token) pairs
   int q_seq;          // query tokens per sequence: row r belongs to sequence r / n_q / q_seq
   int64_t s_cap;
-  // balanced split of the MLA path: sequence b's partials are slots
-  // seg_desc[b].x .. + seg_desc[b].y - 1 of a [slot][n_q] layout; null for
-  // the per-sequence [row][n_split] layout
+  // balanced split (MLA and GQA MFMA paths): sequence b's partials are slots
+  // seg_desc[b].x .. + seg_desc[b].y - 1 of a [slot][q_seq][n_q] layout;
+  // null for the per-sequence [row][n_split] layout
   const int2* seg_desc;
 };
 
@@ -132,6 +140,11 @@ constexpr int kMlaMaxTableSlice = 1024;
 // Balanced split of the MLA path: the cost, in tiles, charged to a sequence
 // for the start of a piece on it.
 constexpr int kMlaPieceCost = 7;
+// The same for the balanced split of the GQA MFMA kernel (one wave per
+// workgroup: Q, block-table slice and first tile are three dependent memory
+// round trips, each a few microseconds under load, against about a
+// microsecond per streamed tile).
+constexpr int kGqaPieceCost = 8;
 
 // Optional events that a launch records around the kernel itself
 // (hipExtLaunchKernel), for measuring the kernel's own duration.

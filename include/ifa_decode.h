@@ -174,15 +174,17 @@ ifa_status ifa_decode_num_splits(const ifa_decode_args* args, int32_t* num_split
 
 /* Whether a call with `args` splits per sequence (*balanced = 0) or
  * balanced (1).  The balanced split is the automatic choice (num_splits 0)
- * of the MLA shape for batch <= 256 (when a run spans at most 1022 cache
- * blocks).  Every sequence with L > 0 tokens is cut into t = ceil(L / 32)
- * tiles (the last one ragged) and weighs 7 + t units: 7 for starting a piece
- * on it, then one per tile.  The V units of the batch, sequence after
- * sequence, are cut into R = min(n, V) runs, run r the units
- * [floor(r V / R), floor((r + 1) V / R)) (n = ifa_decode_num_splits); a run
- * takes the tiles whose units it holds.  Each run is one workgroup, so the
- * work per compute unit is about the same whatever the mix of lengths; a
- * run's piece of sequence b is one partial, in slot r + b. */
+ * for batch <= 256 of the MLA shape (when a run spans at most 1022 cache
+ * blocks) and of the GQA shapes that run on the matrix cores (head dim 128
+ * with 16-bit or int8 K/V).  Every sequence with L > 0 tokens is cut into
+ * t = ceil(L / 32) tiles (the last one ragged) and weighs P + t units: P for
+ * starting a piece on it (7 on the MLA shape, 8 on the GQA shapes), then one
+ * per tile.  The V units of the batch, sequence after sequence, are cut into
+ * R = min(n, V) runs, run r the units [floor(r V / R), floor((r + 1) V / R))
+ * (n = ifa_decode_num_splits); a run takes the tiles whose units it holds.
+ * Each run is one workgroup per (KV head, group of query rows), so the work
+ * per compute unit is about the same whatever the mix of lengths; a run's
+ * piece of sequence b is one partial, in slot r + b. */
 ifa_status ifa_decode_split_mode(const ifa_decode_args* args, int32_t* balanced);
 
 /* Phase 2 (aclnnIncreFlashAttentionV3): split-KV decode followed by the
@@ -206,7 +208,8 @@ ifa_status ifa_decode(const ifa_decode_args* args, void* workspace, size_t works
  * other paths rank the lengths inside the split-KV kernel and leave it
  * unused.
  * The balanced split lays the partials out by slot instead: attn_out fp32
- * [n + B][N_q][v_dim], softmax_max and softmax_sum fp32 [n + B][N_q], and the
+ * [n + B][S_q][N_q][v_dim], softmax_max and softmax_sum fp32 [n + B][S_q][N_q]
+ * (S_q = query tokens per sequence), and the
  * fourth array holds, for each sequence with at least one token, the int32
  * pair (first slot, number of slots) of its pieces, in token order. */
 ifa_status ifa_decode_splitkv(const ifa_decode_args* args, void* workspace, size_t workspace_bytes,
