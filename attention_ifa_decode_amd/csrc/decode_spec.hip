@@ -98,6 +98,21 @@ __device__ __forceinline__ void dma16_lane(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off offset:0 nt" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
+// The same from a wave-uniform base plus a 32-bit per-lane byte offset.  The
+// base is read from the first active lane, so that it sits in scalar
+// registers whatever the compiler made of it; that read is a VALU write of
+// those SGPRs, and a vector memory instruction may read an SGPR only 5 wait
+// states after a VALU wrote it.  The compiler inserts such waits before its
+// own instructions but not before inline asm, so the asm carries them.
+__device__ __forceinline__ void dma16_off(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t x = reinterpret_cast<uint64_t>(base);
+  const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 offset:0 nt" ::"v"(voff),
+               "s"(reinterpret_cast<const void*>(u)), "{m0}"(lds)
+               : "memory");
+}
+
 // 4 bytes per lane, lane l's at LDS byte address lds + 4 l
 __device__ __forceinline__ void dma4_lane(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dword %0, off offset:0" ::"v"(src), "{m0}"(lds) : "memory");
@@ -313,7 +328,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
       }
       incl[k] = carry + t;
       lenv[k] = Lb;
-      carry += __shfl(t, 63);
+      carry += __builtin_amdgcn_readfirstlane(__shfl(t, 63));  // the chunk's total, in a scalar register
     }
     ttotal = carry;
     // runs: min(n_split, total cost) of them, so that none is empty; run r
@@ -471,12 +486,8 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     const char* vbase = static_cast<const char*>(a.v);
     const uint32_t ring_lds = lds_addr(ring);
 
-    // Queue tile j into ring slot `slot`: LDS chunk position P of the K (or V)
-    // tile holds row t = P / CPR, chunk (P % CPR) ^ swz16(t) (int8: swz(t)) of token tstart + t
-    // (rows past the split's end repeat its last row).  A tile's 32 tokens lie
-    // in at most 3 cache blocks.
-    auto queue_tile = [&](int j, int slot) {
-      const int tstart = start + kTile * j;
+    // per-lane rows of the tile starting at token tstart into LDS byte address dst
+    auto queue_rows = [&](int tstart, uint32_t dst) {
       uint32_t tok0 = 0, adj0 = 0, adj1 = 0, adj2 = 0;
       if constexpr (PAGED) {
         const uint32_t bi0 = fast_div((uint32_t)tstart, a.bs_magic, a.bs_shift);
@@ -486,7 +497,6 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
         adj1 = block_id(bi0 + 1 <= bil ? bi0 + 1 : bil);
         adj2 = block_id(bi0 + 2 <= bil ? bi0 + 2 : bil);
       }
-      const uint32_t dst = ring_lds + slot * SLOT;
 #pragma unroll
       for (int i = 0; i < LT; ++i) {
         const int P = 64 * i + lane_p;
@@ -508,6 +518,58 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
         const uint64_t off = row * RB + 16u * (uint32_t)c;
         dma16_lane(kbase + off, dst + 1024 * i);
         dma16_lane(vbase + off, dst + TB + 1024 * i);
+      }
+    };
+
+    // Queue tile j into ring slot `slot`: LDS chunk position P of the K (or V)
+    // tile holds row t = P / CPR, chunk (P % CPR) ^ swz16(t) (int8: swz(t)) of token tstart + t
+    // (rows past the split's end repeat its last row).  A tile's 32 tokens lie
+    // in at most 3 cache blocks.
+    //
+    // A whole tile (32 tokens of the piece, in one cache block or in a
+    // contiguous cache) is 32 rows at a fixed stride from its first row: lane
+    // l's chunk of load i then sits at byte loff[i] from that row, the same
+    // for every such tile, and the tile costs a scalar base per K and V and
+    // the loads.  Other tiles (straddling a block boundary, or the piece's
+    // last) take the per-lane row computation.
+    const uint32_t row_stride = a.token_major ? (uint32_t)a.n_kv * RB : (uint32_t)RB;
+    uint32_t loff[LT];
+#pragma unroll
+    for (int i = 0; i < LT; ++i) {
+      const int P = 64 * i + lane_p;
+      const int t = P / CPR;
+      loff[i] = (uint32_t)t * row_stride + 16u * (uint32_t)((P % CPR) ^ (I8 ? swz(t) : swz16(t)));
+    }
+    auto queue_tile = [&](int j, int slot) {
+      const int tstart = start + kTile * j;
+      const uint32_t dst = ring_lds + slot * SLOT;
+      bool whole = tstart + kTile <= end;
+      uint64_t row0 = 0;  // row of token tstart
+      if constexpr (PAGED) {
+        const uint32_t bs = (uint32_t)a.block_size;
+        const uint32_t bi = fast_div((uint32_t)tstart, a.bs_magic, a.bs_shift);
+        const uint32_t u = (uint32_t)tstart - bi * bs;
+        whole = whole && u + kTile <= bs;
+        if (whole) {
+          const uint32_t blk = block_id(bi);
+          row0 = a.token_major ? ((uint64_t)blk * bs + u) * (uint32_t)a.n_kv + (uint32_t)g
+                               : ((uint64_t)blk * (uint32_t)a.n_kv + (uint32_t)g) * bs + u;
+        }
+      } else {
+        row0 = a.token_major ? ((uint64_t)b * (uint64_t)a.s_cap + (uint32_t)tstart) * (uint32_t)a.n_kv + (uint32_t)g
+                             : ((uint64_t)b * (uint32_t)a.n_kv + (uint32_t)g) * (uint64_t)a.s_cap + (uint32_t)tstart;
+      }
+      if (whole) {
+        const uint64_t boff = row0 * RB;
+        const char* kt = kbase + boff;
+        const char* vt = vbase + boff;
+#pragma unroll
+        for (int i = 0; i < LT; ++i) {
+          dma16_off(kt, loff[i], dst + 1024 * i);
+          dma16_off(vt, loff[i], dst + TB + 1024 * i);
+        }
+      } else {
+        queue_rows(tstart, dst);
       }
       if constexpr (TOK) {
         // parameter array 2 k + (lane / 32), token tstart + lane % 32 (clamped
