@@ -230,6 +230,31 @@ __device__ __forceinline__ void scale_acc(V& v, float s) {
   }
 }
 
+// Elements idx .. idx + 7 of a QT array as floats, with 16-byte loads (the
+// array 16-byte aligned, idx a multiple of 8) ...
+template <int QT>
+__device__ __forceinline__ void load8_vec(const void* base, int64_t idx, float (&out)[8]) {
+  if constexpr (QT == kF32) {
+    const f32x4_t* p = reinterpret_cast<const f32x4_t*>(static_cast<const float*>(base) + idx);
+    const f32x4_t x = p[0], y = p[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = x[e], out[4 + e] = y[e];
+  } else {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + idx);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint16_t h = (uint16_t)(word(x, e >> 1) >> (16 * (e & 1)));
+      out[e] = QT == kBF16 ? bf16_bits_to_f32(h) : (float)__builtin_bit_cast(_Float16, h);
+    }
+  }
+}
+// ... or with element loads
+template <int QT>
+__device__ __forceinline__ void load8_elem(const void* base, int64_t idx, float (&out)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = load_as_f32<QT>(base, idx + e);
+}
+
 // int8 bytes of one dword -> the fp16 pairs 1152 + x of bytes (0, 1) and (2, 3)
 __device__ __forceinline__ u32x2 widen_i8(uint32_t w) {
   const uint32_t b = w ^ 0x80808080u;
@@ -376,11 +401,13 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     const int kg = lane_p / NC;  // which group of 8 k-slots of an MFMA this lane feeds
     const int col = lane_p % NC;
     // The antiquant parameters, read afresh for each piece: hoisted out of
-    // the piece loop, the per-channel ones would hold 128 registers across it.
+    // the piece loop, the per-channel ones would hold 128 registers across
+    // it.  Only the KV head's offset into them is made opaque per piece, so
+    // that their loads stay global loads.
     const float* aq_scale = a.aq_scale;
     const float* aq_offset = a.aq_offset;
     int aq_g = __builtin_amdgcn_readfirstlane(g * a.aq_stride_g);  // the KV head's parameters
-    if constexpr (BAL) asm volatile("" : "+s"(aq_scale), "+s"(aq_offset), "+s"(aq_g));
+    if constexpr (BAL) asm volatile("" : "+s"(aq_g));
 
     // ---- this lane's row (the MFMA column it holds), its mask over the drafts ----
     const int rr = hg * NC + col;  // row of the KV head's q_seq * group rows
@@ -403,26 +430,11 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     u32x4 qreg[NKS];
     float kconst = 0.f;  // int8: sum_d q'_d (offset_d - 1152) over the row
     float qsum = 0.f;    // per-token int8: sum_d q_d of the fp16 query
-    if constexpr (I8 && TOK) {
-      // q in fp16 as given (the K scale varies per token and multiplies the score)
-      float part = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          uint32_t pair = 0;
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int d = KSTEP * ks + 8 * kg + 2 * w + e;
-            const _Float16 qh = row_ok ? (_Float16)load_as_f32<QT>(a.q, qrow * kD + d) : (_Float16)0.f;
-            part += (float)qh;
-            pair |= (uint32_t)__builtin_bit_cast(uint16_t, qh) << (16 * e);
-          }
-          qreg[ks][w] = pair;
-        }
-      qsum = col_sum<NC>(part);
-    } else if constexpr (I8) {
-      // q' = q * scale_K rounded to fp16, and this lane's half of the constant
+    if constexpr (I8 && !TOK && NC == 32) {
+      // q' = q * scale_K rounded to fp16, and this lane's half of the constant,
+      // element by element: the batched form below, with 64 channels per
+      // lane here, took this kernel past the 256 registers of two waves per
+      // SIMD
       float part = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
@@ -440,18 +452,96 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
           qreg[ks][w] = pair;
         }
       kconst = col_sum<NC>(part);  // the lanes of one column hold its channels between them
+    } else if constexpr (I8) {
+      // Channels KSTEP ks + 8 kg .. + 7 of the row, and (per channel) their K
+      // parameters, CH k-steps at a time: each chunk's loads are all issued
+      // before any is used, unconditionally (a padding row reads a valid row
+      // and is zeroed after), so a chunk costs one memory round trip rather
+      // than one per element.  (16 columns: one chunk of 4 k-steps, 96
+      // registers; 32 columns: four of 2 k-steps, which keeps the kernel at
+      // two waves per SIMD.)
+      constexpr int CH = NC == 16 ? 4 : 2;
+      const bool qvec = (reinterpret_cast<uintptr_t>(a.q) & 15) == 0;
+      const bool pchan = a.aq_stride_d == 1;  // per channel (2, N_kv, D); else per tensor (2)
+      const bool pvec = ((reinterpret_cast<uintptr_t>(aq_scale) | reinterpret_cast<uintptr_t>(aq_offset)) & 15) == 0;
+      float part = 0.f;
+#pragma unroll
+      for (int c0 = 0; c0 < NKS; c0 += CH) {
+        float qf[CH][8], sc[TOK ? 1 : CH][8], of[TOK ? 1 : CH][8];
+        if (qvec) {
+#pragma unroll
+          for (int k = 0; k < CH; ++k) load8_vec<QT>(a.q, qrow * kD + KSTEP * (c0 + k) + 8 * kg, qf[k]);
+        } else {
+#pragma unroll
+          for (int k = 0; k < CH; ++k) load8_elem<QT>(a.q, qrow * kD + KSTEP * (c0 + k) + 8 * kg, qf[k]);
+        }
+        if constexpr (!TOK) {
+          if (pchan && pvec) {
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+              load8_vec<kF32>(aq_scale, aq_g + KSTEP * (c0 + k) + 8 * kg, sc[k]);
+              load8_vec<kF32>(aq_offset, aq_g + KSTEP * (c0 + k) + 8 * kg, of[k]);
+            }
+          } else if (pchan) {
+#pragma unroll
+            for (int k = 0; k < CH; ++k) {
+              load8_elem<kF32>(aq_scale, aq_g + KSTEP * (c0 + k) + 8 * kg, sc[k]);
+              load8_elem<kF32>(aq_offset, aq_g + KSTEP * (c0 + k) + 8 * kg, of[k]);
+            }
+          } else {
+            const float s0 = aq_scale[aq_g], o0 = aq_offset[aq_g];
+#pragma unroll
+            for (int k = 0; k < CH; ++k)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) sc[k][e] = s0, of[k][e] = o0;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < CH; ++k)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            uint32_t pair = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int j = 2 * w + e;
+              _Float16 qh;
+              if constexpr (TOK) {
+                // q in fp16 as given (the K scale varies per token and multiplies the score)
+                qh = row_ok ? (_Float16)qf[k][j] : (_Float16)0.f;
+                part += (float)qh;
+              } else {
+                // q' = q * scale_K rounded to fp16, and this lane's part of the constant
+                qh = row_ok ? (_Float16)(qf[k][j] * sc[k][j]) : (_Float16)0.f;
+                part = fmaf((float)qh, of[k][j] - 1152.f, part);
+              }
+              pair |= (uint32_t)__builtin_bit_cast(uint16_t, qh) << (16 * e);
+            }
+            qreg[c0 + k][w] = pair;
+          }
+        // the scheduler would otherwise pull the next chunk's loads up here
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the lanes of one column hold its channels between them
+      if constexpr (TOK) qsum = col_sum<NC>(part);
+      else kconst = col_sum<NC>(part);
     } else if ((reinterpret_cast<uintptr_t>(a.q) & 15) == 0) {  // 16-byte loads
+      // loaded unconditionally (a padding row reads a valid row) and zeroed after
       const u32x4* qp = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.q) + qrow * RB) + kg;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qreg[ks] = row_ok ? qp[KSTEP / 8 * ks] : u32x4{0u, 0u, 0u, 0u};
+      for (int ks = 0; ks < NKS; ++ks) qreg[ks] = qp[KSTEP / 8 * ks];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qreg[ks][w] = row_ok ? word(qreg[ks], w) : 0u;
     } else {  // a query buffer aligned to its element only
       const uint16_t* qp = reinterpret_cast<const uint16_t*>(static_cast<const char*>(a.q) + qrow * RB) + 8 * kg;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
-          qreg[ks][w] =
-              row_ok ? (uint32_t)qp[KSTEP * ks + 2 * w] | ((uint32_t)qp[KSTEP * ks + 2 * w + 1] << 16) : 0u;
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t v = (uint32_t)qp[KSTEP * ks + 2 * w] | ((uint32_t)qp[KSTEP * ks + 2 * w + 1] << 16);
+          qreg[ks][w] = row_ok ? v : 0u;
+        }
     }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) settle(qreg[ks]);
@@ -814,34 +904,67 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     const float vb = TOK ? col_sum<NC>(vbias) * inv : 0.f;
 #pragma unroll
     for (int mt = 0; mt < NOT; ++mt) scale_acc(acc[mt], inv);
-    if (row_ok) {
-      // O^T tile mt, register 4 r4 + e: channel NC mt + 8 r4 + 4 kg + e
-      float* o = a.ws_o + pidx * kD;
+    // O^T tile mt, register 4 r4 + e: channel NC mt + 8 r4 + 4 kg + e.  int8
+    // (per channel or per tensor): the V parameters of a group of G tiles'
+    // channels are all loaded before that group's stores (the stores may
+    // alias them for the compiler, which would otherwise wait for each load
+    // in turn); 16 columns: all 8 tiles at once, 64 registers.
+    constexpr int G = NC == 16 ? NOT : 1;
+    const float* ps = aq_scale + a.aq_stride_kv + aq_g;
+    const float* po = aq_offset + a.aq_stride_kv + aq_g;
+    const bool vvec = a.aq_stride_d == 1 && ((reinterpret_cast<uintptr_t>(ps) | reinterpret_cast<uintptr_t>(po)) & 15) == 0;
+    float* o = a.ws_o + pidx * kD;
 #pragma unroll
-      for (int mt = 0; mt < NOT; ++mt)
+    for (int m0 = 0; m0 < NOT; m0 += G) {
+      f32x4_t vsc[I8 && !TOK ? G : 1][AW / 4], voff[I8 && !TOK ? G : 1][AW / 4];
+      if constexpr (I8 && !TOK) {
+        if (vvec) {
 #pragma unroll
-        for (int r4 = 0; r4 < AW / 4; ++r4) {
-          const int d = NC * mt + 8 * r4 + 4 * kg;
-          f32x4_t v;
+          for (int m = 0; m < G; ++m)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[mt][4 * r4 + e];
-          if constexpr (TOK) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] += vb;
-          } else if constexpr (I8) {
-            // P V ran on 1152 + x: x_hat = (x + offset) * scale per channel (index 1)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int vq = a.aq_stride_kv + aq_g + (d + e) * a.aq_stride_d;
-              v[e] = aq_scale[vq] * (v[e] - 1152.f + aq_offset[vq]);
+            for (int r4 = 0; r4 < AW / 4; ++r4) {
+              const int d = NC * (m0 + m) + 8 * r4 + 4 * kg;
+              vsc[m][r4] = *reinterpret_cast<const f32x4_t*>(ps + d);
+              voff[m][r4] = *reinterpret_cast<const f32x4_t*>(po + d);
             }
-          }
-          *reinterpret_cast<f32x4_t*>(o + d) = v;
+        } else {
+#pragma unroll
+          for (int m = 0; m < G; ++m)
+#pragma unroll
+            for (int r4 = 0; r4 < AW / 4; ++r4)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int d = (NC * (m0 + m) + 8 * r4 + 4 * kg + e) * a.aq_stride_d;
+                vsc[m][r4][e] = ps[d];
+                voff[m][r4][e] = po[d];
+              }
         }
-      if (kg == 0) {
-        a.ws_m[pidx] = mtrue * kLn2;
-        a.ws_l[pidx] = ltot > 0.f ? ltot * fast_exp2(mref - mtrue) : 0.f;
       }
+      if (row_ok) {
+#pragma unroll
+        for (int m = 0; m < G; ++m)
+#pragma unroll
+          for (int r4 = 0; r4 < AW / 4; ++r4) {
+            const int mt = m0 + m;
+            const int d = NC * mt + 8 * r4 + 4 * kg;
+            f32x4_t v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[mt][4 * r4 + e];
+            if constexpr (TOK) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] += vb;
+            } else if constexpr (I8) {
+              // P V ran on 1152 + x: x_hat = (x + offset) * scale per channel (index 1)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = vsc[m][r4][e] * (v[e] - 1152.f + voff[m][r4][e]);
+            }
+            *reinterpret_cast<f32x4_t*>(o + d) = v;
+          }
+      }
+    }
+    if (row_ok && kg == 0) {
+      a.ws_m[pidx] = mtrue * kLn2;
+      a.ws_l[pidx] = ltot > 0.f ? ltot * fast_exp2(mref - mtrue) : 0.f;
     }
 
     // next piece: the next sequence with tiles, while the run lasts
