@@ -417,13 +417,19 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     const int64_t qrow = ((int64_t)b * a.q_seq + qi) * a.n_q + hrow;
     const int64_t pidx = pbase + ((int64_t)qi * a.n_q + hrow) * pstride;  // this row's partial
     const int draft0 = L - a.q_seq;  // position of draft token 0
-    uint32_t vis = ~0u;              // bit k: the row attends to draft token k
+    uint32_t vis = ~0u;  // bit k: the row attends to draft token k
     if (a.mask_mode == 3) {
       vis = (2u << qi) - 1u;
     } else if (a.mask_mode == 9) {
-      vis = 0;
+      // the row's q_seq <= 16 mask bytes, all loaded (at clamped, in-bounds
+      // positions) before any is used
       const uint8_t* m = a.tree_mask + ((int64_t)b * a.q_seq + qi) * a.q_seq;
-      for (int k = 0; k < a.q_seq; ++k) vis |= (m[k] == 0 ? 1u : 0u) << k;
+      uint8_t mk[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) mk[k] = m[min(k, a.q_seq - 1)];
+      vis = 0;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) vis |= (k < a.q_seq && mk[k] == 0 ? 1u : 0u) << k;
     }
 
     // ---- Q^T operand: channels KSTEP ks + 8 kg .. + 7 per k-step (zero for padding rows) ----
