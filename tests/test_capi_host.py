@@ -314,8 +314,9 @@ def test_mla_balanced_split_plan():
 
 def test_gqa_balanced_split_plan():
     """The automatic split of the GQA shapes on the matrix cores (head dim 128,
-    16-bit or int8 K/V) is balanced for batch <= 256: about 2048 one-wave
-    workgroups, n = 2048 / (N_kv * row groups) runs, fewer when the batch's
+    16-bit or int8 K/V) is balanced for batch <= 256: one round of resident
+    one-wave workgroups (1024 for 16-bit K/V, 2048 for int8),
+    n = that / (N_kv * row groups) runs, fewer when the batch's
     units at full length (B (max_len / 32 + 8)) give a run less than 32 of
     them; partials in n + B slots of S_q * N_q rows.  int8 K/V with more than
     16 query rows per KV head, explicit split counts, batches over 256 and
@@ -327,12 +328,12 @@ def test_gqa_balanced_split_plan():
         assert lib().ifa_decode_num_splits(ctypes.byref(a), ctypes.byref(n)) == 0, ifa.last_error()
         return n.value
 
-    # paged bf16, B 64, 8192 tokens at most, 4 rows per KV head: 2048 / 8 runs
+    # paged bf16, B 64, 8192 tokens at most, 4 rows per KV head: 1024 / 8 runs
     a = base_args(num_splits=0)
-    assert split_mode(a) == 1 and runs(a) == 256
+    assert split_mode(a) == 1 and runs(a) == 128
     st, sz = ws_size(a)
     assert st == ifa.IFA_OK, ifa.last_error()
-    rows = (256 + 64) * 32
+    rows = (128 + 64) * 32
     assert sz == al(rows * 128 * 4) + 2 * al(rows * 4) + al(64 * 8)
     # the padded fp16 shape (B 16, s_cap 4096): 16 (128 + 8) / 32 = 68 runs
     c2 = dict(num_splits=0, batch=16, kv_layout=ifa.IFA_KV_BNSD, s_cap=4096, q_dtype=ifa.IFA_F16,
@@ -342,15 +343,15 @@ def test_gqa_balanced_split_plan():
     assert runs(base_args(num_splits=0, batch=1, max_blocks_per_seq=1)) == 1
     # multi-token decode: 4 tokens x 4 heads = 16 rows per KV head, S_q N_q rows per slot
     mt = base_args(num_splits=0, q_seq_len=4, sparse_mode=ifa.IFA_MASK_CAUSAL)
-    assert split_mode(mt) == 1 and runs(mt) == 256
-    rows = (256 + 64) * 4 * 32
+    assert split_mode(mt) == 1 and runs(mt) == 128
+    rows = (128 + 64) * 4 * 32
     assert ws_size(mt)[1] == al(rows * 128 * 4) + 2 * al(rows * 4) + al(64 * 8)
-    # 64 rows per KV head: 2 row groups of 32 columns -> 2048 / 16 runs
-    assert runs(base_args(num_splits=0, q_seq_len=16)) == 128
+    # 64 rows per KV head: 2 row groups of 32 columns -> 1024 / 16 runs
+    assert runs(base_args(num_splits=0, q_seq_len=16)) == 64
     # int8 K/V: balanced with at most 16 rows per KV head, per sequence above
     i8 = dict(num_splits=0, kv_dtype=ifa.IFA_I8, antiquant_scale=FAKE, antiquant_offset=FAKE,
               antiquant_mode=ifa.IFA_ANTIQUANT_PER_CHANNEL, num_heads=64)
-    assert split_mode(base_args(**i8)) == 1
+    assert split_mode(base_args(**i8)) == 1 and runs(base_args(**i8)) == 256  # 2048 / 8
     assert split_mode(base_args(q_seq_len=4, **i8)) == 0
     assert split_mode(base_args(num_splits=4)) == 0
     assert split_mode(base_args(num_splits=0, batch=257, num_blocks=9000)) == 0
