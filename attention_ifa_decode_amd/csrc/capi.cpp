@@ -98,19 +98,20 @@ int auto_splits_mfma(const ifa_decode_args* a, int64_t n_kv, int rows_kv, int64_
 // waves per SIMD are the register limit): every run starts at once and they
 // finish together, where a second round of equal runs would start in step
 // and pay the start of a workgroup twice (2048 runs of 16-bit rows measured
-// 2-25% slower than 1024).  At least 4 kGqaPieceCost units per run at the
-// longest lengths (on the padded fp16 decode of 16 sequences of up to 4096
-// tokens, 68 runs measured as fast as the per-sequence split, 136 and 256
-// runs 5-10% slower).  The per-sequence split sizes its splits by each
-// sequence's length, so with mixed lengths the longest splits (and the tail
-// of the kernel) are about twice the mean; equal runs finish together.
+// 2-25% slower than 1024).  Short runs cost little more than long ones: the
+// runs start together, so their starts overlap, and small batches gain most
+// from the full round (two sequences of about 2000 tokens: 15.5 us at 128
+// runs, 26.3 us at 9, 21.1 us with the per-sequence split).  The only bound is
+// one run per cost unit at the longest lengths; more runs would hold no work.
+// The per-sequence split sizes its splits by each sequence's length, so with
+// mixed lengths the longest splits (and the tail of the kernel) are about
+// twice the mean; equal runs finish together.
 int balanced_runs_gqa(const ifa_decode_args* a, int64_t n_kv, int rows_kv, int64_t max_len) {
   const int64_t per_run = n_kv * ((rows_kv + (rows_kv <= 16 ? 15 : 31)) / (rows_kv <= 16 ? 16 : 32));
   const int64_t resident = (a->kv_dtype == IFA_I8 ? 8LL : 4LL) * kTargetCUs;
   int64_t r = (resident + per_run - 1) / per_run;
   const int64_t units = a->batch * ((max_len + 31) / 32 + ifa::kGqaPieceCost);
-  const int64_t by_len = (units + 4 * ifa::kGqaPieceCost - 1) / (4 * ifa::kGqaPieceCost);
-  if (r > by_len) r = by_len;
+  if (r > units) r = units;
   return (int)(r < 1 ? 1 : (r > kMaxSplits ? kMaxSplits : r));
 }
 

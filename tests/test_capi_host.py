@@ -335,12 +335,13 @@ def test_gqa_balanced_split_plan():
     assert st == ifa.IFA_OK, ifa.last_error()
     rows = (128 + 64) * 32
     assert sz == al(rows * 128 * 4) + 2 * al(rows * 4) + al(64 * 8)
-    # the padded fp16 shape (B 16, s_cap 4096): 16 (128 + 8) / 32 = 68 runs
+    # the padded fp16 shape (B 16, s_cap 4096): one round, 1024 / 8 runs
     c2 = dict(num_splits=0, batch=16, kv_layout=ifa.IFA_KV_BNSD, s_cap=4096, q_dtype=ifa.IFA_F16,
               kv_dtype=ifa.IFA_F16, out_dtype=ifa.IFA_F16)
-    assert split_mode(base_args(**c2)) == 1 and runs(base_args(**c2)) == 68
-    # one short sequence: runs of at least 32 units
-    assert runs(base_args(num_splits=0, batch=1, max_blocks_per_seq=1)) == 1
+    assert split_mode(base_args(**c2)) == 1 and runs(base_args(**c2)) == 128
+    # one sequence of at most one block (128 tokens): 4 tiles + 8 start units,
+    # one run per unit
+    assert runs(base_args(num_splits=0, batch=1, max_blocks_per_seq=1)) == 12
     # multi-token decode: 4 tokens x 4 heads = 16 rows per KV head, S_q N_q rows per slot
     mt = base_args(num_splits=0, q_seq_len=4, sparse_mode=ifa.IFA_MASK_CAUSAL)
     assert split_mode(mt) == 1 and runs(mt) == 128

@@ -1,8 +1,9 @@
 """GPU check of ifa_decode_noalloc, the entry point for callers that cannot
 allocate: called through the C ABI, its output must equal ifa_decode's (same
 kernels, same split plan, partials in the library's fixed array instead of a
-caller workspace), bit for bit, on calls in a row whose sizes shrink, so that
-contents the array keeps from a larger call cannot leak into a smaller one."""
+caller workspace), bit for bit, on calls in a row, the last three each
+smaller than the one before, so that contents the array keeps from a larger
+call cannot leak into a smaller one."""
 
 import ctypes
 
@@ -54,7 +55,8 @@ def test_noalloc_equals_ifa_decode_on_shrinking_calls():
         a, b = _pair(w)
         _same(a, b)
         sizes.append(ifa.call_for_workload(w.to("cuda")).workspace_bytes)
-    assert sizes[0] > sizes[2] > sizes[3] > 0
+    # the MLA call's partials are the largest; the calls after it shrink
+    assert sizes[1] > max(sizes[0], sizes[2]) and sizes[2] > sizes[3] > 0
 
 
 def test_noalloc_rejects_calls_beyond_its_array():
