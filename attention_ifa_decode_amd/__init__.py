@@ -241,6 +241,9 @@ class DecodeCall:
         bal = ctypes.c_int32(0)
         _check(lib.ifa_decode_split_mode(ctypes.byref(a), ctypes.byref(bal)))
         self.balanced = bool(bal.value)
+        # partial outputs: fp16 on the MLA shape (qk_dim 576, v_dim 512), else fp32
+        self.mla = qk_dim == 576 and v_dim == 512
+        self.partial_dtype = torch.float16 if self.mla else torch.float32
         self.noalloc = noalloc
         if noalloc:  # partials in the library's fixed array (ifa_decode_noalloc)
             self.workspace_bytes, self.workspace = 0, None
@@ -295,7 +298,8 @@ class DecodeCall:
 
     def partials(self):
         """Views of the workspace after ``splitkv()``: (attn_out, softmax_max,
-        softmax_sum) with shapes (B, N_q, n, v_dim), (B, N_q, n), (B, N_q, n);
+        softmax_sum) with shapes (B, N_q, n, v_dim), (B, N_q, n), (B, N_q, n),
+        attn_out in ``partial_dtype`` (fp16 on the MLA shape, else fp32);
         with S_q query tokens B counts (sequence, query token) pairs.  The
         per-sequence split only; see ``partial_slots`` for the balanced one."""
         if self.balanced:
@@ -305,14 +309,15 @@ class DecodeCall:
         f = self.workspace.view(torch.float32) if self.workspace_bytes else None
         rows = B * nq * n
         al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-        off_m = al(rows * dv * 4) // 4
+        ob = 2 if self.mla else 4  # attn_out fp16 on the MLA shape
+        off_m = al(rows * dv * ob) // 4
         off_l = off_m + al(rows * 4) // 4
-        return (f[:rows * dv].view(B, nq, n, dv), f[off_m:off_m + rows].view(B, nq, n),
-                f[off_l:off_l + rows].view(B, nq, n))
+        o = self.workspace.view(self.partial_dtype)[:rows * dv].view(B, nq, n, dv)
+        return (o, f[off_m:off_m + rows].view(B, nq, n), f[off_l:off_l + rows].view(B, nq, n))
 
     def partial_slots(self):
         """Views of the workspace after ``splitkv()`` with the balanced split:
-        (attn_out (n + B, S_q * N_q, v_dim), softmax_max (n + B, S_q * N_q),
+        (attn_out (n + B, S_q * N_q, v_dim) in ``partial_dtype``, softmax_max (n + B, S_q * N_q),
         softmax_sum (n + B, S_q * N_q), (first slot, slot count) int32 (B, 2));
         run r's piece of sequence b is slot r + b, and query token t of head h
         is row t * N_q + h of a slot."""
@@ -324,12 +329,13 @@ class DecodeCall:
         f = self.workspace.view(torch.float32)
         rows = slots * nq
         al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-        off_m = al(rows * dv * 4) // 4
+        ob = 2 if self.mla else 4  # attn_out fp16 on the MLA shape
+        off_m = al(rows * dv * ob) // 4
         off_l = off_m + al(rows * 4) // 4
         off_p = off_l + al(rows * 4) // 4
         desc = self.workspace.view(torch.int32)[off_p:off_p + 2 * B].view(B, 2)
-        return (f[:rows * dv].view(slots, nq, dv), f[off_m:off_m + rows].view(slots, nq),
-                f[off_l:off_l + rows].view(slots, nq), desc)
+        o = self.workspace.view(self.partial_dtype)[:rows * dv].view(slots, nq, dv)
+        return (o, f[off_m:off_m + rows].view(slots, nq), f[off_l:off_l + rows].view(slots, nq), desc)
 
 
 def decode(q, k_cache, v_cache, block_table, actual_seq_lengths, num_heads: int, num_key_value_heads: int,

@@ -316,7 +316,8 @@ ifa_status validate_and_plan(const ifa_decode_args* a, Plan* plan) {
   const size_t rows = p.balanced ? ((size_t)p.n_split + (size_t)a->batch) * (size_t)q_seq * (size_t)a->num_heads
                                  : (size_t)a->batch * (size_t)q_seq * (size_t)a->num_heads * (size_t)p.n_split;
   p.off_o = 0;
-  p.off_m = align256(rows * (size_t)a->v_dim * sizeof(float));
+  // partial outputs: fp32, fp16 on the MLA path
+  p.off_m = align256(rows * (size_t)a->v_dim * (p.path == Path::kMla ? 2 : sizeof(float)));
   p.off_l = p.off_m + align256(rows * sizeof(float));
   p.off_plan = p.off_l + align256(rows * sizeof(float));
   // longest-first plan: (sequence, clamped length) per rank, int32 pairs; in
@@ -418,7 +419,7 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
   M.kv = a->key_cache;
   M.block_table = a->block_table;
   M.seq_lens = a->actual_seq_lengths;
-  M.ws_o = reinterpret_cast<float*>(w + p.off_o);
+  M.ws_o = reinterpret_cast<_Float16*>(w + p.off_o);
   M.ws_m = reinterpret_cast<float*>(w + p.off_m);
   M.ws_l = reinterpret_cast<float*>(w + p.off_l);
   M.batch = (int)a->batch;
@@ -443,7 +444,8 @@ ifa_status run_splitkv(const ifa_decode_args* a, const Plan& p, void* ws, hipStr
 ifa_status run_combine(const ifa_decode_args* a, const Plan& p, const void* ws, hipStream_t stream) {
   const char* w = static_cast<const char*>(ws);
   ifa::CombineLaunch C{};
-  C.ws_o = reinterpret_cast<const float*>(w + p.off_o);
+  C.ws_o = w + p.off_o;
+  C.o_f16 = p.path == Path::kMla;
   C.ws_m = reinterpret_cast<const float*>(w + p.off_m);
   C.ws_l = reinterpret_cast<const float*>(w + p.off_l);
   C.seq_lens = a->actual_seq_lengths;

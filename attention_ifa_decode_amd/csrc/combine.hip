@@ -60,19 +60,22 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, const float4& v) 
 }
 
 // One wave per (batch, head) row.  A row's partial outputs are n_split
-// contiguous vectors of VD floats; lanes read them as float4 columns, so a
-// load instruction covers PARTS = 64 / (VD/4) splits (4 at VD 64, 2 at 128,
-// 1 at 512, where each lane holds two columns).  All loads of a batch of
-// splits are issued before the statistics are reduced, so a row costs one
-// memory round trip rather than one per split.
-template <int OT, int VD>
+// contiguous vectors of VD values, fp32 or (H, the MLA path) fp16; lanes
+// read them in 16-byte units of E = 4 or 8 channels, so a load instruction
+// covers PARTS = 64 / (VD/E) splits (4 at VD 64, 2 at 128, 1 at 512, where
+// fp32 lanes hold two units).  All loads of a batch of splits are issued
+// before the statistics are reduced, so a row costs one memory round trip
+// rather than one per split.
+template <int OT, int VD, bool H>
 __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
-  constexpr int kQuads = VD / 4;
-  constexpr int kLanesPerSplit = kQuads < 64 ? kQuads : 64;
+  constexpr int kE = H ? 8 : 4;  // channels per 16-byte unit
+  constexpr int kUnits = VD / kE;
+  constexpr int kLanesPerSplit = kUnits < 64 ? kUnits : 64;
   constexpr int kParts = 64 / kLanesPerSplit;
-  constexpr int kCols = kQuads / kLanesPerSplit;
-  constexpr int kSteps = kCols == 2 ? 16 : 8;  // loads in flight per lane: 32 at VD 512, 8 below
-  constexpr int kBatch = kSteps * kParts;                     // splits per batch of loads
+  constexpr int kCols = kUnits / kLanesPerSplit;
+  // loads in flight per lane: 32 at VD 512, 8 below
+  constexpr int kSteps = kCols == 2 ? 16 : (kParts == 1 ? 32 : 8);
+  constexpr int kBatch = kSteps * kParts;  // splits per batch of loads
   __shared__ float sm_m[kRowsPerBlock][kMaxSplitsPerRow];
   __shared__ float sm_w[kRowsPerBlock][kMaxSplitsPerRow];
 
@@ -89,8 +92,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
   // reads the sequence's slot range first.
   int64_t L64 = a.seq_lens[b / a.q_seq];
   const int L = (int)(L64 < 0 ? 0 : (L64 > a.s_cap ? a.s_cap : L64));
-  const float4* o;
+  const uint4* o;
   const float *m, *l;
+  const char* const wo = static_cast<const char*>(a.ws_o);
+  constexpr int64_t kRowBytes = (int64_t)VD * (H ? 2 : 4);
   int ostep, mstep, nload, nvalid = 0;
   if (a.seg_desc) {
     // slot s holds rows (query token, head): row qi n_q + h of q_seq n_q
@@ -102,24 +107,24 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
     nvalid = max(nvalid, 0);
     const int per_slot = a.q_seq * a.n_q;
     const int64_t first = (int64_t)s0 * per_slot + (int64_t)qi * a.n_q + h;
-    o = reinterpret_cast<const float4*>(a.ws_o + first * VD);
+    o = reinterpret_cast<const uint4*>(wo + first * kRowBytes);
     m = a.ws_m + first;
     l = a.ws_l + first;
-    ostep = per_slot * kQuads, mstep = per_slot, nload = nvalid;
+    ostep = per_slot * kUnits, mstep = per_slot, nload = nvalid;
   } else {
-    o = reinterpret_cast<const float4*>(a.ws_o + (int64_t)row * a.n_split * VD);
+    o = reinterpret_cast<const uint4*>(wo + (int64_t)row * a.n_split * kRowBytes);
     m = a.ws_m + (int64_t)row * a.n_split;
     l = a.ws_l + (int64_t)row * a.n_split;
-    ostep = kQuads, mstep = 1, nload = a.n_split;
+    ostep = kUnits, mstep = 1, nload = a.n_split;
   }
-  float4 v[kSteps][kCols];
+  uint4 v[kSteps][kCols];
   auto load_batch = [&](int s0) {
 #pragma unroll
     for (int j = 0; j < kSteps; ++j) {
       const int s = s0 + j * kParts + part;
 #pragma unroll
       for (int c = 0; c < kCols; ++c)
-        v[j][c] = s < nload ? o[(int64_t)s * ostep + c * kLanesPerSplit + col] : float4{0.f, 0.f, 0.f, 0.f};
+        v[j][c] = s < nload ? o[(int64_t)s * ostep + c * kLanesPerSplit + col] : uint4{0u, 0u, 0u, 0u};
     }
   };
   load_batch(0);
@@ -159,9 +164,26 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
 
-  float4 acc[kCols];
+  typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+  // a unit's channels as floats
+  auto unpack = [](const uint4& u, float (&f)[kE]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    if constexpr (H) {
 #pragma unroll
-  for (int c = 0; c < kCols; ++c) acc[c] = float4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < 4; ++k) {
+        const f16x2_t x = __builtin_bit_cast(f16x2_t, w[k]);
+        f[2 * k] = (float)x[0], f[2 * k + 1] = (float)x[1];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(w[k]);
+    }
+  };
+  float acc[kCols][kE];
+#pragma unroll
+  for (int c = 0; c < kCols; ++c)
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[c][e] = 0.f;
   for (int s0 = 0; s0 < nvalid; s0 += kBatch) {
     if (s0 > 0) load_batch(s0);
 #pragma unroll
@@ -171,10 +193,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
         const float w = sm_w[wave][s];
 #pragma unroll
         for (int c = 0; c < kCols; ++c) {
-          acc[c].x = fmaf(w, v[j][c].x, acc[c].x);
-          acc[c].y = fmaf(w, v[j][c].y, acc[c].y);
-          acc[c].z = fmaf(w, v[j][c].z, acc[c].z);
-          acc[c].w = fmaf(w, v[j][c].w, acc[c].w);
+          float f[kE];
+          unpack(v[j][c], f);
+#pragma unroll
+          for (int e = 0; e < kE; ++e) acc[c][e] = fmaf(w, f[e], acc[c][e]);
         }
       }
     }
@@ -182,11 +204,19 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
   for (int c = 0; c < kCols; ++c) {
-    float4 r = acc[c];
-    if constexpr (kParts == 4) r.x = xor16_sum(r.x), r.y = xor16_sum(r.y), r.z = xor16_sum(r.z), r.w = xor16_sum(r.w);
-    if constexpr (kParts >= 2) r.x = xor32_sum(r.x), r.y = xor32_sum(r.y), r.z = xor32_sum(r.z), r.w = xor32_sum(r.w);
-    r.x *= inv, r.y *= inv, r.z *= inv, r.w *= inv;
-    if (part == 0) store4<OT>(a.out, (int64_t)row * VD + (c * kLanesPerSplit + col) * 4, r);
+#pragma unroll
+    for (int e = 0; e < kE; ++e) {
+      float r = acc[c][e];
+      if constexpr (kParts == 4) r = xor16_sum(r);
+      if constexpr (kParts >= 2) r = xor32_sum(r);
+      acc[c][e] = r * inv;
+    }
+    if (part == 0) {
+#pragma unroll
+      for (int k = 0; k < kE / 4; ++k)
+        store4<OT>(a.out, (int64_t)row * VD + (c * kLanesPerSplit + col) * kE + 4 * k,
+                   float4{acc[c][4 * k], acc[c][4 * k + 1], acc[c][4 * k + 2], acc[c][4 * k + 3]});
+    }
   }
   if (a.lse && lane == 0) a.lse[row] = tot > 0.f ? M + __logf(tot) : kNegInf;
 }
@@ -223,12 +253,12 @@ __global__ void __launch_bounds__(256) update_kernel(const UpdateLaunch a) {
   }
 }
 
-template <int VD>
+template <int VD, bool H>
 hipError_t launch_combine_vd(const CombineLaunch& p, dim3 grid, hipStream_t stream) {
   switch (p.out_dtype) {
-    case kF32: hipLaunchKernelGGL((combine_kernel<kF32, VD>), grid, dim3(256), 0, stream, p); break;
-    case kF16: hipLaunchKernelGGL((combine_kernel<kF16, VD>), grid, dim3(256), 0, stream, p); break;
-    case kBF16: hipLaunchKernelGGL((combine_kernel<kBF16, VD>), grid, dim3(256), 0, stream, p); break;
+    case kF32: hipLaunchKernelGGL((combine_kernel<kF32, VD, H>), grid, dim3(256), 0, stream, p); break;
+    case kF16: hipLaunchKernelGGL((combine_kernel<kF16, VD, H>), grid, dim3(256), 0, stream, p); break;
+    case kBF16: hipLaunchKernelGGL((combine_kernel<kBF16, VD, H>), grid, dim3(256), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -258,10 +288,11 @@ hipError_t launch_combine(const CombineLaunch& p, hipStream_t stream) {
   if (rows >= (int64_t)1 << 31) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
   if (p.n_split < 1 || p.n_split > kMaxSplitsPerRow) return hipErrorInvalidValue;
+  if (p.o_f16) return p.v_dim == 512 ? launch_combine_vd<512, true>(p, grid, stream) : hipErrorInvalidValue;
   switch (p.v_dim) {
-    case 64: return launch_combine_vd<64>(p, grid, stream);
-    case 128: return launch_combine_vd<128>(p, grid, stream);
-    case 512: return launch_combine_vd<512>(p, grid, stream);
+    case 64: return launch_combine_vd<64, false>(p, grid, stream);
+    case 128: return launch_combine_vd<128, false>(p, grid, stream);
+    case 512: return launch_combine_vd<512, false>(p, grid, stream);
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

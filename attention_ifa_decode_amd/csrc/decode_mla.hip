@@ -45,6 +45,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
 
 constexpr int kDqk = 576, kDv = 512;
 constexpr int kRowBytes = kDqk * 2;             // 1152 bytes per cached token row
@@ -583,8 +584,11 @@ mla_splitkv_kernel(const MlaLaunch a) {
     const int64_t pidx = pbase + (int64_t)head * pstride;
     // O^T leaves through LDS, 128 channels at a time: lane (head, h) holds
     // 4 consecutive channels of its head per accumulator quad, so direct
-    // stores would write 32-byte pieces of 32 rows; read back row-wise, each
-    // store writes 512 contiguous bytes of two heads' rows.  The wave uses
+    // stores would write 8-byte (fp16) pieces of 32 rows; read back
+    // row-wise, each store writes 256 contiguous bytes of each of two heads'
+    // rows.  The partial outputs are fp16 (max and sum stay fp32): a
+    // normalised partial is a convex combination of V rows, within fp16's
+    // range as long as V is.  The wave uses
     // half of a ring slot that no wave reads any more (every slot but the
     // last tile's is free once the wave has left the loop; the next piece's
     // first barrier orders the reuse).  Rows are padded to 528 bytes, which
@@ -594,7 +598,7 @@ mla_splitkv_kernel(const MlaLaunch a) {
       const int last = (ntiles - 1) % STAGES;
       const uint32_t obuf = ring_lds + ((last + 1 + (wave >> 1)) % STAGES) * kTileBytes + (wave & 1) * 32 * kORow;
       const int hl = lane & 31;
-      float* const orow0 = a.ws_o + (pbase + (int64_t)(head - hl) * pstride) * kDv;
+      _Float16* const orow0 = a.ws_o + (pbase + (int64_t)(head - hl) * pstride) * kDv;
 #pragma unroll
       for (int c = 0; c < kMTiles / 4; ++c) {
 #pragma unroll
@@ -610,7 +614,9 @@ mla_splitkv_kernel(const MlaLaunch a) {
         for (int i = 0; i < 16; ++i) {
           const int r = 2 * i + h;  // row (head of the wave) this lane stores
           const f32x4_t v = lds_read_f32x4(obuf + r * kORow + 16 * hl);
-          *reinterpret_cast<f32x4_t*>(orow0 + (int64_t)r * pstride * kDv + 128 * c + 4 * hl) = v;
+          // rounded to fp16 (nearest even): 256 contiguous bytes per row
+          const f16x4_t w = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+          *reinterpret_cast<f16x4_t*>(orow0 + (int64_t)r * pstride * kDv + 128 * c + 4 * hl) = w;
         }
       }
     }

@@ -60,7 +60,9 @@ struct MlaLaunch {
   const void* kv;          // pool (num_blocks, 1, block_size, qk_dim) bf16; V = first v_dim channels
   const int32_t* block_table;
   const int64_t* seq_lens;
-  float* ws_o;
+  // partial outputs in fp16 (statistics in fp32): a normalised partial is a
+  // convex combination of V rows, so it stays within fp16's range when V does
+  _Float16* ws_o;
   float* ws_m;
   float* ws_l;
   int batch, n_q, n_split;
@@ -81,7 +83,8 @@ struct MlaLaunch {
 };
 
 struct CombineLaunch {
-  const float* ws_o;
+  const void* ws_o;   // partial outputs: fp32, or fp16 when o_f16 (the MLA path)
+  bool o_f16;
   const float* ws_m;
   const float* ws_l;
   const int64_t* seq_lens;

@@ -199,7 +199,11 @@ ifa_status ifa_decode(const ifa_decode_args* args, void* workspace, size_t works
  *   attn_out    fp32 [B][N_q][n][v_dim]   softmax-normalised over the split
  *   softmax_max fp32 [B][N_q][n]          max of the scaled logits (natural units)
  *   softmax_sum fp32 [B][N_q][n]          sum of e^(s_j - softmax_max)
- * in that order, each array starting at a 256-byte aligned offset
+ * in that order, each array starting at a 256-byte aligned offset; on the
+ * MLA shape (qk_dim 576, v_dim 512, one KV head) attn_out is fp16, rounded
+ * to nearest even (max and sum stay fp32): a normalised partial is a convex
+ * combination of V rows, so it is exact to fp16 rounding while |V| stays
+ * below 65504 (larger V overflows the partial)
  * (n = ifa_decode_num_splits).  Empty splits are not written; the sink is not
  * applied here.  When batch <= 256 a fourth array follows, int32 pairs [B]:
  * (sequence, clamped length) in descending length order (ties by index).
@@ -208,7 +212,8 @@ ifa_status ifa_decode(const ifa_decode_args* args, void* workspace, size_t works
  * other paths rank the lengths inside the split-KV kernel and leave it
  * unused.
  * The balanced split lays the partials out by slot instead: attn_out fp32
- * [n + B][S_q][N_q][v_dim], softmax_max and softmax_sum fp32 [n + B][S_q][N_q]
+ * (fp16 on the MLA shape) [n + B][S_q][N_q][v_dim], softmax_max and
+ * softmax_sum fp32 [n + B][S_q][N_q]
  * (S_q = query tokens per sequence), and the
  * fourth array holds, for each sequence with at least one token, the int32
  * pair (first slot, number of slots) of its pieces, in token order. */

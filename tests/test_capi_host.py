@@ -299,7 +299,12 @@ def test_mla_balanced_split_plan():
     st, sz = ws_size(a)
     assert st == ifa.IFA_OK, ifa.last_error()
     rows = (256 + 32) * 128
-    assert sz == al(rows * 512 * 4) + 2 * al(rows * 4) + al(32 * 8)
+    # attn_out partials in fp16 on the MLA shape, max and sum in fp32
+    assert sz == al(rows * 512 * 2) + 2 * al(rows * 4) + al(32 * 8)
+    # per-sequence split: the same element sizes
+    st, sz = ws_size(base_args(num_splits=16, **mla))
+    rows = 32 * 128 * 16
+    assert st == ifa.IFA_OK and sz == al(rows * 512 * 2) + 2 * al(rows * 4) + al(32 * 8)
     for nq, runs in ((256, 128), (64, 256), (32, 256), (96, 256), (224, 146)):
         a = base_args(num_splits=0, **dict(mla, num_heads=nq))
         assert split_mode(a) == 1

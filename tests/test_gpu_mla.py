@@ -183,8 +183,9 @@ def test_mla_balanced_partials_match_oracle_triples(n_q, lengths):
     assert call.balanced
     call.splitkv()
     torch.cuda.synchronize()
-    po, pm, ps, desc = (x.cpu().numpy() for x in call.partial_slots())
-    po, pm, ps = po.astype(np.float64), pm.astype(np.float64), ps.astype(np.float64)
+    po, pm, ps, desc = call.partial_slots()  # attn_out partials in fp16 on the MLA shape
+    assert po.dtype == torch.float16
+    po, pm, ps, desc = po.double().cpu().numpy(), pm.double().cpu().numpy(), ps.double().cpu().numpy(), desc.cpu().numpy()
     pref, bounds = _balanced_runs(lengths, call.num_splits)
     qf = w.q.double().numpy()
     checked = 0
