@@ -215,17 +215,27 @@ __device__ __forceinline__ uint16_t round16(float v) {
   else return __builtin_bit_cast(uint16_t, (_Float16)v);
 }
 
-// In-place scale of one accumulator tile, kept in accumulator registers (a
-// plain multiply would make the allocator copy the tiles to VGPRs).
-template <typename V>
+// In-place scale of one accumulator tile: the multiply keeps each value's
+// register, so the rare rescale branch gives the tile no new registers
+// (which made the compiler copy it at the join).  VREG: the tile lives in
+// ordinary registers, as do the 16-column kernels' MFMA accumulators (at most
+// 256 registers, so the compiler picks the MFMAs' ordinary-register form; a
+// tile pinned to accumulator registers made it copy O there and back around
+// every tile's MFMAs).  The 32-column kernels keep their tiles in
+// accumulator registers.
+template <bool VREG, typename V>
 __device__ __forceinline__ void scale_acc(V& v, float s) {
 #pragma unroll
   for (int r = 0; r < (int)(sizeof(V) / sizeof(float)); ++r) {
     float x = v[r];
-    float tmp;
-    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                 : "+a"(x), "=&v"(tmp)
-                 : "v"(s));
+    if constexpr (VREG) {
+      asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(s));
+    } else {
+      float tmp;
+      asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                   : "+a"(x), "=&v"(tmp)
+                   : "v"(s));
+    }
     v[r] = x;
   }
 }
@@ -262,9 +272,13 @@ __device__ __forceinline__ u32x2 widen_i8(uint32_t w) {
 }
 
 // BAL: the balanced split (a.balanced), a kernel of its own so that the
-// per-sequence kernel stays a single piece
+// per-sequence kernel stays a single piece.  The 16-column kernels are
+// bounded to 256 registers (two waves per SIMD; the 16-bit ones are held to
+// one by their LDS anyway), under which the compiler keeps MFMA accumulators
+// in ordinary registers.
 template <int QT, int KV, bool PAGED, bool TOK, int NC, bool BAL>
-__global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int work_items) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NC == 16 ? 2 : 1)))
+gqa_mfma_kernel(const GqaLaunch a, int work_items) {
   using S = SpecShape<KV, TOK>;
   constexpr int RB = S::RB, CPR = S::CPR, TB = S::TB, LT = S::LT, SLOT = S::SLOT, MK = S::MK;
   constexpr int kStages = S::STAGES;
@@ -767,6 +781,9 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
             kb[m][ks] = lds_read_b128(slot + offS[m][ks]);
           }
         }
+      // every K operand read is issued before the first MFMA (left alone, the
+      // scheduler put each read next to its MFMA and waited for it there)
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int m = 0; m < NSA; ++m)
 #pragma unroll
@@ -840,7 +857,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
         lsum_r *= alpha;
         vbias *= alpha;
 #pragma unroll
-        for (int mt = 0; mt < NOT; ++mt) scale_acc(acc[mt], alpha);
+        for (int mt = 0; mt < NOT; ++mt) scale_acc<NC == 16>(acc[mt], alpha);
         mref = mnew;
       }
       // P^T operand: k-slot j of lane group kg in 16-token k-step kk is score
@@ -909,7 +926,7 @@ __global__ void __launch_bounds__(64) gqa_mfma_kernel(const GqaLaunch a, int wor
     const float inv = lr > 0.f ? 1.f / lr : 0.f;  // 0: every token of the split removed for this row
     const float vb = TOK ? col_sum<NC>(vbias) * inv : 0.f;
 #pragma unroll
-    for (int mt = 0; mt < NOT; ++mt) scale_acc(acc[mt], inv);
+    for (int mt = 0; mt < NOT; ++mt) scale_acc<NC == 16>(acc[mt], inv);
     // O^T tile mt, register 4 r4 + e: channel NC mt + 8 r4 + 4 kg + e.  int8
     // (per channel or per tensor): the V parameters of a group of G tiles'
     // channels are all loaded before that group's stores (the stores may
