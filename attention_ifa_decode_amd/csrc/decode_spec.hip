@@ -98,19 +98,25 @@ __device__ __forceinline__ void dma16_lane(const void* src, uint32_t lds) {
   asm volatile("global_load_lds_dwordx4 %0, off offset:0 nt" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
-// The same from a wave-uniform base plus a 32-bit per-lane byte offset.  The
-// base is read from the first active lane, so that it sits in scalar
-// registers whatever the compiler made of it; that read is a VALU write of
-// those SGPRs, and a vector memory instruction may read an SGPR only 5 wait
-// states after a VALU wrote it.  The compiler inserts such waits before its
-// own instructions but not before inline asm, so the asm carries them.
-__device__ __forceinline__ void dma16_off(const void* base, uint32_t voff, uint32_t lds) {
+// A wave-uniform address in scalar registers, read from the first active
+// lane (whatever the compiler made of it).  That read is a VALU write of the
+// SGPRs, and a vector memory instruction may read an SGPR only 5 wait states
+// after a VALU wrote it; the compiler inserts such waits before its own
+// instructions but not before inline asm.  So the address passes through an
+// asm that holds the wait and names it as an operand: every load that uses
+// the result comes after the wait.
+__device__ __forceinline__ const void* sgpr_base(const void* base) {
   const uint64_t x = reinterpret_cast<uint64_t>(base);
-  const uint64_t u = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
-                     (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x);
-  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 offset:0 nt" ::"v"(voff),
-               "s"(reinterpret_cast<const void*>(u)), "{m0}"(lds)
-               : "memory");
+  const void* u = reinterpret_cast<const void*>(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(x >> 32)) << 32) |
+                                                (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)x));
+  asm volatile("s_nop 4" : "+s"(u));
+  return u;
+}
+
+// The same as dma16_lane, from a base in scalar registers (sgpr_base) plus a
+// 32-bit per-lane byte offset.
+__device__ __forceinline__ void dma16_off(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("global_load_lds_dwordx4 %0, %1 offset:0 nt" ::"v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 
 // 4 bytes per lane, lane l's at LDS byte address lds + 4 l
@@ -671,8 +677,8 @@ gqa_mfma_kernel(const GqaLaunch a, int work_items) {
       }
       if (whole) {
         const uint64_t boff = row0 * RB;
-        const char* kt = kbase + boff;
-        const char* vt = vbase + boff;
+        const void* kt = sgpr_base(kbase + boff);
+        const void* vt = sgpr_base(vbase + boff);
 #pragma unroll
         for (int i = 0; i < LT; ++i) {
           dma16_off(kt, loff[i], dst + 1024 * i);
