@@ -839,7 +839,11 @@ gqa_mfma_kernel(const GqaLaunch a, int work_items) {
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < NSV; ++r) sv[r] = (sacc[r / AW][r % AW] + kconst) * a.scale_log2;
+        for (int r = 0; r < NSV; ++r) {
+          // (16-bit K: no per-row constant; adding 0 is not free in floating point)
+          if constexpr (I8) sv[r] = (sacc[r / AW][r % AW] + kconst) * a.scale_log2;
+          else sv[r] = sacc[r / AW][r % AW] * a.scale_log2;
+        }
       }
       if (tstart + kTile > end || tstart + kTile > draft0) {  // the split's tail, or draft tokens
 #pragma unroll
