@@ -18,7 +18,7 @@ import attention_ifa_decode_amd as ifa
 import oracle
 from synth import config_workload, make_workload
 
-from test_gpu_decode import _announce, _compare, _full_check, _sampled_rows, whole_sequence_rows
+from test_gpu_decode import _announce, _compare, _full_check, _gpu, _sampled_rows, whole_sequence_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -247,3 +247,42 @@ def test_mla_balanced_batch_limit():
     call = ifa.call_for_workload(wg)
     assert call.balanced
     _full_check(w)
+
+
+def test_mla_large_values_within_fp16_partials():
+    """Partial outputs are fp16 on the MLA shape: a normalised partial is a
+    convex combination of V rows, so V up to 6e4 in magnitude passes through
+    them.  Cache rows scaled by 1e4 (then clipped to 6e4): the output matches
+    the oracle to the bf16 output's relative precision, with no inf."""
+    w = _mla(lengths=[700, 90], seed=61)
+    w.k_cache.copy_((w.k_cache.float() * 1e4).clamp(-6e4, 6e4).to(torch.bfloat16))  # in place: V aliases K
+    _announce(f"mla large values {w.name} lens={w.lengths()}")
+    out, lse = _gpu(w)
+    ref_out, ref_lse = oracle.decode_workload(w)
+    assert np.isfinite(out).all()
+    scale = float(np.max(np.abs(ref_out)))
+    assert scale > 1e3
+    err = float(np.max(np.abs(out - ref_out)))
+    print(f"[parity] large values: max-abs {err:.3e} of max |oracle| {scale:.3e}", flush=True)
+    assert err <= 5e-3 * scale
+    assert float(np.max(np.abs(lse - ref_lse))) <= 1e-3 * max(1.0, float(np.max(np.abs(ref_lse))))
+
+
+def test_mla_values_beyond_fp16_overflow_visibly():
+    """Beyond 65504 an fp16 partial overflows: one V channel held at 7e4 in
+    every cached row (the same shift of every score, so the weights do not
+    change) comes out inf for every row, and the other channels and lse stay
+    those of the oracle.  The limit shows in the output rather than as a
+    finite error."""
+    w = _mla(lengths=[300, 41], seed=62)
+    c = 17
+    w.k_cache[..., c] = 7e4
+    _announce(f"mla fp16 overflow {w.name} lens={w.lengths()}")
+    out, lse = _gpu(w)
+    ref_out, ref_lse = oracle.decode_workload(w)
+    assert np.isinf(out[..., c]).all()
+    keep = np.ones(out.shape[-1], dtype=bool)
+    keep[c] = False
+    err = float(np.max(np.abs(out[..., keep] - ref_out[..., keep])))
+    assert err <= 1e-2, err
+    assert float(np.max(np.abs(lse - ref_lse))) <= 1e-3 * max(1.0, float(np.max(np.abs(ref_lse))))
