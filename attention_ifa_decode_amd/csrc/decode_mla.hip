@@ -598,7 +598,13 @@ mla_splitkv_kernel(const MlaLaunch a) {
       const int last = (ntiles - 1) % STAGES;
       const uint32_t obuf = ring_lds + ((last + 1 + (wave >> 1)) % STAGES) * kTileBytes + (wave & 1) * 32 * kORow;
       const int hl = lane & 31;
-      _Float16* const orow0 = a.ws_o + (pbase + (int64_t)(head - hl) * pstride) * kDv;
+      // this lane's first row (head h of the wave) at channel 4 hl; its later
+      // rows follow every two heads.  The address advances by one stride per
+      // store: left to itself the compiler precomputed the 16 row addresses
+      // (64-bit products) once, held them across the 4 rounds and spilled
+      // them, and each store then waited for its reload.
+      _Float16* const lane_row = a.ws_o + (pbase + (int64_t)(head - hl + h) * pstride) * kDv + 4 * hl;
+      const int64_t row_step = 2 * (int64_t)pstride * kDv;
 #pragma unroll
       for (int c = 0; c < kMTiles / 4; ++c) {
 #pragma unroll
@@ -610,13 +616,16 @@ mla_splitkv_kernel(const MlaLaunch a) {
             for (int e = 0; e < 4; ++e) v[e] = acc[4 * c + j][4 * q + e] * inv;
             lds_write_f32x4(obuf + hl * kORow + 4 * (32 * j + 8 * q + 4 * h), v);
           }
+        int64_t off = 128 * c;
+        asm volatile("" : "+v"(off));  // per round, not hoisted (an offset: the pointer stays global)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = 2 * i + h;  // row (head of the wave) this lane stores
           const f32x4_t v = lds_read_f32x4(obuf + r * kORow + 16 * hl);
           // rounded to fp16 (nearest even): 256 contiguous bytes per row
           const f16x4_t w = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-          *reinterpret_cast<f16x4_t*>(orow0 + (int64_t)r * pstride * kDv + 128 * c + 4 * hl) = w;
+          *reinterpret_cast<f16x4_t*>(lane_row + off) = w;
+          off += row_step;
         }
       }
     }
