@@ -399,9 +399,14 @@ mla_splitkv_kernel(const MlaLaunch a) {
     };
 
     // ---- Q^T operand: this wave's 32 heads, 8 channels per lane per k-step ----
-    const int head = hg * (32 * NW) + wave * 32 + (lane & 31);
-    const bf16x8_t* qrow =
-        reinterpret_cast<const bf16x8_t*>(static_cast<const char*>(a.q) + ((int64_t)b * a.n_q + head) * kRowBytes) + h;
+    // The row address comes from a lane index laundered per piece: a hoisted
+    // copy would be spilled, and reloading it waits for every older load,
+    // tile 0's included, before Q's loads can go out.
+    int qlane = lane;
+    asm volatile("" : "+v"(qlane));
+    const int head = hg * (32 * NW) + wave * 32 + (qlane & 31);
+    const int64_t qoff = ((int64_t)b * a.n_q + head) * kRowBytes + 16 * (qlane >> 5);
+    const bf16x8_t* qrow = reinterpret_cast<const bf16x8_t*>(static_cast<const char*>(a.q) + qoff);
     // Tile 0 is queued first so that its loads and Q's are in flight
     // together; the wait for Q (older loads complete first) then covers
     // tile 0, which the first step needs anyway.
