@@ -477,8 +477,6 @@ mla_splitkv_kernel(const MlaLaunch a) {
         wait_vmem<0>();
       }
       __syncthreads();  // every wave's share of tile i is in; tile i-1 is consumed
-      // tile i + STAGES - 1 goes into the slot of tile i - 1
-      if (i + STAGES - 1 < ntiles) queue_tile(i + STAGES - 1, (i + STAGES - 1) % STAGES);
       const uint32_t slot = ring_lds + (i % STAGES) * kTileBytes;
       const int tstart = start + kTile * i;
 
@@ -550,6 +548,12 @@ mla_splitkv_kernel(const MlaLaunch a) {
 
       // keep the softmax out of the PV schedule: interleaving it would lengthen
       // register live ranges and starve the V^T read-ahead
+      __builtin_amdgcn_sched_barrier(0);
+
+      // Tile i + STAGES - 1 goes into the slot of tile i - 1, free since the
+      // barrier.  Queued here rather than right after it, its loads do not
+      // hold up the first QK^T MFMAs; PV waits on LDS reads anyway.
+      if (i + STAGES - 1 < ntiles) queue_tile(i + STAGES - 1, (i + STAGES - 1) % STAGES);
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- O^T += V^T . P^T (MFMA n: k-step n / 16, row tile n % 16) ----
