@@ -34,8 +34,9 @@
 // byte permute (fp16 has unit spacing in [1024, 2048)), so both products run
 // on fp16 MFMAs.  The K scale is folded into q (q' = q * scale_K, rounded to
 // fp16) and the K offset into a per-row constant sum_d q'_d (offset_d - 1152);
-// each V tile is widened into an fp16 copy in LDS for the transposing read,
-// and the V scale and offset are applied to the normalised output.
+// V^T operands come from the int8 tile through the byte-transposing read
+// (ds_read_b64_tr_b8) and are widened in registers, and the V scale and
+// offset are applied to the normalised output.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -50,7 +51,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 
 constexpr int kD = 128;
 constexpr int kTile = 32;                // tokens per tile
-constexpr int kRowB16 = kD * 2;          // bytes of a 16-bit row (and of the int8 V tile's fp16 copy)
+constexpr int kRowB16 = kD * 2;          // bytes of a 16-bit row
 constexpr float kRescale = 8.f;
 constexpr float kMrefInit = -1e30f;
 constexpr int kBalChunks = kLongestFirstMaxBatch / 64;  // sequences per lane in the balanced split
@@ -74,9 +75,17 @@ struct SpecShape {
   static_assert(2 * LT * (STAGES - 1) <= 63 && STAGES >= 2 && STAGES <= 3, "vmcnt, ring");
 };
 
-// Row t of an int8 tile (8 chunks of 16 bytes) keeps chunk c at position
-// c ^ swz(t).
-__device__ __forceinline__ int swz(int t) { return (2 * (t & 3) + ((t >> 2) & 1)) ^ (2 * ((t >> 3) & 1)); }
+// Row t of an int8 tile (8 chunks of 16 bytes, 128-byte rows: rows of one
+// parity share a bank half) keeps chunk c at position c ^ swz(t):
+//   - 16 consecutive rows from a multiple of 16 take 8 values per parity (the
+//     S^T operand reads: 16 rows, one chunk);
+//   - bit 4 of t flips bit 1, so the rows 4 kg + 0..3 and 16 + 4 kg + 0..3 of
+//     two neighbouring groups kg (a 32-lane phase of the transposing V^T read
+//     in 16 columns; in 32 columns, rows r and 8 + r with two chunks) also
+//     take 16 different 16-byte bank groups.
+__device__ __forceinline__ int swz(int t) {
+  return (2 * (t & 3) + ((t >> 2) & 1)) ^ (2 * ((t >> 3) & 1)) ^ (2 * ((t >> 4) & 1));
+}
 
 // Row t of a 16-bit tile (16 chunks, 256 bytes: every row starts in LDS bank
 // 0) keeps chunk c at position c ^ swz16(t), with swz16 the bit order of
@@ -86,8 +95,6 @@ __device__ __forceinline__ int swz(int t) { return (2 * (t & 3) + ((t >> 2) & 1)
 //   - 8 consecutive rows (from a multiple of 8) differ in swz16 / 2, and 4
 //     consecutive rows (from a multiple of 4) in swz16 / 4 (the transposing
 //     V^T reads: 8 rows x 2 chunks, or 4 rows x 4 chunks, per 32-lane phase);
-//   - rows 2j and 2j + 1 differ in parity (the int8 V widening writes: 2 rows
-//     x 8 even or 8 odd chunk positions per 16-lane phase).
 // So none of these accesses meets another in one bank (a 3-bit swizzle left
 // each of them two-way conflicted).
 __device__ __forceinline__ int swz16(int t) {
@@ -158,6 +165,15 @@ __device__ __forceinline__ void lds_write_b128(uint32_t addr, const u32x4& v) {
 
 __device__ __forceinline__ s16x4_t lds_read_tr16(uint32_t addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(uintptr_t)addr);
+}
+
+// Transposing read of bytes: in each 16-lane group, source lane s names 8
+// bytes (row s / 2, columns 8 (s % 2) .. + 7 of an 8-row x 16-column block),
+// and lane i receives column i of the block, byte j from row j.
+__device__ __forceinline__ u32x2 lds_read_tr8(uint32_t addr) {
+  typedef __attribute__((ext_vector_type(2))) int i32x2;
+  const i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(uintptr_t)addr);
+  return u32x2{(uint32_t)r[0], (uint32_t)r[1]};
 }
 
 // 32x32x16 MFMA on 16-bit operands held as raw 16-byte vectors
@@ -713,8 +729,8 @@ gqa_mfma_kernel(const GqaLaunch a, int work_items) {
         const int c8 = (KSTEP * ks + 8 * kg) / 8;  // 8-channel group of the row
         offS[m][ks] = I8 ? t * RB + 16 * ((c8 >> 1) ^ swz(t)) + 8 * (c8 & 1) : t * RB + 16 * (c8 ^ swz16(t));
       }
-    // V^T A operand (transposing read) on 16-bit rows (the int8 V tile's fp16
-    // copy).  In 16-lane group gq, source lane s = 4 r + q reads 4 channels of
+    // V^T A operand (transposing read) on 16-bit rows.  In 16-lane group gq,
+    // source lane s = 4 r + q reads 4 channels of
     // one row, the group a 4-row x 16-channel block, and the read hands lane i
     // of the group the 4 tokens of channel i of the block.
     //   32 columns: row 8 rd + 4 (gq / 2) + r, chunk 8 hi + 4 (tile & 1) + 2
@@ -725,8 +741,27 @@ gqa_mfma_kernel(const GqaLaunch a, int work_items) {
     //     with hi = tile / 4, for the k-slots 0..3 (tokens 4 kg + 0..3) and
     //     4..7 (tokens 16 + 4 kg + 0..3) of the single 32-token k-step.
     // Offsets [hi][tile part][rd]; half q % 2.
-    uint32_t offV[2][4][2];
-    {
+    //
+    // int8 V: the byte-transposing read takes the same k-slots straight from
+    // the int8 tile, 8 tokens per lane.  Source lane s = 2 j + e of group gq
+    // names row j of the block (the token of k-slot j) and channels 8 e .. + 7
+    // of the MFMA's 16: chunk `tile` (16 columns) or 2 (tile % 4) + (gq & 1)
+    // (32 columns), tokens as above; in 32 columns k-step 1 lies 16 rows
+    // further, where bit 4 of the row changes the swizzle, so it has offsets
+    // of its own.  Offset n belongs to PV MFMA n.
+    uint32_t offV[I8 ? 1 : 2][4][2];
+    uint32_t offV8[I8 ? 8 : 1];
+    if constexpr (I8) {
+      const int s = lane_p & 15, gq = lane_p >> 4;
+      const int j = s >> 1, e = s & 1;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const int kk = NC == 32 ? n / NOT : 0, mt = NC == 32 ? n % NOT : n;
+        const int t = NC == 32 ? 16 * kk + 8 * (j >> 2) + 4 * (gq >> 1) + (j & 3) : 16 * (j >> 2) + 4 * gq + (j & 3);
+        const int c = NC == 32 ? 2 * mt + (gq & 1) : mt;
+        offV8[n] = t * RB + 16 * (c ^ swz(t)) + 8 * e;
+      }
+    } else {
       const int s = lane_p & 15, gq = lane_p >> 4;
       const int r = s >> 2, q = s & 3;
 #pragma unroll
@@ -794,31 +829,6 @@ gqa_mfma_kernel(const GqaLaunch a, int work_items) {
       for (int m = 0; m < NSA; ++m)
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) sacc[m] = mfma_nc<NC, MK>(kb[m][ks], qreg[ks], sacc[m]);
-
-      // int8: widen this V tile into an fp16 copy in 16-bit row layout, written
-      // over the whole slot (K and V, 2 x 4 KB), whose K operands are in
-      // registers by now.  All int8 chunks are read before any write (a wave's
-      // LDS operations complete in order).  Lane takes positions P = lane + 64 k
-      // of the int8 V tile: row t = P / 8, chunk c = (P % 8) ^ swz(t) = channels
-      // 16 c .. 16 c + 15, which become fp16 chunks 2 c and 2 c + 1 of row t.
-      if constexpr (I8) {
-        u32x4 x[TB / 1024];
-#pragma unroll
-        for (int k = 0; k < TB / 1024; ++k) x[k] = lds_read_b128(slot + TB + 16 * (lane_p + 64 * k));
-#pragma unroll
-        for (int k = 0; k < TB / 1024; ++k) {
-          const int P = lane_p + 64 * k;
-          const int t = P >> 3;
-          const int c = (P & 7) ^ swz(t);
-          const u32x2 w0 = widen_i8(x[k][0]), w1 = widen_i8(x[k][1]), w2 = widen_i8(x[k][2]), w3 = widen_i8(x[k][3]);
-          const u32x4 lo = {w0[0], w0[1], w1[0], w1[1]}, hi = {w2[0], w2[1], w3[0], w3[1]};
-          lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c) ^ swz16(t)), lo);
-          lds_write_b128(slot + t * kRowB16 + 16 * ((2 * c + 1) ^ swz16(t)), hi);
-        }
-        // the reads below see this wave's writes
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-      }
 
       // ---- online softmax over this lane's row (column) ----
       // score register r (accumulator register r % AW of S^T tile r / AW) holds
@@ -908,17 +918,23 @@ gqa_mfma_kernel(const GqaLaunch a, int work_items) {
       // ---- O^T += V^T . P^T ----
       // 32 columns: MFMA n takes k-step n / 4 and row tile n % 4 (32 channels);
       // 16 columns: MFMA n takes row tile n (16 channels) over all 32 tokens
-      const uint32_t vt = I8 ? slot : slot + TB;
       u32x4 vb[8];
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const int kk = NC == 32 ? n / NOT : 0, mt = NC == 32 ? n % NOT : n;
-        const int tp = NC == 32 ? (mt & 1) : (mt & 3);
-        const int hi8 = NC == 32 ? (mt >> 1) : (mt >> 2);
-        const uint32_t imm = kRowB16 * 16 * kk;
-        const s16x4_t lo = lds_read_tr16(vt + offV[hi8][tp][0] + imm);
-        const s16x4_t hi = lds_read_tr16(vt + offV[hi8][tp][1] + imm);
-        vb[n] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        if constexpr (I8) {
+          // 8 tokens of one channel as int8, widened to the fp16 values 1152 + x
+          const u32x2 x = lds_read_tr8(slot + TB + offV8[n]);
+          const u32x2 w0 = widen_i8(x[0]), w1 = widen_i8(x[1]);
+          vb[n] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+        } else {
+          const int kk = NC == 32 ? n / NOT : 0, mt = NC == 32 ? n % NOT : n;
+          const int tp = NC == 32 ? (mt & 1) : (mt & 3);
+          const int hi8 = NC == 32 ? (mt >> 1) : (mt >> 2);
+          const uint32_t imm = kRowB16 * 16 * kk;
+          const s16x4_t lo = lds_read_tr16(slot + TB + offV[hi8][tp][0] + imm);
+          const s16x4_t hi = lds_read_tr16(slot + TB + offV[hi8][tp][1] + imm);
+          vb[n] = __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
       }
 #pragma unroll
       for (int n = 0; n < 8; ++n) {

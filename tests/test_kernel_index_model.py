@@ -3,7 +3,8 @@
 The GQA kernel (decode_spec.hip) and the MLA kernel (decode_mla.hip) move
 tiles HBM -> LDS with direct-to-LDS loads that place 16-byte chunks at
 XOR-swizzled positions, and read them back as MFMA operands (row-wise for
-the scores, with the transposing 8-byte read for V^T).  Each formula below is
+the scores, with a transposing 8-byte read for V^T: 16-bit elements, or int8
+bytes widened in registers).  Each formula below is
 the kernel's own, restated per lane; the tests check what has to hold between
 them: the loads place every chunk of a tile exactly once, every read finds
 the logical chunk it means, the two address paths of a tile load agree, and
@@ -19,8 +20,12 @@ import pytest
 TILE = 32  # tokens per tile (both kernels)
 
 
-def swz(t):  # 3-bit swizzle: int8 GQA rows (8 chunks) and MLA rows (72 chunks)
+def swz(t):  # 3-bit swizzle of MLA rows (72 chunks)
     return (2 * (t & 3) + ((t >> 2) & 1)) ^ (2 * ((t >> 3) & 1))
+
+
+def swz_i8(t):  # int8 GQA rows (8 chunks): the MLA swizzle, bit 1 also flipped by bit 4 of the row
+    return swz(t) ^ (2 * ((t >> 4) & 1))
 
 
 def swz16(t):  # 4-bit swizzle of 256-byte rows (16 chunks)
@@ -33,7 +38,7 @@ def gqa_shape(i8):
     rb = 128 if i8 else 256  # bytes of one token row of one KV head
     cpr = rb // 16  # chunks per row
     lt = TILE * rb // 1024  # load instructions per K (or V) tile
-    return rb, cpr, lt, (swz if i8 else swz16)
+    return rb, cpr, lt, (swz_i8 if i8 else swz16)
 
 
 def gqa_placement(i8):
@@ -58,11 +63,6 @@ def test_gqa_tile_loads_place_every_chunk_once(i8):
         assert P == t * cpr + (c ^ sw(t))
 
 
-def phys16(t, c):
-    """Byte offset in a 16-bit (or the int8 V tile's fp16 copy) tile of logical chunk c of row t."""
-    return t * 256 + 16 * (c ^ swz16(t))
-
-
 @pytest.mark.parametrize("nc", [16, 32])
 def test_gqa_score_operand_reads(nc):
     """S^T A operand: lane (col, kg) at k-step ks reads channels KSTEP ks + 8 kg
@@ -78,7 +78,7 @@ def test_gqa_score_operand_reads(nc):
             t = nc * m + col
             c8 = (kstep * ks + 8 * kg) // 8  # 8-channel group of the row
             if i8:
-                off = t * rb + 16 * ((c8 >> 1) ^ swz(t)) + 8 * (c8 & 1)
+                off = t * rb + 16 * ((c8 >> 1) ^ swz_i8(t)) + 8 * (c8 & 1)
                 row, chunk = place[off // 16]
                 assert (row, chunk, (off % 16) // 8) == (t, c8 >> 1, c8 & 1)  # 16 channels per int8 chunk
             else:
@@ -86,20 +86,75 @@ def test_gqa_score_operand_reads(nc):
                 assert off % 16 == 0 and place[off // 16] == (t, c8)
 
 
-def test_gqa_int8_v_widening_round_trip():
-    """int8 V tile chunk at position P (row t = P / 8, logical chunk c = channels
-    16 c .. + 15) is written as fp16 chunks 2 c and 2 c + 1 of row t in the
-    16-bit layout; together the 256 positions write every fp16 chunk once."""
+def pv_tokens(nc, kk, gq):
+    """Tokens of k-slots 0..7 of the P^T operand in lane group gq (k-step kk):
+    the S^T accumulator's token order, which the V^T operand must follow."""
+    if nc == 32:  # 4 h + 0..3 and 8 + 4 h + 0..3 of the 16-token k-step, h = gq / 2
+        first = 16 * kk + 4 * (gq >> 1)
+        return [first + r for r in range(4)] + [first + 8 + r for r in range(4)]
+    return [4 * gq + r for r in range(4)] + [16 + 4 * gq + r for r in range(4)]
+
+
+def tr8_receive(addrs, byte_at):
+    """ds_read_b64_tr_b8 on one 16-lane group: source lane s names 8 bytes at
+    addrs[s] (row s / 2, columns 8 (s % 2) .. + 7 of the block); lane i
+    receives column i, byte j from row j (measured with an in-bounds probe)."""
+    return [[byte_at(addrs[2 * j + i // 8] + i % 8) for j in range(8)] for i in range(16)]
+
+
+@pytest.mark.parametrize("nc", [16, 32])
+def test_gqa_int8_transposing_v_reads(nc):
+    """int8 V^T operand of PV MFMA n: lane i of group gq receives channel
+    base + i (the MFMA row) for the 8 tokens of its k-slots, in slot order,
+    from the int8 tile as the loads placed it."""
     place = gqa_placement(True)
-    written = []
-    for k in range(4):
-        for lane in range(64):
-            P = lane + 64 * k
-            t = P >> 3
-            c = (P & 7) ^ swz(t)
-            assert place[P] == (t, c)
-            written += [phys16(t, 2 * c), phys16(t, 2 * c + 1)]
-    assert sorted(written) == list(range(0, 8192, 16))
+    not_ = 128 // nc
+
+    def byte_at(off):  # (token, channel) of LDS byte `off` of the int8 V tile
+        t, c = place[off // 16]
+        return (t, 16 * c + off % 16)
+
+    for n in range(8):
+        kk = n // not_ if nc == 32 else 0
+        mt = n % not_ if nc == 32 else n
+        for gq in range(4):
+            addrs = []
+            for s in range(16):
+                j, e = s >> 1, s & 1
+                t = (16 * kk + 8 * (j >> 2) + 4 * (gq >> 1) + (j & 3)) if nc == 32 else (16 * (j >> 2) + 4 * gq + (j & 3))
+                c = 2 * mt + (gq & 1) if nc == 32 else mt
+                addrs.append(t * 128 + 16 * (c ^ swz_i8(t)) + 8 * e)
+            base = 32 * mt + 16 * (gq & 1) if nc == 32 else 16 * mt
+            got = tr8_receive(addrs, byte_at)
+            for i in range(16):
+                assert got[i] == [(tok, base + i) for tok in pv_tokens(nc, kk, gq)], (nc, n, gq, i)
+
+
+@pytest.mark.parametrize("nc", [16, 32])
+def test_gqa_int8_transposing_v_reads_bank_groups(nc):
+    """A 32-lane phase of that read (groups 2p, 2p + 1) names 16 rows x 16
+    bytes that fall in 16 different 16-byte bank groups of a 256-byte bank
+    sweep (128-byte rows alternate bank halves)."""
+    not_ = 128 // nc
+    for n in range(8):
+        kk = n // not_ if nc == 32 else 0
+        mt = n % not_ if nc == 32 else n
+        for p in range(2):
+            groups = set()
+            for gq in (2 * p, 2 * p + 1):
+                for j in range(8):
+                    t = (16 * kk + 8 * (j >> 2) + 4 * (gq >> 1) + (j & 3)) if nc == 32 else (16 * (j >> 2) + 4 * gq + (j & 3))
+                    c = 2 * mt + (gq & 1) if nc == 32 else mt
+                    groups.add((t * 128 // 16 + (c ^ swz_i8(t))) % 16)
+            assert len(groups) == 16, (nc, n, p)
+
+
+def test_gqa_int8_old_swizzle_conflicts_in_the_transposing_read():
+    """Without the row-bit-4 term, rows t and t + 16 of one 16-column group
+    share a bank group (why the int8 swizzle has it)."""
+    for gq in range(4):
+        groups = [(t * 128 // 16 + (0 ^ swz(t))) % 16 for t in [4 * gq + r for r in range(4)] + [16 + 4 * gq + r for r in range(4)]]
+        assert len(set(groups)) == 4
 
 
 @pytest.mark.parametrize("nc", [16, 32])
@@ -266,10 +321,13 @@ def test_mla_operand_reads():
 # ----------------------------------------------------------------------------- swizzle properties
 
 def test_swizzles_repeat_every_16_rows():
-    """The operand offsets add 16 rows per k-step as an immediate: valid only
-    because both swizzles depend on the row modulo 16."""
+    """The 16-bit and MLA operand offsets add 16 rows per k-step as an
+    immediate: valid only because those swizzles depend on the row modulo 16.
+    The int8 swizzle repeats every 32 rows (a tile) and its reads take
+    explicit offsets per k-step."""
     for t in range(64):
         assert swz(t) == swz(t + 16) and swz16(t) == swz16(t + 16)
+        assert swz_i8(t) == swz_i8(t + 32) and swz_i8(t) == swz_i8(t + 16) ^ 2
 
 
 def test_swz16_bank_properties():
@@ -291,11 +349,21 @@ def test_swz_spreads_rows_over_bank_groups():
     """3-bit swizzle: 8 consecutive rows (from a multiple of 8) take 8
     positions, and rows t and t + 8 differ; on 1152-byte MLA rows, which
     alternate bank halves, 16 consecutive rows' copies of one chunk then land
-    in 16 different 16-byte bank groups (64 banks x 4 bytes)."""
-    for k in range(4):
-        assert len({swz(t) for t in range(8 * k, 8 * k + 8)}) == 8
+    in 16 different 16-byte bank groups (64 banks x 4 bytes).  The int8 GQA
+    swizzle keeps both properties inside each 16-row window from a multiple of
+    16 (the only rows its S^T operand reads take together), and on its
+    128-byte rows those 16 rows' copies of one chunk also take 16 different
+    bank groups."""
+    for sw in (swz, swz_i8):
+        for k in range(4):
+            assert len({sw(t) for t in range(8 * k, 8 * k + 8)}) == 8
     for t in range(32):
         assert swz(t) != swz(t + 8)
+    for t in [t for t in range(64) if t % 16 < 8]:
+        assert swz_i8(t) != swz_i8(t + 8)
+    for c in range(8):
+        for k in range(2):
+            assert len({(t * 128 // 16 + (c ^ swz_i8(t))) % 16 for t in range(16 * k, 16 * k + 16)}) == 16
     for c in range(MLA_CHUNKS):
         for k in range(2):
             groups = {((t * MLA_ROWB) // 16 + (c ^ swz(t))) % 16 for t in range(16 * k, 16 * k + 16)}
