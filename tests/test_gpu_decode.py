@@ -148,6 +148,19 @@ def test_many_workgroups_ragged(kv, layout, n_q, d):
     _full_check(w, 4)
 
 
+@pytest.mark.parametrize("layout", ["paged", "bnsd"])
+def test_int8_group_32(layout):
+    """One query token with 32 query heads per KV head: the 32-column int8
+    kernel at S_q 1 (per-channel antiquant, sink), per-sequence splits and the
+    balanced split."""
+    lens = [1, 33, 64, 700, 2049]
+    kw = dict(block_size=64, extra_blocks=1) if layout == "paged" else dict(s_cap=2112)
+    w = make_workload(batch=len(lens), n_q=64, n_kv=2, qk_dim=128, kv_dtype="i8", layout=layout, lengths=lens,
+                      seed=160, sink=True, antiquant=True, **kw)
+    for splits in (3, None):
+        _full_check(w, splits)
+
+
 @pytest.mark.parametrize("batch", [65, 130, 256, 257])
 @pytest.mark.parametrize("kv", ["bf16", "i8"])
 def test_longest_first_batch_sizes(batch, kv):

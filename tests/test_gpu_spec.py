@@ -82,6 +82,20 @@ def test_multi_token_per_token_antiquant(mode, aq):
     _check(w, q, mode, _tree(len(lens), q_seq, 142) if mode == "tree" else None, 2)
 
 
+@pytest.mark.parametrize("mode", ["none", "causal", "tree"])
+@pytest.mark.parametrize("aq", ["channel", "token", "token_head"])
+def test_multi_token_int8_32_rows(mode, aq):
+    """int8 with 32 query rows per KV head (S_q 4 x group 8): the 32-column
+    MFMA kernel, whose V^T operands come through the byte-transposing read
+    with offsets of their own for each 16-token k-step; lengths leave a
+    ragged last tile and one tile-aligned sequence."""
+    q_seq, lens = 4, [1, 4, 37, 300, 1030, 96]
+    w = make_workload(batch=len(lens), n_q=16, n_kv=2, qk_dim=128, kv_dtype="i8", layout="paged", block_size=32,
+                      lengths=lens, seed=150, sink=True, antiquant=True, antiquant_mode=aq, extra_blocks=1)
+    q = _query(len(lens), q_seq, 16, 128, torch.bfloat16, 151)
+    _check(w, q, mode, _tree(len(lens), q_seq, 152) if mode == "tree" else None, 3)
+
+
 @pytest.mark.parametrize("q_seq,n_q,n_kv,d", [(2, 32, 8, 128), (3, 64, 8, 128), (7, 4, 4, 64), (16, 8, 8, 64),
                                              (5, 16, 2, 128)])
 @pytest.mark.parametrize("mode", ["causal", "tree"])
