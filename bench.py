@@ -260,6 +260,8 @@ def main():
                     help="cache layout instead of the config's own (paged <-> paged_bsh, bnsd <-> bsnd)")
     ap.add_argument("--q-seq", type=int, default=1, help="query tokens per sequence (1..16)")
     ap.add_argument("--mask", default="causal", choices=["none", "causal", "tree"])
+    ap.add_argument("--antiquant-mode", default=None, choices=["channel", "tensor", "token", "token_head"],
+                    help="int8 workloads: where the antiquant scale and offset vary (default: the config's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-ceiling", action="store_true")
     ap.add_argument("--reps", type=int, default=100, help="reps of the step-median and kernel-time loops")
@@ -291,7 +293,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     over = {} if args.kv_layout is None else {"layout": args.kv_layout}
+    if args.antiquant_mode is not None:
+        over["antiquant_mode"] = args.antiquant_mode
     w = config_workload(args.config, seed=args.seed, device=dev, **over)
+    if args.antiquant_mode is not None and w.kv_dtype != torch.int8:
+        sys.exit("--antiquant-mode applies to int8 K/V workloads (config 4)")
     kv_bytes = w.kv_bytes()
     # enough independent copies that the 256 MB infinity cache never serves KV
     copies = 1 if kv_bytes > 3 * MALL_BYTES else min(4, -(-3 * MALL_BYTES // max(kv_bytes, 1)))
@@ -318,7 +324,7 @@ def main():
                               antiquant_offset=x.antiquant_offset,
                               num_splits=x.num_splits if args.num_splits is None else args.num_splits,
                               v_dim=x.v_dim, out_dtype=x.out_dtype, kv_layout=x.layout,
-                              sparse_mode=modes[args.mask], tree_mask=tm)
+                              sparse_mode=modes[args.mask], tree_mask=tm, antiquant_mode=x.antiquant_mode)
 
     calls = [make_call(x, i) for i, x in enumerate(works)]
 
@@ -402,7 +408,8 @@ def main():
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     # algorithmic flops: QK^T and PV for every valid token and query head
     flops = sum(w.lengths()) * w.n_q * args.q_seq * 2 * (w.qk_dim + w.v_dim)  # masked tokens counted too
-    traffic = read_traffic(args.config) if args.kv_layout is None and args.q_seq == 1 else None
+    default_shape = args.kv_layout is None and args.q_seq == 1 and args.antiquant_mode is None
+    traffic = read_traffic(args.config) if default_shape else None
     dtype_name = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16", torch.int8: "i8"}
     lens = w.lengths()
     result = {
@@ -437,6 +444,7 @@ def main():
             "num_splits": calls[0].num_splits,
             "q_seq_len": args.q_seq,
             "mask": args.mask if args.q_seq > 1 else "none",
+            "antiquant_mode": w.antiquant_mode if w.kv_dtype == torch.int8 else None,
             "kv_bytes_per_step": kv_bytes,
             "input_copies": copies,
             "timed_as": "HIP graph replays" if args.graph else "plain ifa_decode calls",
@@ -458,7 +466,7 @@ def main():
             "read_ceiling_gbs": None if ceiling is None else round(ceiling, 1),
             "frac_of_read_ceiling": None if ceiling is None else round(achieved / ceiling, 4),
             "flops_per_launch": flops,
-            "counters": read_counters(args.config) if args.kv_layout is None and args.q_seq == 1 else None,
+            "counters": read_counters(args.config) if default_shape else None,
             "mfma_tflops": round(flops / (kern_ms * 1e-3) / 1e12, 2) if w.qk_dim == 576 else None,
             "mfma_frac_bf16_dense": round(flops / (kern_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
             if w.qk_dim == 576 else None,
