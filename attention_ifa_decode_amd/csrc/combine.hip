@@ -73,8 +73,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const CombineLaunch a) {
   constexpr int kLanesPerSplit = kUnits < 64 ? kUnits : 64;
   constexpr int kParts = 64 / kLanesPerSplit;
   constexpr int kCols = kUnits / kLanesPerSplit;
-  // loads in flight per lane: 32 at VD 512, 8 below
-  constexpr int kSteps = kCols == 2 ? 16 : (kParts == 1 ? 32 : 8);
+  // 16-byte loads in flight per lane: 16 at VD 512 (64 registers of them, so
+  // that the kernel stays under 104 VGPRs and five waves fit per SIMD: a
+  // launch of up to 1280 four-row workgroups is then resident in one round),
+  // 8 below; a row with more splits takes further batches
+  constexpr int kSteps = kCols == 2 ? 8 : (kParts == 1 ? 16 : 8);
   constexpr int kBatch = kSteps * kParts;  // splits per batch of loads
   __shared__ float sm_m[kRowsPerBlock][kMaxSplitsPerRow];
   __shared__ float sm_w[kRowsPerBlock][kMaxSplitsPerRow];
