@@ -195,6 +195,7 @@ def make_workload(
     device: Union[str, torch.device] = "cpu",
     poison: bool = True,
     extra_blocks: int = 0,
+    value_seed: Optional[int] = None,
     num_splits: int = 0,
 ) -> Workload:
     """Build one seeded workload.
@@ -207,6 +208,9 @@ def make_workload(
     "token" (2, B, s_cap) (one pair per logical token position) and
     "token_head" (2, B, N_kv, s_cap), with s_cap the paged capacity
     max_blocks_per_seq * block_size or the contiguous padded length.
+    ``value_seed`` (default ``seed + 1``) seeds the tensor values alone, so
+    that workloads with one ``seed`` and different ``value_seed`` share their
+    lengths, block table and poisoned slots and differ only in the values.
     """
     v_dim = qk_dim if v_dim is None else v_dim
     n_kv_eff = n_q if n_kv == 0 else n_kv
@@ -218,7 +222,7 @@ def make_workload(
     sgen = torch.Generator().manual_seed(seed)
     lens = _draw_lengths(lengths, batch, sgen)
     dev = torch.device(device)
-    vgen = torch.Generator(device=dev).manual_seed(seed + 1)
+    vgen = torch.Generator(device=dev).manual_seed(seed + 1 if value_seed is None else value_seed)
     kdt = DTYPES[kv_dtype]
 
     q = _randn_as((batch, n_q, qk_dim), DTYPES[q_dtype], vgen, dev)

@@ -58,3 +58,23 @@ def test_config_shapes():
     w = config_workload(5, batch=2, lengths=[100, 300], max_blocks_per_seq=4)
     assert w.v_aliases_k and w.k_cache.shape[1:] == (1, 128, 576)
     assert abs(w.scale - 1 / math.sqrt(192)) < 1e-15
+
+
+def test_value_seed_keeps_structure_and_changes_values():
+    """Timing copies of one workload (same seed, another value seed) share the
+    lengths, block table, pool size and poisoned slots, so every copy is the
+    same workload; only the values differ."""
+    for layout in ("paged", "bnsd"):
+        kw = dict(batch=3, n_q=4, n_kv=2, qk_dim=8, kv_dtype="bf16", layout=layout, block_size=16,
+                  lengths=("uniform", 1, 60), s_cap=64 if layout == "bnsd" else None, seed=5)
+        a = make_workload(**kw)
+        b = make_workload(value_seed=99, **kw)
+        assert a.lengths() == b.lengths()
+        assert a.k_cache.shape == b.k_cache.shape
+        if layout == "paged":
+            assert torch.equal(a.block_table, b.block_table)
+        assert torch.equal(torch.isnan(a.k_cache), torch.isnan(b.k_cache))
+        assert torch.equal(torch.isnan(a.v_cache), torch.isnan(b.v_cache))
+        valid = ~torch.isnan(a.k_cache)
+        assert not torch.equal(a.k_cache[valid], b.k_cache[valid])
+        assert not torch.equal(a.q, b.q)
