@@ -48,6 +48,7 @@ GQA_MFMA_SOURCES = ["attention_ifa_decode_amd/csrc/decode_spec.hip", "attention_
 MLA_SOURCES = ["attention_ifa_decode_amd/csrc/decode_mla.hip", "attention_ifa_decode_amd/csrc/common.hpp"]
 # HBM counter summaries per workload (in its own layout and query length)
 TRAFFIC_FILES = {
+    2: ("gqa_mfma_c2_f16_bnsd_traffic.txt", GQA_MFMA_SOURCES),
     3: ("gqa_mfma_c3_bf16_paged_traffic.txt", GQA_MFMA_SOURCES),
     4: ("gqa_mfma_c4_i8_paged_sink_traffic.txt", GQA_MFMA_SOURCES),
     5: ("mla_splitkv_c5_bf16_paged_traffic.txt", MLA_SOURCES),
